@@ -1,0 +1,92 @@
+"""The seeded generator: determinism, boosts, statistics and the paged layout."""
+
+import math
+
+import numpy as np
+import torch
+
+import synth
+
+
+def test_prefill_is_deterministic():
+    a = synth.prefill_inputs(batch=1, hq=4, hkv=2, L=256, d=64, block_k=32, seed=5)
+    b = synth.prefill_inputs(batch=1, hq=4, hkv=2, L=256, d=64, block_k=32, seed=5)
+    c = synth.prefill_inputs(batch=1, hq=4, hkv=2, L=256, d=64, block_k=32, seed=6)
+    for x, y in [(a.q, b.q), (a.k, b.k), (a.v, b.v)]:
+        assert torch.equal(x, y)
+    assert not torch.equal(a.q, c.q)
+
+
+def test_prefill_boosts_and_logit_std():
+    d, L, bk = 128, 2048, 128
+    p = synth.prefill_inputs(batch=1, hq=2, hkv=1, L=L, d=d, dtype=torch.float32, block_k=bk,
+                             window=False, seed=1)
+    q, k = p.q[0].double(), p.k[0, 0].double()
+    logits = p.scale * q @ k.T                          # [2, L, L]
+    al = set(p.aligned[0][0])
+    assert len(al) == round(0.1 * (L // bk)) and 0 not in al
+    content = torch.ones(L, dtype=torch.bool)
+    content[0] = False
+    for j in al:
+        content[j * bk:(j + 1) * bk] = False
+    std = logits[:, :, content].std().item()
+    assert 0.95 < std < 1.05
+    # sink and aligned boosts are exact in the control channels
+    assert torch.allclose(p.scale * q[..., d - 2] * k[0, d - 2], torch.full_like(q[..., 0], 10.0), atol=1e-5)
+    j = min(al)
+    assert abs(p.scale * k[j * bk, d - 1].item() - 6.0) < 1e-5
+
+
+def test_window_boost_decays():
+    d, L = 128, 4096
+    p = synth.prefill_inputs(batch=1, hq=8, hkv=1, L=L, d=d, dtype=torch.float32, block_k=128,
+                             window=True, seed=2)
+    q, k = p.q[0, :, :, :d - 2].double(), p.k[0, 0, :, :d - 2].double()
+    logits = p.scale * q @ k.T
+    i = torch.arange(1024, L)
+    for delta, tol in [(0, 0.3), (512, 0.3), (2048, 0.3)]:
+        mean = logits[:, i, i - delta].mean().item()
+        assert abs(mean - 3.0 * math.exp(-delta / 512.0)) < tol, (delta, mean)
+
+
+def test_bf16_rne_helper_matches_torch_cast():
+    x = np.random.default_rng(0).standard_normal(10000) * 100
+    want = torch.tensor(x, dtype=torch.float64).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(synth.to_bf16_rne_numpy(x), want)
+
+
+def test_paged_layout():
+    B, ctx, page = 3, 200, 16
+    d = synth.decode_inputs(batch=B, hq=8, hkv=2, ctx=ctx, d=64, page_size=page, block_k=64, seed=9,
+                            seq_lens=[200, 37, 64])
+    bt = d.block_table
+    lens = d.seq_lens.tolist()
+    used = []
+    for b in range(B):
+        npg = -(-lens[b] // page)
+        used += bt[b, :npg].tolist()
+        # slots after the last key are NaN; keys before it are finite
+        last = bt[b, npg - 1].item()
+        n_last = lens[b] - (npg - 1) * page
+        assert torch.isfinite(d.k_cache[last, :, :n_last].float()).all()
+        assert torch.isnan(d.k_cache[last, :, n_last:].float()).all()
+        assert torch.isnan(d.v_cache_t[last, :, :, n_last:].float()).all()
+        # unused table entries point at a NaN page
+        for pid in bt[b, npg:].tolist():
+            assert torch.isnan(d.k_cache[pid].float()).all()
+    assert len(set(used)) == len(used)          # pages are not shared
+    P = d.k_cache.shape[0]
+    spare = sorted(set(range(P)) - set(used))
+    assert len(spare) >= 1
+    for pid in spare:
+        assert torch.isnan(d.k_cache[pid].float()).all()
+    # sink at token 0 of every sequence
+    for b in range(B):
+        first = bt[b, 0].item()
+        assert abs(d.scale * d.k_cache[first, :, 0, 62].float() - 10.0).max() < 0.05
+
+
+def test_latent_cache_has_no_v():
+    d = synth.decode_inputs(batch=2, hq=16, hkv=1, ctx=64, d=72, dv=64, page_size=16, block_k=64,
+                            seed=1, latent=True)
+    assert d.v_cache_t is None and d.head_dim_v == 64 and d.k_cache.shape[1] == 1
