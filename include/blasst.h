@@ -1,0 +1,203 @@
+/*
+ * blasst.h - C ABI of the BLASST block-sparse attention library for AMD MI355X (gfx950).
+ *
+ * The method (pages about "BLASST: Dynamic BLocked Attention Sparsity via Softmax Thresholding",
+ * arXiv 2512.12087):
+ *   - attention is computed FlashAttention-style, visiting the KV blocks of a query tile left to
+ *     right with an online softmax (running max m, running sum l, rescaled output)
+ *     [xllm-io review, sections 解决方案概述 and 整体框架图];
+ *   - block j is skipped when every row i of the query tile has m~_i - m_i < ln(lambda), where m~
+ *     is the block-local row max and m the running max [xllm-io review, 核心公式 skip condition;
+ *     gist.science (de), 2. Methodik / Kernidee];
+ *   - a skipped block contributes nothing: its exp, its V load and its P.V product are elided
+ *     [gist.science (de), Kernidee; fugumt.com English abstract];
+ *   - lambda = a / L with L the context length, and a calibration model
+ *     lambda * L = alpha * exp(beta * s) for a target sparsity s [xllm-io review, 核心公式
+ *     threshold calibration and calibration model];
+ *   - prefill keeps QK^T for every block and elides exp and P.V; decode elides the V load and
+ *     decides at the K-load stage with batched loads [xllm-io review, 预填充内核优化 and
+ *     解码内核优化].
+ *
+ * Conventions for every entry point:
+ *   - All device buffers are owned by the caller.  The library allocates no device memory and keeps
+ *     no pointer after a call returns.  Scratch space (decode with num_splits > 1) is passed in as
+ *     a caller-owned workspace whose size the *_workspace_size query returns.
+ *   - Work is enqueued on the caller's HIP stream (hipStream_t passed as void*; NULL = the default
+ *     stream) and the call returns before the work completes.
+ *   - Every argument check runs before the first HIP call, so invalid arguments are reported
+ *     without touching the device.  Errors are returned as a status code; a message for the last
+ *     error of the calling thread is available from blasst_last_error().  Nothing aborts or throws.
+ *   - Numerics: bf16 or fp32 inputs, fp32 accumulation, natural-log units for lambda and for the
+ *     critical values.  lambda must lie in [0, 1]; lambda = 0 (ln lambda = -inf) is dense.
+ *   - Skip-mask bytes: 0 = kept, 1 = skipped, 2 = not live (no visible key for the whole tile).
+ *   - Critical value of a live tile-block: max over the tile's rows of (m~_i - m_i) in logit units
+ *     (softmax scale applied), with m the running max BEFORE the block (+inf for the first block of
+ *     a split).  The block is skipped iff crit < ln(lambda).  NaN for blocks that are not live.
+ */
+#ifndef BLASST_H
+#define BLASST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BLASST_OK = 0,
+  BLASST_ERR_INVALID_ARG = 1,   /* a pointer, size, stride or threshold is invalid */
+  BLASST_ERR_UNSUPPORTED = 2,   /* valid request, but no kernel for this head dim / block / dtype */
+  BLASST_ERR_HIP = 3,           /* a HIP call or kernel launch failed */
+  BLASST_ERR_WORKSPACE = 4      /* workspace missing or smaller than *_workspace_size() */
+} blasst_status;
+
+typedef enum { BLASST_BF16 = 0, BLASST_FP32 = 1 } blasst_dtype;
+
+typedef enum {
+  BLASST_THR_LAMBDA = 0,   /* use `lambda` directly, must be in [0, 1] */
+  BLASST_THR_A_OVER_L = 1  /* lambda = min(1, a / L), L = seqlen_k (prefill) or seq_lens[b] (decode) */
+} blasst_threshold_mode;
+
+typedef struct {
+  int32_t mode;     /* blasst_threshold_mode */
+  int32_t reserved; /* must be 0 */
+  double lambda;    /* mode BLASST_THR_LAMBDA */
+  double a;         /* mode BLASST_THR_A_OVER_L, a >= 0 */
+} blasst_threshold;
+
+/* Counter slots written (accumulated with atomics) when `counters` is not NULL; the caller zeroes
+ * the buffer before the call if it wants per-call numbers. */
+enum { BLASST_CNT_LIVE = 0, BLASST_CNT_SKIPPED = 1, BLASST_NUM_COUNTERS = 2 };
+
+/*
+ * Prefill: causal or full attention of seqlen_q queries over seqlen_k keys per (batch, q head).
+ *
+ * Layouts (element strides; the last dimension is contiguous):
+ *   q [batch][num_q_heads][seqlen_q][head_dim_qk]    strides q_stride = {batch, head, token}
+ *   k [batch][num_kv_heads][seqlen_k][head_dim_qk]   strides k_stride
+ *   v [batch][num_kv_heads][seqlen_k][head_dim_v]    strides v_stride
+ *   o [batch][num_q_heads][seqlen_q][head_dim_v]     strides o_stride, dtype out_dtype
+ *   lse [batch][num_q_heads][seqlen_q] fp32 contiguous (natural log), nullable
+ * Head mapping: q head h reads kv head h / (num_q_heads / num_kv_heads) (MHA, GQA, MQA).
+ * Causal masking is bottom-right aligned: key k is visible to query row i iff
+ *   k <= i + (seqlen_k - seqlen_q).
+ * Query tile = block_q consecutive rows of one q head; KV block = block_k consecutive keys.
+ * The live blocks of a tile are cut into num_splits contiguous chunks of ceil(J / num_splits)
+ * blocks; the running max used by the skip rule restarts at -inf at every chunk, so the first block
+ * of every chunk is kept.  The output is the softmax over the union of kept keys.
+ * Diagnostics (nullable, device memory):
+ *   skip_mask [batch][num_q_heads][ceil(seqlen_q/block_q)][ceil(seqlen_k/block_k)] uint8
+ *   crit      same shape, fp32
+ *   counters  BLASST_NUM_COUNTERS x uint64
+ * stats_only != 0: compute QK^T, block maxima, decisions, mask, crit and counters only; o and lse
+ * are not written (calibration pass).
+ * softmax_scale <= 0 selects 1/sqrt(head_dim_qk).
+ * Supported kernels: bf16 in, bf16 or fp32 out, head_dim_qk == head_dim_v in {64, 128},
+ * block_q == block_k in {64, 128}; fp32 in/out, head_dim 64 or 128, block_q == block_k == 64.
+ */
+typedef struct {
+  size_t struct_size;        /* sizeof(blasst_prefill_params), for ABI checking */
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  uint8_t *skip_mask;
+  float *crit;
+  unsigned long long *counters;
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+  blasst_threshold thr;
+  int32_t in_dtype, out_dtype; /* blasst_dtype */
+  int32_t batch, seqlen_q, seqlen_k, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v;
+  int32_t causal, block_q, block_k, num_splits, stats_only;
+  float softmax_scale;
+} blasst_prefill_params;
+
+/*
+ * Decode: one query token per sequence attends to all seq_lens[b] keys of a paged KV cache,
+ * split along the keys into num_splits chunks that run in parallel and are merged by a log-sum-exp
+ * combine.
+ *
+ * Layouts (contiguous):
+ *   q           [batch][num_q_heads][head_dim_qk]
+ *   k_cache     [num_pages][num_kv_heads][page_size][head_dim_qk]
+ *   v_cache     [num_pages][num_kv_heads][head_dim_v][page_size]  (V transposed inside each page)
+ *               NULL selects latent attention (MLA): V is the first head_dim_v channels of K.
+ *   block_table [batch][max_pages_per_seq] int32 page ids; entries past a sequence's last page
+ *               are never read
+ *   seq_lens    [batch] int32, 1 <= seq_lens[b] <= max_pages_per_seq * page_size
+ *   o           [batch][num_q_heads][head_dim_v], dtype out_dtype
+ *   lse         [batch][num_q_heads] fp32, nullable
+ * Query tile = tile_rows q heads of one sequence that share a kv head (0 selects all
+ * num_q_heads / num_kv_heads of them); KV block = block_k keys (a multiple of page_size).
+ * Diagnostics (nullable):
+ *   skip_mask/crit [batch][num_kv_heads][G / tile_rows][ceil(max_pages_per_seq*page_size/block_k)]
+ *   counters as for prefill.
+ * workspace: needed when num_splits > 1, at least blasst_decode_workspace_size() bytes, device
+ * memory, 256-byte aligned.
+ * Supported kernels: bf16 in, bf16/fp32 out; page_size 16; block_k 64;
+ *   GQA/MHA/MQA: head_dim_qk == head_dim_v == 128, tile_rows <= 16;
+ *   latent (v_cache NULL): head_dim_qk == 576, head_dim_v == 512, tile_rows == 128 (MLA-shaped).
+ */
+typedef struct {
+  size_t struct_size;        /* sizeof(blasst_decode_params) */
+  const void *q, *k_cache, *v_cache;
+  const int32_t *block_table, *seq_lens;
+  void *o;
+  float *lse;
+  uint8_t *skip_mask;
+  float *crit;
+  unsigned long long *counters;
+  void *workspace;
+  size_t workspace_bytes;
+  blasst_threshold thr;
+  int32_t in_dtype, out_dtype;
+  int32_t batch, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v;
+  int32_t page_size, max_pages_per_seq, num_pages;
+  int32_t block_k, num_splits, tile_rows, stats_only;
+  float softmax_scale;
+  int32_t reserved;          /* must be 0 */
+} blasst_decode_params;
+
+/* Prefill forward (see the struct comment).  stream: hipStream_t or NULL. */
+blasst_status blasst_prefill(const blasst_prefill_params *params, void *stream);
+
+/* Paged split-KV decode forward (see the struct comment).  stream: hipStream_t or NULL. */
+blasst_status blasst_decode(const blasst_decode_params *params, void *stream);
+
+/* Workspace bytes that blasst_decode needs for these params (0 when num_splits == 1).  Returns 0
+ * and sets the last error when the params are invalid. */
+size_t blasst_decode_workspace_size(const blasst_decode_params *params);
+
+/*
+ * Host-only calibration [xllm-io review, 核心公式 calibration model lambda * L = alpha * exp(beta s);
+ * 模型组件 calibration module: one forward pass over a sample].
+ *
+ * blasst_calib_quantile: from n critical values (host fp32 array, as written by a stats_only pass;
+ * NaN entries are ignored, +inf entries count as never skippable), the ln(lambda) at which a
+ * fraction target_s of them lies strictly below: with k = ceil(target_s * N) it is the midpoint of
+ * the k-th and (k+1)-th smallest values, capped at 0 (lambda <= 1); target_s = 0 gives -inf.
+ *
+ * blasst_calibrate: ordinary least squares of y = ln(lambda_i * L_i) on x = s_i over n >= 2 points
+ * (host arrays), giving alpha = exp(intercept), beta = slope and the rmse of y.  Requires
+ * lambda_i > 0, L_i > 0 and at least two distinct s_i.
+ *
+ * blasst_lambda_for: the deployed threshold min(1, alpha * exp(beta * s) / L).
+ */
+blasst_status blasst_calib_quantile(const float *crit, int64_t n, double target_s, double *ln_lambda);
+blasst_status blasst_calibrate(const double *L, const double *s, const double *lambda, int32_t n,
+                               double *alpha, double *beta, double *rmse);
+double blasst_lambda_for(double alpha, double beta, double s, double L);
+
+/* Status text, last error message of the calling thread, library version (major*10000+minor*100+patch),
+ * and the struct sizes the library was built with (for binding checks). */
+const char *blasst_status_string(blasst_status status);
+const char *blasst_last_error(void);
+int32_t blasst_version(void);
+size_t blasst_prefill_params_size(void);
+size_t blasst_decode_params_size(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLASST_H */

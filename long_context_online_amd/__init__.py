@@ -1,0 +1,19 @@
+"""BLASST block-sparse attention for AMD MI355X (gfx950): HIP kernels behind a C ABI
+(include/blasst.h, libblasst.so) and a thin ctypes binding with the same entry-point names."""
+
+from .blasst import (  # noqa: F401
+    BlasstError,
+    blasst_prefill,
+    blasst_decode,
+    blasst_decode_workspace_size,
+    blasst_calib_quantile,
+    blasst_calibrate,
+    blasst_lambda_for,
+    prefill_params,
+    decode_params,
+    lib,
+    LIB_PATH,
+    KEPT,
+    SKIPPED,
+    NOT_LIVE,
+)

@@ -1,0 +1,274 @@
+"""ctypes binding of libblasst.so (argument marshalling only).
+
+Every function here only turns torch tensors / Python numbers into the C structs of
+include/blasst.h and calls the library; all computation happens in the HIP kernels (or, for the
+calibration helpers, in the library's host code).  torch is used for device memory and streams.
+The library must have been built (``long_context_online_amd.build``); nothing falls back to
+another implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libblasst.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
+BF16, FP32 = 0, 1
+THR_LAMBDA, THR_A_OVER_L = 0, 1
+KEPT, SKIPPED, NOT_LIVE = 0, 1, 2
+
+EXPORTED = [
+    "blasst_prefill", "blasst_decode", "blasst_decode_workspace_size", "blasst_calib_quantile",
+    "blasst_calibrate", "blasst_lambda_for", "blasst_status_string", "blasst_last_error",
+    "blasst_version", "blasst_prefill_params_size", "blasst_decode_params_size",
+]
+
+
+class BlasstError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"blasst status {status}: {message}")
+        self.status = status
+
+
+class Threshold(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("lambda_", ctypes.c_double), ("a", ctypes.c_double)]
+
+
+class PrefillParams(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("skip_mask", ctypes.c_void_p), ("crit", ctypes.c_void_p), ("counters", ctypes.c_void_p),
+        ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+        ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+        ("thr", Threshold),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32), ("seqlen_q", ctypes.c_int32), ("seqlen_k", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32), ("stats_only", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("skip_mask", ctypes.c_void_p), ("crit", ctypes.c_void_p), ("counters", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("thr", Threshold),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("block_k", ctypes.c_int32), ("num_splits", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
+        ("stats_only", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Loads libblasst.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m long_context_online_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.blasst_prefill.argtypes = [ctypes.POINTER(PrefillParams), ctypes.c_void_p]
+        L.blasst_prefill.restype = ctypes.c_int
+        L.blasst_decode.argtypes = [ctypes.POINTER(DecodeParams), ctypes.c_void_p]
+        L.blasst_decode.restype = ctypes.c_int
+        L.blasst_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeParams)]
+        L.blasst_decode_workspace_size.restype = ctypes.c_size_t
+        L.blasst_calib_quantile.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_int64, ctypes.c_double,
+                                            ctypes.POINTER(ctypes.c_double)]
+        L.blasst_calib_quantile.restype = ctypes.c_int
+        dp = ctypes.POINTER(ctypes.c_double)
+        L.blasst_calibrate.argtypes = [dp, dp, dp, ctypes.c_int32, dp, dp, dp]
+        L.blasst_calibrate.restype = ctypes.c_int
+        L.blasst_lambda_for.argtypes = [ctypes.c_double] * 4
+        L.blasst_lambda_for.restype = ctypes.c_double
+        L.blasst_status_string.argtypes = [ctypes.c_int]
+        L.blasst_status_string.restype = ctypes.c_char_p
+        L.blasst_last_error.argtypes = []
+        L.blasst_last_error.restype = ctypes.c_char_p
+        L.blasst_version.restype = ctypes.c_int32
+        L.blasst_prefill_params_size.restype = ctypes.c_size_t
+        L.blasst_decode_params_size.restype = ctypes.c_size_t
+        if L.blasst_prefill_params_size() != ctypes.sizeof(PrefillParams) or \
+                L.blasst_decode_params_size() != ctypes.sizeof(DecodeParams):
+            raise ImportError("libblasst.so struct layout does not match this binding")
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != OK:
+        raise BlasstError(status, lib().blasst_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _threshold(lam, a):
+    if (lam is None) == (a is None):
+        raise ValueError("give exactly one of lam and a")
+    if lam is not None:
+        return Threshold(THR_LAMBDA, 0, float(lam), 0.0)
+    return Threshold(THR_A_OVER_L, 0, 0.0, float(a))
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _strides3(t):
+    s = t.stride()
+    if s[3] != 1:
+        raise ValueError("the last dimension must be contiguous")
+    return (ctypes.c_int64 * 3)(s[0], s[1], s[2])
+
+
+def prefill_params(q, k, v, o, *, causal, block_q, block_k, num_splits=1, lam=None, a=None,
+                   softmax_scale=0.0, lse=None, skip_mask=None, crit=None, counters=None,
+                   stats_only=False, out_dtype=None):
+    """Fills the C params struct for blasst_prefill from tensors (no call)."""
+    p = PrefillParams()
+    p.struct_size = ctypes.sizeof(PrefillParams)
+    p.q, p.k, p.v = _ptr(q), _ptr(k), _ptr(v)
+    p.o = _ptr(o)
+    p.lse, p.skip_mask, p.crit, p.counters = _ptr(lse), _ptr(skip_mask), _ptr(crit), _ptr(counters)
+    p.q_stride, p.k_stride, p.v_stride = _strides3(q), _strides3(k), _strides3(v)
+    p.o_stride = _strides3(o) if o is not None else (ctypes.c_int64 * 3)(0, 0, 0)
+    p.thr = _threshold(lam, a)
+    p.in_dtype = _dtype_code(q)
+    p.out_dtype = _dtype_code(o) if o is not None else (p.in_dtype if out_dtype is None else out_dtype)
+    p.batch, p.num_q_heads, p.seqlen_q, p.head_dim_qk = q.shape
+    p.num_kv_heads, p.seqlen_k = k.shape[1], k.shape[2]
+    p.head_dim_v = v.shape[3]
+    p.causal, p.block_q, p.block_k = int(bool(causal)), block_q, block_k
+    p.num_splits, p.stats_only = num_splits, int(bool(stats_only))
+    p.softmax_scale = float(softmax_scale)
+    return p
+
+
+def blasst_prefill(q, k, v, o, *, stream=None, **kw):
+    """BLASST prefill forward.  q [B, Hq, Lq, D], k/v [B, Hkv, Lk, D], o [B, Hq, Lq, Dv]
+    (last dim contiguous).  Keyword args follow the C params (causal, block_q, block_k,
+    num_splits, lam or a, softmax_scale, lse, skip_mask, crit, counters, stats_only)."""
+    p = prefill_params(q, k, v, o, **kw)
+    _check(lib().blasst_prefill(ctypes.byref(p), _stream(stream)))
+
+
+def decode_params(q, k_cache, v_cache, block_table, seq_lens, o, *, page_size, block_k, num_splits,
+                  lam=None, a=None, tile_rows=0, head_dim_v=None, softmax_scale=0.0, lse=None,
+                  skip_mask=None, crit=None, counters=None, workspace=None, stats_only=False,
+                  out_dtype=None):
+    """Fills the C params struct for blasst_decode from tensors (no call)."""
+    p = DecodeParams()
+    p.struct_size = ctypes.sizeof(DecodeParams)
+    p.q, p.k_cache, p.v_cache = _ptr(q), _ptr(k_cache), _ptr(v_cache)
+    p.block_table, p.seq_lens = _ptr(block_table), _ptr(seq_lens)
+    p.o, p.lse = _ptr(o), _ptr(lse)
+    p.skip_mask, p.crit, p.counters = _ptr(skip_mask), _ptr(crit), _ptr(counters)
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    p.thr = _threshold(lam, a)
+    p.in_dtype = _dtype_code(q)
+    p.out_dtype = _dtype_code(o) if o is not None else (p.in_dtype if out_dtype is None else out_dtype)
+    p.batch, p.num_q_heads, p.head_dim_qk = q.shape
+    p.num_pages, p.num_kv_heads, page, _ = k_cache.shape
+    if page != page_size:
+        raise ValueError("k_cache page dimension does not match page_size")
+    if head_dim_v is None:
+        head_dim_v = v_cache.shape[2] if v_cache is not None else p.head_dim_qk
+    p.head_dim_v = head_dim_v
+    p.page_size, p.max_pages_per_seq = page_size, block_table.shape[1]
+    p.block_k, p.num_splits, p.tile_rows = block_k, num_splits, tile_rows
+    p.stats_only = int(bool(stats_only))
+    p.softmax_scale = float(softmax_scale)
+    p.reserved = 0
+    return p
+
+
+def blasst_decode_workspace_size(*args, **kw) -> int:
+    p = decode_params(*args, **kw)
+    n = lib().blasst_decode_workspace_size(ctypes.byref(p))
+    err = lib().blasst_last_error().decode()
+    if n == 0 and err:
+        raise BlasstError(ERR_INVALID_ARG, err)
+    return int(n)
+
+
+def blasst_decode(q, k_cache, v_cache, block_table, seq_lens, o, *, stream=None, **kw):
+    """BLASST paged split-KV decode.  q [B, Hq, D]; k_cache [P, Hkv, page, D]; v_cache
+    [P, Hkv, Dv, page] (V transposed per page) or None for latent attention (V = K[..., :Dv]);
+    block_table [B, max_pages] int32; seq_lens [B] int32; o [B, Hq, Dv]."""
+    p = decode_params(q, k_cache, v_cache, block_table, seq_lens, o, **kw)
+    _check(lib().blasst_decode(ctypes.byref(p), _stream(stream)))
+
+
+def blasst_calib_quantile(crit, target_s: float) -> float:
+    """ln(lambda) at which a fraction target_s of the critical values lies below (host array)."""
+    c = np.ascontiguousarray(np.asarray(crit, dtype=np.float32).ravel())
+    out = ctypes.c_double()
+    _check_host(lib().blasst_calib_quantile(c.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), c.size,
+                                            float(target_s), ctypes.byref(out)))
+    return out.value
+
+
+def blasst_calibrate(L, s, lam):
+    """Least-squares fit of ln(lambda * L) = ln(alpha) + beta * s.  Returns (alpha, beta, rmse)."""
+    arrs = [np.ascontiguousarray(np.asarray(x, dtype=np.float64).ravel()) for x in (L, s, lam)]
+    n = arrs[0].size
+    if any(x.size != n for x in arrs):
+        raise ValueError("L, s and lam must have the same length")
+    dp = ctypes.POINTER(ctypes.c_double)
+    alpha, beta, rmse = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check_host(lib().blasst_calibrate(*(x.ctypes.data_as(dp) for x in arrs), n, ctypes.byref(alpha),
+                                       ctypes.byref(beta), ctypes.byref(rmse)))
+    return alpha.value, beta.value, rmse.value
+
+
+def blasst_lambda_for(alpha: float, beta: float, s: float, L: float) -> float:
+    return float(lib().blasst_lambda_for(alpha, beta, s, L))
+
+
+def _check_host(status: int):
+    if status != OK:
+        raise BlasstError(status, "invalid calibration input")
+
+
+def ln_lambda(lam=None, a=None, L=None) -> float:
+    """ln(lambda) for reporting (lambda = a / L capped at 1)."""
+    if lam is None:
+        lam = min(1.0, a / L)
+    return -math.inf if lam == 0 else math.log(lam)

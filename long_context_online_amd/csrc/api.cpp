@@ -1,0 +1,256 @@
+// Host side of the C ABI: argument validation (all before the first HIP call), threshold
+// resolution, kernel selection and launch.  See include/blasst.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/blasst.h"
+#include "common.hpp"
+
+namespace blasst {
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int D, int BC, bool out_f32, hipStream_t st);
+hipError_t launch_prefill_f32(const PrefillArgs &a, int D, hipStream_t st);
+hipError_t launch_decode_gqa(const DecodeArgs &a, hipStream_t st);
+hipError_t launch_decode_latent(const DecodeArgs &a, hipStream_t st);
+}  // namespace blasst
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+blasst_status fail(blasst_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+blasst_status ok() {
+  g_err[0] = '\0';
+  return BLASST_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ln(lambda) for a fixed threshold or for a / L; returns false when the threshold is invalid.
+bool resolve_threshold(const blasst_threshold &t, double L, double *ln_lam, const char **why) {
+  if (t.reserved != 0) { *why = "thr.reserved must be 0"; return false; }
+  if (t.mode == BLASST_THR_LAMBDA) {
+    if (!(t.lambda >= 0.0 && t.lambda <= 1.0)) { *why = "lambda must lie in [0, 1]"; return false; }
+    *ln_lam = t.lambda == 0.0 ? -INFINITY : std::log(t.lambda);
+    return true;
+  }
+  if (t.mode == BLASST_THR_A_OVER_L) {
+    if (!(t.a >= 0.0) || !std::isfinite(t.a)) { *why = "a must be finite and >= 0"; return false; }
+    if (L <= 0) { *why = "L must be > 0"; return false; }
+    const double lam = std::fmin(1.0, t.a / L);
+    *ln_lam = lam == 0.0 ? -INFINITY : std::log(lam);
+    return true;
+  }
+  *why = "unknown threshold mode";
+  return false;
+}
+
+float thr_raw_from(double ln_lam, double scale) {
+  if (std::isinf(ln_lam)) return -INFINITY;
+  return static_cast<float>(ln_lam / scale);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *blasst_status_string(blasst_status s) {
+  switch (s) {
+    case BLASST_OK: return "ok";
+    case BLASST_ERR_INVALID_ARG: return "invalid argument";
+    case BLASST_ERR_UNSUPPORTED: return "unsupported configuration";
+    case BLASST_ERR_HIP: return "HIP error";
+    case BLASST_ERR_WORKSPACE: return "workspace missing or too small";
+  }
+  return "unknown status";
+}
+
+const char *blasst_last_error(void) { return g_err; }
+int32_t blasst_version(void) { return 10000; }
+size_t blasst_prefill_params_size(void) { return sizeof(blasst_prefill_params); }
+size_t blasst_decode_params_size(void) { return sizeof(blasst_decode_params); }
+
+blasst_status blasst_prefill(const blasst_prefill_params *p, void *stream) {
+  if (!p) return fail(BLASST_ERR_INVALID_ARG, "params is NULL");
+  if (p->struct_size != sizeof(blasst_prefill_params))
+    return fail(BLASST_ERR_INVALID_ARG, "struct_size %zu != %zu", p->struct_size, sizeof(blasst_prefill_params));
+  if (!p->q || !p->k || !p->v) return fail(BLASST_ERR_INVALID_ARG, "q, k and v must be non-NULL");
+  if (!p->stats_only && !p->o) return fail(BLASST_ERR_INVALID_ARG, "o must be non-NULL unless stats_only");
+  if (p->batch < 1 || p->seqlen_q < 1 || p->seqlen_k < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 ||
+      p->head_dim_qk < 1 || p->head_dim_v < 1)
+    return fail(BLASST_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (p->num_q_heads % p->num_kv_heads)
+    return fail(BLASST_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                p->num_q_heads, p->num_kv_heads);
+  if (p->block_q < 1 || p->block_k < 1) return fail(BLASST_ERR_INVALID_ARG, "block sizes must be >= 1");
+  if (p->num_splits < 1) return fail(BLASST_ERR_INVALID_ARG, "num_splits must be >= 1");
+  if (p->in_dtype != BLASST_BF16 && p->in_dtype != BLASST_FP32) return fail(BLASST_ERR_INVALID_ARG, "bad in_dtype");
+  if (p->out_dtype != BLASST_BF16 && p->out_dtype != BLASST_FP32) return fail(BLASST_ERR_INVALID_ARG, "bad out_dtype");
+  if (p->causal != 0 && p->causal != 1) return fail(BLASST_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!std::isfinite(p->softmax_scale)) return fail(BLASST_ERR_INVALID_ARG, "softmax_scale must be finite");
+  for (int i = 0; i < 3; ++i)
+    if (p->q_stride[i] < 0 || p->k_stride[i] < 0 || p->v_stride[i] < 0 || p->o_stride[i] < 0)
+      return fail(BLASST_ERR_INVALID_ARG, "strides must be >= 0");
+  const double scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0 / std::sqrt((double)p->head_dim_qk);
+  double ln_lam;
+  const char *why = "";
+  if (!resolve_threshold(p->thr, p->seqlen_k, &ln_lam, &why)) return fail(BLASST_ERR_INVALID_ARG, "%s", why);
+
+  // ---- kernel coverage ----
+  const int D = p->head_dim_qk;
+  if (p->head_dim_v != D) return fail(BLASST_ERR_UNSUPPORTED, "head_dim_v must equal head_dim_qk");
+  if (p->block_q != p->block_k) return fail(BLASST_ERR_UNSUPPORTED, "block_q must equal block_k");
+  const int elem = p->in_dtype == BLASST_BF16 ? 2 : 4;
+  const int vec = 16 / elem;
+  if (p->in_dtype == BLASST_BF16) {
+    if (!((D == 64 || D == 128) && (p->block_k == 64 || p->block_k == 128)))
+      return fail(BLASST_ERR_UNSUPPORTED, "bf16 prefill supports head dim 64/128 and blocks 64/128");
+  } else {
+    if (!((D == 64 || D == 128) && p->block_k == 64 && p->out_dtype == BLASST_FP32))
+      return fail(BLASST_ERR_UNSUPPORTED, "fp32 prefill supports head dim 64/128, blocks 64, fp32 out");
+  }
+  if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || (p->o && !aligned16(p->o)))
+    return fail(BLASST_ERR_UNSUPPORTED, "q, k, v and o must be 16-byte aligned");
+  const int oelem = p->out_dtype == BLASST_BF16 ? 2 : 4;
+  for (int i = 0; i < 3; ++i)
+    if (p->q_stride[i] % vec || p->k_stride[i] % vec || p->v_stride[i] % vec || p->o_stride[i] % (16 / oelem))
+      return fail(BLASST_ERR_UNSUPPORTED, "strides must be multiples of 16 bytes");
+
+  blasst::PrefillArgs a{};
+  a.q = p->q; a.k = p->k; a.v = p->v; a.o = p->o; a.lse = p->lse;
+  a.mask = p->skip_mask; a.crit = p->crit; a.counters = p->counters;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = p->q_stride[i]; a.ks[i] = p->k_stride[i]; a.vs[i] = p->v_stride[i]; a.os[i] = p->o_stride[i];
+  }
+  a.B = p->batch; a.Lq = p->seqlen_q; a.Lk = p->seqlen_k; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
+  a.G = p->num_q_heads / p->num_kv_heads;
+  a.nqt = (p->seqlen_q + p->block_q - 1) / p->block_q;
+  a.nkb = (p->seqlen_k + p->block_k - 1) / p->block_k;
+  a.causal = p->causal; a.num_splits = p->num_splits; a.stats_only = p->stats_only ? 1 : 0;
+  a.scale = (float)scale;
+  a.scale_log2 = (float)(scale * 1.4426950408889634);
+  a.thr_raw = thr_raw_from(ln_lam, scale);
+  if ((double)a.B * a.Hq * a.nqt > 2147483647.0 || (double)a.B * a.Hq * a.nqt * a.nkb > 2147483647.0)
+    return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
+
+  hipError_t e;
+  if (p->in_dtype == BLASST_BF16)
+    e = blasst::launch_prefill_bf16(a, D, p->block_k, p->out_dtype == BLASST_FP32, (hipStream_t)stream);
+  else
+    e = blasst::launch_prefill_f32(a, D, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BLASST_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static blasst_status validate_decode(const blasst_decode_params *p, bool need_ptrs, size_t *ws_bytes) {
+  if (!p) return fail(BLASST_ERR_INVALID_ARG, "params is NULL");
+  if (p->struct_size != sizeof(blasst_decode_params))
+    return fail(BLASST_ERR_INVALID_ARG, "struct_size %zu != %zu", p->struct_size, sizeof(blasst_decode_params));
+  if (p->reserved != 0) return fail(BLASST_ERR_INVALID_ARG, "reserved must be 0");
+  if (p->batch < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 || p->head_dim_qk < 1 || p->head_dim_v < 1)
+    return fail(BLASST_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (p->num_q_heads % p->num_kv_heads)
+    return fail(BLASST_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (p->page_size < 1 || p->max_pages_per_seq < 1 || p->num_pages < 1)
+    return fail(BLASST_ERR_INVALID_ARG, "page_size, max_pages_per_seq and num_pages must be >= 1");
+  if (p->block_k < 1 || p->block_k % p->page_size)
+    return fail(BLASST_ERR_INVALID_ARG, "block_k must be a positive multiple of page_size");
+  if (p->num_splits < 1) return fail(BLASST_ERR_INVALID_ARG, "num_splits must be >= 1");
+  const int G = p->num_q_heads / p->num_kv_heads;
+  const int tr = p->tile_rows == 0 ? G : p->tile_rows;
+  if (tr < 1 || G % tr) return fail(BLASST_ERR_INVALID_ARG, "tile_rows must divide num_q_heads/num_kv_heads");
+  if (p->in_dtype != BLASST_BF16 && p->in_dtype != BLASST_FP32) return fail(BLASST_ERR_INVALID_ARG, "bad in_dtype");
+  if (p->out_dtype != BLASST_BF16 && p->out_dtype != BLASST_FP32) return fail(BLASST_ERR_INVALID_ARG, "bad out_dtype");
+  if (!std::isfinite(p->softmax_scale)) return fail(BLASST_ERR_INVALID_ARG, "softmax_scale must be finite");
+  double ln_lam;
+  const char *why = "";
+  if (!resolve_threshold(p->thr, 1.0, &ln_lam, &why)) return fail(BLASST_ERR_INVALID_ARG, "%s", why);
+  if (need_ptrs) {
+    if (!p->q || !p->k_cache || !p->block_table || !p->seq_lens)
+      return fail(BLASST_ERR_INVALID_ARG, "q, k_cache, block_table and seq_lens must be non-NULL");
+    if (!p->stats_only && !p->o) return fail(BLASST_ERR_INVALID_ARG, "o must be non-NULL unless stats_only");
+  }
+  // ---- kernel coverage ----
+  if (p->in_dtype != BLASST_BF16) return fail(BLASST_ERR_UNSUPPORTED, "decode supports bf16 inputs");
+  if (p->page_size != 16 || p->block_k != 64) return fail(BLASST_ERR_UNSUPPORTED, "decode supports page 16, block 64");
+  const bool latent = p->v_cache == nullptr;
+  if (latent) {
+    if (p->num_kv_heads != 1 || p->head_dim_qk != 576 || p->head_dim_v != 512 || tr != 128)
+      return fail(BLASST_ERR_UNSUPPORTED, "latent decode supports 1 kv head, dims 576/512, tile_rows 128");
+  } else {
+    if (p->head_dim_qk != 128 || p->head_dim_v != 128 || tr > 16)
+      return fail(BLASST_ERR_UNSUPPORTED, "decode supports head dim 128 and tile_rows <= 16");
+  }
+  if (need_ptrs && (!aligned16(p->q) || !aligned16(p->k_cache) || (p->v_cache && !aligned16(p->v_cache)) ||
+                    (p->o && !aligned16(p->o))))
+    return fail(BLASST_ERR_UNSUPPORTED, "q, caches and o must be 16-byte aligned");
+  const size_t parts = (size_t)p->batch * p->num_q_heads * p->num_splits;
+  size_t bytes = 0;
+  if (p->num_splits > 1) {
+    const size_t o_bytes = (parts * p->head_dim_v * sizeof(float) + 255) / 256 * 256;
+    bytes = o_bytes + (parts * sizeof(float) + 255) / 256 * 256;
+  }
+  *ws_bytes = bytes;
+  return BLASST_OK;
+}
+
+size_t blasst_decode_workspace_size(const blasst_decode_params *p) {
+  size_t bytes = 0;
+  if (validate_decode(p, false, &bytes) != BLASST_OK) return 0;
+  ok();
+  return bytes;
+}
+
+blasst_status blasst_decode(const blasst_decode_params *p, void *stream) {
+  size_t ws = 0;
+  blasst_status st = validate_decode(p, true, &ws);
+  if (st != BLASST_OK) return st;
+  if (ws > 0 && !p->stats_only) {
+    if (!p->workspace || p->workspace_bytes < ws)
+      return fail(BLASST_ERR_WORKSPACE, "workspace of %zu bytes required", ws);
+    if (reinterpret_cast<uintptr_t>(p->workspace) & 255u)
+      return fail(BLASST_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  const double scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0 / std::sqrt((double)p->head_dim_qk);
+  const int G = p->num_q_heads / p->num_kv_heads;
+  const int tr = p->tile_rows == 0 ? G : p->tile_rows;
+  blasst::DecodeArgs a{};
+  a.q = p->q; a.kc = p->k_cache; a.vc = p->v_cache; a.table = p->block_table; a.seq_lens = p->seq_lens;
+  a.o = p->o; a.lse = p->lse; a.mask = p->skip_mask; a.crit = p->crit; a.counters = p->counters;
+  if (ws > 0 && !p->stats_only) {
+    const size_t parts = (size_t)p->batch * p->num_q_heads * p->num_splits;
+    const size_t o_bytes = (parts * p->head_dim_v * sizeof(float) + 255) / 256 * 256;
+    a.ws_o = (float *)p->workspace;
+    a.ws_lse = (float *)((char *)p->workspace + o_bytes);
+  }
+  a.B = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = G; a.tile_rows = tr; a.n_rt = G / tr;
+  a.page = p->page_size; a.max_pages = p->max_pages_per_seq; a.block_k = p->block_k;
+  a.nkb = (int)(((int64_t)p->max_pages_per_seq * p->page_size + p->block_k - 1) / p->block_k);
+  a.num_splits = p->num_splits; a.stats_only = p->stats_only ? 1 : 0; a.out_f32 = p->out_dtype == BLASST_FP32;
+  a.scale = (float)scale;
+  a.scale_log2 = (float)(scale * 1.4426950408889634);
+  if (p->thr.mode == BLASST_THR_LAMBDA) {
+    a.thr_mode = 0;
+    a.thr_raw = thr_raw_from(p->thr.lambda == 0.0 ? -INFINITY : std::log(p->thr.lambda), scale);
+  } else {
+    a.thr_mode = 1;
+    a.a = (float)p->thr.a;
+  }
+  hipError_t e = p->v_cache ? blasst::launch_decode_gqa(a, (hipStream_t)stream)
+                            : blasst::launch_decode_latent(a, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return fail(BLASST_ERR_UNSUPPORTED, "no decode kernel for this shape");
+  if (e != hipSuccess) return fail(BLASST_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Shared device helpers of the BLASST HIP kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace blasst {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Mask byte values.
+constexpr uint8_t kKept = 0, kSkipped = 1, kNotLive = 2;
+
+// Arguments of the prefill kernels (one launch = the whole problem).
+struct PrefillArgs {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  uint8_t *mask;
+  float *crit;
+  unsigned long long *counters;
+  int64_t qs[3], ks[3], vs[3], os[3];  // element strides: batch, head, token
+  int B, Lq, Lk, Hq, Hkv, G;           // G = Hq / Hkv
+  int nqt, nkb;                        // query tiles per head, key blocks per row of the mask
+  int causal, num_splits, stats_only;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e): exp(scale*(s - m)) = exp2(scale_log2*(s - m))
+  float thr_raw;     // ln(lambda) / scale: skip iff (m~ - m) < thr_raw on raw logits
+};
+
+// Arguments of the paged decode kernels.
+struct DecodeArgs {
+  const void *q, *kc, *vc;
+  const int32_t *table, *seq_lens;
+  void *o;
+  float *lse;
+  uint8_t *mask;
+  float *crit;
+  unsigned long long *counters;
+  float *ws_o;    // [B][Hq][S][Dv] per-split normalised outputs (num_splits > 1)
+  float *ws_lse;  // [B][Hq][S]
+  int B, Hq, Hkv, G, tile_rows, n_rt;
+  int page, max_pages, block_k, nkb;
+  int num_splits, stats_only, out_f32;
+  int thr_mode;    // 0: fixed lambda (thr_raw valid); 1: lambda_b = min(1, a / seq_lens[b])
+  float thr_raw;   // ln(lambda) / scale
+  float a;         // for thr_mode 1
+  float scale, scale_log2;
+};
+
+// Row vote of the skip rule on raw (unscaled) logits: the row votes "skip" when
+// m~ - m < thr, written as !(m~ - m >= thr) so that a row without visible keys (m~ = -inf, giving
+// -inf or NaN) votes skip, and a row whose running max is still -inf (giving +inf) votes keep.
+__device__ __forceinline__ bool row_votes_skip(float m_blk, float m_run, float thr) {
+  return !((m_blk - m_run) >= thr);
+}
+
+// Critical value of one row in raw units: m~ - m with (-inf) - x = -inf, x - (-inf) = +inf.
+__device__ __forceinline__ float row_crit(float m_blk, float m_run) {
+  return m_blk == kNegInf ? kNegInf : m_blk - m_run;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max over lanes l and l ^ 32
+__device__ __forceinline__ float max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+
+// max over the 32 lanes that share l / 32 ... used for per-wave reductions of per-row values that
+// are replicated in both halves: a full butterfly over offsets 16, 8, 4, 2, 1.
+__device__ __forceinline__ float max_lanes32(float x) {
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+// max over the 16-lane groups: lanes l, l ^ 16, l ^ 32, l ^ 48
+__device__ __forceinline__ float max_xor16_32(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ __forceinline__ float sum_xor16_32(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// 16-byte chunk swizzle used by the LDS tiles: chunk c of row r is stored at chunk c ^ swz(r).
+// For 8 consecutive rows starting at a multiple of 8 the swizzle takes 8 distinct values, and for
+// rows 8*i + e (i = 0..NCH-1, fixed e) it is a bijection of i, so both the MFMA operand reads and the
+// transposed tile writes spread over the banks.
+template <int NCH>
+__device__ __forceinline__ int swz(int row) {
+  return (row ^ (row >> 3)) & (NCH - 1);
+}
+
+}  // namespace blasst

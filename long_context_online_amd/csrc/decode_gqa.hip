@@ -1,0 +1,322 @@
+// BLASST decode over a paged KV cache, split along the keys (GQA / MHA / MQA, head dim 128).
+//
+// Method: for each KV block, the block-local max of the tile's query rows is compared with the
+// running max, and a block that every row votes to skip is dropped: its V block is never loaded
+// and it gets no exp and no P.V.  The decision is taken at the K-load stage, and K is processed in
+// batches of several blocks before the V loads of the surviving blocks are issued together, so
+// the skip does not stall the load pipeline (pages: xllm-io review, 解码内核优化; gist.science (de),
+// 3. Kernel-Design).  Splitting the keys into num_splits chunks merged by a log-sum-exp combine is
+// part of the defined semantics here (each chunk restarts the running max).
+//
+// MI355X design:
+//   * one workgroup = (sequence, kv head, row tile, split); 4 waves; wave w owns the w-th 16-token
+//     page of every 64-token block, so each wave issues page-sized, page-aligned loads;
+//   * K-first batch of NB blocks: each wave loads its NB K pages straight into MFMA operand
+//     registers (16 bytes per lane per k-step), computes S^T = K q^T with
+//     v_mfma_f32_16x16x32_bf16 (the tile's <= 16 q heads are the N columns), and publishes its
+//     per-page row maxima in LDS; after one barrier every thread derives the block maxima and the
+//     sequential decisions of the whole batch (the same values in every wave, so the branch is
+//     uniform);
+//   * then the V pages of the surviving blocks only are loaded: the V cache stores each page
+//     transposed ([dv][token]), so a lane's 4 consecutive tokens of one dv row are one 8-byte load
+//     and a 16-row m-tile is one 512-byte contiguous read; P^T goes from the score registers to the
+//     B operand of v_mfma_f32_16x16x16_bf16 without any shuffle;
+//   * the next batch's K loads are issued before the PV products of the current batch, so K
+//     traffic overlaps the arithmetic;
+//   * all waves use the same running max, so their partial outputs add up; one LDS reduction per
+//     split, then either the final output (one split) or a per-split partial for the combine
+//     kernel.
+#include "common.hpp"
+
+namespace blasst {
+
+namespace {
+constexpr int D = 128, PAGE = 16, BK = 64, NWAVE = 4, NB = 4;
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
+  __shared__ float sPmax[NB][NWAVE][16];
+  __shared__ float sRed[NWAVE][16][D + 4];
+  __shared__ float sL[NWAVE][16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;   // query column (q head inside the tile)
+  const int grp = lane >> 4; // 16-lane group
+
+  int bid = blockIdx.x;
+  const int split = bid % a.num_splits;
+  bid /= a.num_splits;
+  const int rt = bid % a.n_rt;
+  bid /= a.n_rt;
+  const int g = bid % a.Hkv;
+  const int b = bid / a.Hkv;
+
+  const int cap = a.max_pages * PAGE;
+  const int L = min(a.seq_lens[b], cap);
+  const int J = (L + BK - 1) / BK;
+  const int chunk = (J + a.num_splits - 1) / a.num_splits;
+  const int j0 = split * chunk;
+  const int j1 = min(J, j0 + chunk);
+  const bool col_ok = n < a.tile_rows;
+  const int hq = g * a.G + rt * a.tile_rows + n;
+
+  float thr = a.thr_raw;
+  if (a.thr_mode == 1) {
+    const float lam = fminf(1.f, a.a / (float)L);
+    thr = lam > 0.f ? __logf(lam) / a.scale : kNegInf;
+  }
+
+  // q fragments: B operand of S^T = K q^T; lane holds dims kk*32 + grp*8 .. +7 of query column n
+  bf16x8 qf[4];
+  const __bf16 *qp = (const __bf16 *)a.q + ((int64_t)b * a.Hq + hq) * D;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) qf[kk] = col_ok ? *(const bf16x8 *)(qp + kk * 32 + grp * 8) : bf16x8{};
+
+  const __bf16 *kc = (const __bf16 *)a.kc;
+  const __bf16 *vc = (const __bf16 *)a.vc;
+  const int32_t *table = a.table + (int64_t)b * a.max_pages;
+  const int64_t page_stride = (int64_t)a.Hkv * PAGE * D;  // elements per physical page (all heads)
+
+  float m_dec = kNegInf, m_acc = kNegInf, l_part = 0.f;
+  f32x4 o_acc[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) o_acc[i] = f32x4{};
+  unsigned live_cnt = 0, skip_cnt = 0;
+  const int mask_row = ((b * a.Hkv + g) * a.n_rt + rt) * a.nkb;
+
+  u32x4 kreg[NB][4];
+  auto load_k = [&](int jb) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int pg = (jb + i) * (BK / PAGE) + wave;
+      const bool ok = (jb + i) < j1 && pg * PAGE < L;
+      const int pid = ok ? table[pg] : 0;
+      const __bf16 *src = kc + (int64_t)pid * page_stride + ((int64_t)g * PAGE + n) * D + grp * 8;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kreg[i][kk] = ok ? *(const u32x4 *)(src + kk * 32) : u32x4{};
+    }
+  };
+
+  if (j0 < j1) load_k(j0);
+  for (int jb = j0; jb < j1; jb += NB) {
+    const int nb = min(NB, j1 - jb);
+    // ---- scores of this wave's page of each block in the batch ----
+    f32x4 s[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      s[i] = f32x4{};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        s[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[i][kk]), qf[kk], s[i], 0, 0, 0);
+      // keys past the sequence end (and blocks past the batch) are masked out
+      const int keyb = (jb + i) * BK + wave * PAGE + grp * 4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (i >= nb || keyb + r >= L) s[i][r] = kNegInf;
+      float pm = fmaxf(fmaxf(s[i][0], s[i][1]), fmaxf(s[i][2], s[i][3]));
+      pm = max_xor16_32(pm);
+      if (grp == 0) sPmax[i][wave][n] = pm;
+    }
+    __syncthreads();
+    // ---- in-batch sequential decisions (identical in every wave) ----
+    int keep_bits = 0;
+    float mblk[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      float mb = fmaxf(fmaxf(sPmax[i][0][n], sPmax[i][1][n]), fmaxf(sPmax[i][2][n], sPmax[i][3][n]));
+      if (!col_ok) mb = kNegInf;
+      mblk[i] = mb;
+      if (i < nb) {
+        const int j = jb + i;
+        if (j == j0) m_dec = kNegInf;
+        const bool skip_row = row_votes_skip(mb, m_dec, thr);
+        const bool keep = __ballot(!skip_row) != 0ull;
+        if (a.crit) {
+          float c = row_crit(mb, m_dec);
+          c = fmaxf(c, __shfl_xor(c, 8));
+          c = fmaxf(c, __shfl_xor(c, 4));
+          c = fmaxf(c, __shfl_xor(c, 2));
+          c = fmaxf(c, __shfl_xor(c, 1));
+          if (tid == 0) a.crit[mask_row + j] = c * a.scale;
+        }
+        if (tid == 0 && a.mask) a.mask[mask_row + j] = keep ? kKept : kSkipped;
+        m_dec = fmaxf(m_dec, mb);
+        keep_bits |= (keep ? 1 : 0) << i;
+        ++live_cnt;
+        if (!keep) ++skip_cnt;
+      }
+    }
+    if (a.stats_only) keep_bits = 0;
+    // ---- V loads of the surviving blocks only ----
+    u32x2 vreg[NB][D / 16];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (keep_bits & (1 << i)) {
+        const int pg = (jb + i) * (BK / PAGE) + wave;
+        const bool ok = pg * PAGE < L;
+        const int pid = ok ? table[pg] : 0;
+        const __bf16 *src = vc + (int64_t)pid * page_stride + (int64_t)g * D * PAGE + n * PAGE + grp * 4;
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) vreg[i][mt] = ok ? *(const u32x2 *)(src + mt * 16 * PAGE) : u32x2{};
+      }
+    }
+    // ---- prefetch the next batch's K while the PV products run ----
+    if (jb + NB < j1) load_k(jb + NB);
+    // ---- kept blocks: online softmax and O^T += V^T P^T ----
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (!(keep_bits & (1 << i))) continue;
+      const float m_new = fmaxf(m_acc, mblk[i]);
+      if (__ballot(m_new > m_acc) != 0ull) {
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_acc - m_new) * a.scale_log2);
+        l_part *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) o_acc[mt] *= alpha;
+        m_acc = m_new;
+      }
+      const float base = (m_acc == kNegInf) ? 0.f : m_acc * a.scale_log2;
+      bf16x4 pf;
+      const int keyb = (jb + i) * BK + wave * PAGE + grp * 4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(s[i][r], a.scale_log2, -base));
+        l_part += p;
+        pf[r] = (__bf16)p;
+      }
+      // tokens past the sequence end hold arbitrary bytes: zero their V so 0 * NaN cannot appear
+      const bool tail = keyb + 3 >= L;
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) {
+        u32x2 vv = vreg[i][mt];
+        if (tail) {
+          if (keyb + 0 >= L) vv[0] &= 0xffff0000u;
+          if (keyb + 1 >= L) vv[0] &= 0x0000ffffu;
+          if (keyb + 2 >= L) vv[1] &= 0xffff0000u;
+          if (keyb + 3 >= L) vv[1] &= 0x0000ffffu;
+        }
+        o_acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vv), pf, o_acc[mt], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // sPmax is rewritten by the next batch
+  }
+
+  if (tid == 0 && a.counters) {
+    atomicAdd(&a.counters[0], (unsigned long long)live_cnt);
+    atomicAdd(&a.counters[1], (unsigned long long)skip_cnt);
+  }
+  if (a.mask || a.crit) {
+    // blocks of the row that no split covers (past the sequence end) are not live; split 0 writes them
+    if (split == 0)
+      for (int j = J + tid; j < a.nkb; j += 256) {
+        if (a.mask) a.mask[mask_row + j] = kNotLive;
+        if (a.crit) a.crit[mask_row + j] = __builtin_nanf("");
+      }
+  }
+  if (a.stats_only) return;
+
+  // ---- reduce the 4 waves' partial sums (all used the same running max) ----
+  const float lw = sum_xor16_32(l_part);
+  if (grp == 0) sL[wave][n] = lw;
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sRed[wave][n][mt * 16 + grp * 4 + r] = o_acc[mt][r];
+  __syncthreads();
+  // 256 threads: thread -> (column, 8 dv)
+  const int col = tid >> 4;          // 0..15
+  const int dv0 = (tid & 15) * 8;    // 0..120
+  // m_acc of column col lives in the lanes with n == col (the same value in every wave)
+  const float m_col = __shfl(m_acc, col);
+  if (col < a.tile_rows) {
+    const float l_tot = sL[0][col] + sL[1][col] + sL[2][col] + sL[3][col];
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float ov[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      ov[e] = (sRed[0][col][dv0 + e] + sRed[1][col][dv0 + e] + sRed[2][col][dv0 + e] + sRed[3][col][dv0 + e]) * inv;
+    const float lse = l_tot > 0.f ? m_col * a.scale + __logf(l_tot) : kNegInf;
+    const int h = g * a.G + rt * a.tile_rows + col;
+    if (a.num_splits == 1) {
+      const int64_t ob = ((int64_t)b * a.Hq + h) * D + dv0;
+      if (OUT_F32) {
+        f32x4 w0 = {ov[0], ov[1], ov[2], ov[3]}, w1 = {ov[4], ov[5], ov[6], ov[7]};
+        *(f32x4 *)((float *)a.o + ob) = w0;
+        *(f32x4 *)((float *)a.o + ob + 4) = w1;
+      } else {
+        u32x4 w;
+        w[0] = pack_bf16x2(ov[0], ov[1]);
+        w[1] = pack_bf16x2(ov[2], ov[3]);
+        w[2] = pack_bf16x2(ov[4], ov[5]);
+        w[3] = pack_bf16x2(ov[6], ov[7]);
+        *(u32x4 *)((__bf16 *)a.o + ob) = w;
+      }
+      if (a.lse && dv0 == 0) a.lse[(int64_t)b * a.Hq + h] = lse;
+    } else {
+      const int64_t pb = (((int64_t)b * a.Hq + h) * a.num_splits + split);
+      float *wo = a.ws_o + pb * D + dv0;
+      f32x4 w0 = {ov[0], ov[1], ov[2], ov[3]}, w1 = {ov[4], ov[5], ov[6], ov[7]};
+      *(f32x4 *)wo = w0;
+      *(f32x4 *)(wo + 4) = w1;
+      if (dv0 == 0) a.ws_lse[pb] = lse;
+    }
+  }
+}
+
+// Log-sum-exp merge of the per-split partials: one workgroup per (sequence, q head), one thread
+// per 4 output channels.
+template <bool OUT_F32>
+__global__ __launch_bounds__(128) void decode_combine_kernel(const float *ws_o, const float *ws_lse, void *o,
+                                                              float *lse_out, int S, int Dv) {
+  const int bh = blockIdx.x;
+  const float *pl = ws_lse + (int64_t)bh * S;
+  float mx = kNegInf;
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, pl[s]);
+  float tot = 0.f;
+  for (int s = 0; s < S; ++s) tot += (pl[s] == kNegInf) ? 0.f : __expf(pl[s] - mx);
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  for (int c = threadIdx.x * 4; c < Dv; c += blockDim.x * 4) {
+    f32x4 acc = f32x4{};
+    for (int s = 0; s < S; ++s) {
+      if (pl[s] == kNegInf) continue;
+      const float w = __expf(pl[s] - mx);
+      acc += w * *(const f32x4 *)(ws_o + ((int64_t)bh * S + s) * Dv + c);
+    }
+    acc *= inv;
+    if (OUT_F32) {
+      *(f32x4 *)((float *)o + (int64_t)bh * Dv + c) = acc;
+    } else {
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[0], acc[1]);
+      w[1] = pack_bf16x2(acc[2], acc[3]);
+      *(u32x2 *)((__bf16 *)o + (int64_t)bh * Dv + c) = w;
+    }
+  }
+  if (lse_out && threadIdx.x == 0) lse_out[bh] = tot > 0.f ? mx + __logf(tot) : kNegInf;
+}
+
+hipError_t launch_decode_combine(const DecodeArgs &a, int Dv, hipStream_t st) {
+  const int grid = a.B * a.Hq;
+  if (a.out_f32)
+    hipLaunchKernelGGL(decode_combine_kernel<true>, dim3(grid), dim3(128), 0, st, a.ws_o, a.ws_lse, a.o, a.lse,
+                       a.num_splits, Dv);
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<false>, dim3(grid), dim3(128), 0, st, a.ws_o, a.ws_lse, a.o, a.lse,
+                       a.num_splits, Dv);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_gqa(const DecodeArgs &a, hipStream_t st) {
+  const int grid = a.B * a.Hkv * a.n_rt * a.num_splits;
+  if (a.out_f32)
+    hipLaunchKernelGGL(decode_gqa_kernel<true>, dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(decode_gqa_kernel<false>, dim3(grid), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_splits == 1 || a.stats_only) return e;
+  return launch_decode_combine(a, D, st);
+}
+
+}  // namespace blasst

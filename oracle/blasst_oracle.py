@@ -114,10 +114,13 @@ def _diff(a, b):
     return out
 
 
-def tile_sequential(q_rows, keys, values, visible, block_k, num_splits, ln_lam, scale):
+def tile_sequential(q_rows, keys, values, visible, block_k, num_splits, ln_lam, scale, force=None):
     """BLASST forward for one query tile, block by block, left to right (the step-by-step rule).
 
     q_rows [R, Dqk], keys [N, Dqk], values [N, Dv], visible [R, N] bool.
+    force: optional {block index: KEPT or SKIPPED} overriding the rule for those blocks.  It exists
+    for blocks whose critical value lies within rounding distance of ln(lambda), where either
+    decision is a correct result (a reading); the caller decides which blocks qualify.
     Returns a dict:
       o [R, Dv], lse [R]   combined output over the splits
       mask [nb] int8       KEPT / SKIPPED / NOT_LIVE per key block
@@ -158,6 +161,10 @@ def tile_sequential(q_rows, keys, values, visible, block_k, num_splits, ln_lam, 
             split_of[j] = s_idx
             if pos == 0 and skip:
                 raise AssertionError("first block of a split was skipped")
+            if force is not None and j in force:
+                skip = force[j] == SKIPPED
+                if skip:
+                    m_after = m                             # a skipped block adds nothing
             if skip:
                 mask[j] = SKIPPED
                 # nothing is added: no exp, no V, no P.V; the running max cannot rise
@@ -245,7 +252,8 @@ def causal_visible(rows, n_keys, Lq, Lk):
     return np.arange(n_keys)[None, :] <= (rows[:, None] + (Lk - Lq))
 
 
-def prefill_tile(q, k, v, b, hq, qt, *, causal, block_q, block_k, num_splits, ln_lam, scale=None):
+def prefill_tile(q, k, v, b, hq, qt, *, causal, block_q, block_k, num_splits, ln_lam, scale=None,
+                 force=None):
     """One prefill query tile: rows [qt*block_q, ...) of q head hq in batch b.
 
     q [B, Hq, Lq, Dqk], k [B, Hkv, Lk, Dqk], v [B, Hkv, Lk, Dv] (any array-likes, upcast to
@@ -268,7 +276,7 @@ def prefill_tile(q, k, v, b, hq, qt, *, causal, block_q, block_k, num_splits, ln
     return tile_sequential(np.asarray(q[b, hq, r0:r1], dtype=np.float64),
                            np.asarray(k[b, g], dtype=np.float64),
                            np.asarray(v[b, g], dtype=np.float64),
-                           vis, block_k, num_splits, ln_lam, scale)
+                           vis, block_k, num_splits, ln_lam, scale, force=force)
 
 
 def prefill(q, k, v, *, causal, block_q, block_k, num_splits=1, lam=None, a=None, scale=None):
@@ -321,7 +329,7 @@ def gather_pages(k_cache, v_cache_t, block_table, b, g, seq_len, page_size, head
 
 
 def decode_tile(q, k_cache, v_cache_t, block_table, seq_lens, b, g, rt, *, page_size, block_k,
-                num_splits, ln_lam, tile_rows, head_dim_v, scale=None):
+                num_splits, ln_lam, tile_rows, head_dim_v, scale=None, force=None):
     """One decode tile: the tile_rows q heads [g*G + rt*tile_rows, ...) of sequence b that share
     kv head g (G = Hq/Hkv).  One query token per sequence sees all keys < seq_len."""
     B, Hq, D = q.shape
@@ -334,7 +342,7 @@ def decode_tile(q, k_cache, v_cache_t, block_table, seq_lens, b, g, rt, *, page_
     h0 = g * G + rt * tile_rows
     rows = np.asarray(q[b, h0:h0 + tile_rows], dtype=np.float64)
     vis = np.ones((rows.shape[0], L), dtype=bool)
-    return tile_sequential(rows, K, V, vis, block_k, num_splits, ln_lam, scale)
+    return tile_sequential(rows, K, V, vis, block_k, num_splits, ln_lam, scale, force=force)
 
 
 def decode(q, k_cache, v_cache_t, block_table, seq_lens, *, page_size, block_k, num_splits,

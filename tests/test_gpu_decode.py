@@ -1,0 +1,151 @@
+"""GPU parity of blasst_decode (paged split-KV, through the C ABI) against the fp64 oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import Report, check_tile, host64
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import long_context_online_amd as m
+    m.lib()
+    return m
+
+
+def _run(m, d, *, splits, lam=None, a=None, tile_rows=0, out_dtype=torch.float32, stats_only=False):
+    B, Hq, D = d.q.shape
+    Hkv = d.k_cache.shape[1]
+    G = Hq // Hkv
+    tr = G if tile_rows == 0 else tile_rows
+    dev = d.q.device
+    max_pages = d.block_table.shape[1]
+    nkb = -(-(max_pages * d.page_size) // 64)
+    o = None if stats_only else torch.full((B, Hq, d.head_dim_v), float("nan"), dtype=out_dtype, device=dev)
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=dev)
+    mask = torch.full((B, Hkv, G // tr, nkb), 7, dtype=torch.uint8, device=dev)
+    crit = torch.full((B, Hkv, G // tr, nkb), 12345.0, dtype=torch.float32, device=dev)
+    cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+    kw = dict(page_size=d.page_size, block_k=64, num_splits=splits, lam=lam, a=a, tile_rows=tile_rows,
+              head_dim_v=d.head_dim_v, lse=None if stats_only else lse, skip_mask=mask, crit=crit,
+              counters=cnt, stats_only=stats_only)
+    nbytes = m.blasst_decode_workspace_size(d.q, d.k_cache, d.v_cache_t, d.block_table, d.seq_lens, o, **kw)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev) if nbytes else None
+    m.blasst_decode(d.q, d.k_cache, d.v_cache_t, d.block_table, d.seq_lens, o, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    return o, lse, mask, crit, cnt
+
+
+def _tile_inputs(d, b):
+    """Host fp64 copies of what one sequence's tiles read: its query, its pages (renumbered 0..n-1)."""
+    L = int(d.seq_lens[b])
+    npg = -(-L // d.page_size)
+    ids = d.block_table[b, :npg].long()
+    kc = host64(d.k_cache[ids])
+    vc = host64(d.v_cache_t[ids]) if d.v_cache_t is not None else None
+    bt = np.arange(npg, dtype=np.int64)[None, :]
+    return host64(d.q[b:b + 1]), kc, vc, bt, np.array([L])
+
+
+def _compare(d, res, *, splits, lam=None, a=None, tiles=None, tile_rows=0, out_bf16=False):
+    o, lse, mask, crit, cnt = res
+    sl = d.seq_lens.cpu().numpy()
+    mh, ch = mask.cpu().numpy(), crit.cpu().numpy()
+    oh = host64(o) if o is not None else None
+    lh = lse.cpu().double().numpy()
+    B, Hq, _ = d.q.shape
+    Hkv = d.k_cache.shape[1]
+    G = Hq // Hkv
+    tr = G if tile_rows == 0 else tile_rows
+    rep = Report()
+    if tiles is None:
+        tiles = [(b, g, rt) for b in range(B) for g in range(Hkv) for rt in range(G // tr)]
+    cache = {}
+    for (b, g, rt) in tiles:
+        if b not in cache:
+            cache = {b: _tile_inputs(d, b)}
+        qh, kc, vc, bt, sl1 = cache[b]
+        ln_lam = oracle.ln_threshold(lam=lam) if lam is not None else oracle.ln_threshold(a=a, L=int(sl[b]))
+        kw = dict(page_size=d.page_size, block_k=64, num_splits=splits, ln_lam=ln_lam, tile_rows=tr,
+                  head_dim_v=d.head_dim_v)
+        ref = oracle.decode_tile(qh, kc, vc, bt, sl1, 0, g, rt, **kw)
+        h0 = g * G + rt * tr
+        nb = ref["mask"].shape[0]
+        assert np.all(mh[b, g, rt, nb:] == 2)
+        check_tile(rep, ref, mh[b, g, rt], ch[b, g, rt], ln_lam,
+                   lambda f: oracle.decode_tile(qh, kc, vc, bt, sl1, 0, g, rt, force=f, **kw),
+                   None if oh is None else oh[b, h0:h0 + tr], None if oh is None else lh[b, h0:h0 + tr],
+                   out_bf16=out_bf16)
+    return rep
+
+
+@pytest.mark.parametrize("splits", [1, 3, 16])
+@pytest.mark.parametrize("a", [0.0, 2.0, 20.0])
+def test_gqa_paged_ragged(splits, a):
+    """32 q / 8 kv heads, d = 128, ragged sequence lengths (including a one-page and a one-token
+    sequence), 16-token pages in a permuted pool with NaN spare pages."""
+    m = _lib()
+    lens = [1000, 64, 17, 2048, 1, 333]
+    d = synth.decode_inputs(batch=len(lens), hq=32, hkv=8, ctx=None, d=128, seq_lens=lens, seed=3,
+                            device="cuda")
+    res = _run(m, d, splits=splits, a=a)
+    rep = _compare(d, res, splits=splits, a=a)
+    print(f"S={splits} a={a}: {rep}")
+    o, _, mask, _, cnt = res
+    mh = mask.cpu().numpy()
+    assert int(cnt[0]) == int((mh != 2).sum()) and int(cnt[1]) == int((mh == 1).sum())
+    if a == 0.0:
+        assert rep.skipped == 0
+
+
+@pytest.mark.parametrize("tile_rows", [1, 2, 4])
+def test_tile_rows_and_bf16_out(tile_rows):
+    m = _lib()
+    d = synth.decode_inputs(batch=3, hq=16, hkv=4, ctx=900, d=128, seed=4, device="cuda")
+    res = _run(m, d, splits=4, lam=0.003, tile_rows=tile_rows, out_dtype=torch.bfloat16)
+    rep = _compare(d, res, splits=4, lam=0.003, tile_rows=tile_rows, out_bf16=True)
+    print(rep)
+
+
+def test_mha_and_mqa():
+    m = _lib()
+    for hq, hkv in [(8, 8), (8, 1)]:
+        d = synth.decode_inputs(batch=2, hq=hq, hkv=hkv, ctx=700, d=128, seed=5, device="cuda")
+        res = _run(m, d, splits=2, lam=0.01)
+        print(_compare(d, res, splits=2, lam=0.01))
+
+
+def test_stats_only_matches_full_pass():
+    m = _lib()
+    d = synth.decode_inputs(batch=4, hq=32, hkv=8, ctx=2000, d=128, seed=6, device="cuda")
+    full = _run(m, d, splits=4, lam=0.005)
+    st = _run(m, d, splits=4, lam=0.005, stats_only=True)
+    assert torch.equal(full[2], st[2]) and torch.equal(full[3], st[3]) and torch.equal(full[4], st[4])
+
+
+@pytest.mark.parametrize("ctx", [32768])
+def test_gqa_decode_full_size_sampled(ctx):
+    """Batch 32, 32 q / 8 kv heads, d = 128, 16-token pages, 64-token blocks, 16 splits (the
+    benchmark's launch configuration); sampled tiles against the oracle, all masks consistent with
+    the critical values."""
+    m = _lib()
+    d = synth.decode_inputs(batch=32, hq=32, hkv=8, ctx=ctx, d=128, seed=synth.config_seed(3), device="cuda")
+    a = 0.02 * ctx
+    res = _run(m, d, splits=16, a=a)
+    o, lse, mask, crit, cnt = res
+    ln_lam = math.log(min(1.0, a / ctx))
+    mh, ch = mask.cpu().numpy(), crit.cpu().numpy()
+    live = mh != 2
+    decided = np.where(live, np.where(ch < ln_lam, 1, 0), 2)
+    band = live & (np.abs(ch - ln_lam) < 1e-3)
+    assert np.array_equal(decided[~band], mh[~band])
+    assert torch.isfinite(o).all()
+    tiles = [(0, 0, 0), (5, 3, 0), (17, 7, 0), (31, 4, 0)]
+    rep = _compare(d, res, splits=16, a=a, tiles=tiles)
+    print(f"sparsity {float((mh == 1).sum()) / live.sum():.3f}; {rep}")

@@ -1,0 +1,163 @@
+"""GPU parity of blasst_prefill (through the C ABI) against the fp64 oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import Report, check_tile, host64
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import long_context_online_amd as m
+    m.lib()
+    return m
+
+
+def _run(m, q, k, v, *, causal, bq, bk, splits, lam=None, a=None, out_dtype=torch.float32, stats_only=False):
+    B, Hq, Lq, D = q.shape
+    Lk, Dv = k.shape[2], v.shape[3]
+    nqt, nkb = -(-Lq // bq), -(-Lk // bk)
+    dev = q.device
+    o = None if stats_only else torch.full((B, Hq, Lq, Dv), float("nan"), dtype=out_dtype, device=dev)
+    lse = torch.full((B, Hq, Lq), float("nan"), dtype=torch.float32, device=dev)
+    mask = torch.full((B, Hq, nqt, nkb), 7, dtype=torch.uint8, device=dev)
+    crit = torch.full((B, Hq, nqt, nkb), 12345.0, dtype=torch.float32, device=dev)
+    cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+    m.blasst_prefill(q, k, v, o, causal=causal, block_q=bq, block_k=bk, num_splits=splits, lam=lam, a=a,
+                     lse=None if stats_only else lse, skip_mask=mask, crit=crit, counters=cnt,
+                     stats_only=stats_only)
+    torch.cuda.synchronize()
+    return o, lse, mask, crit, cnt
+
+
+def _compare_all(q, k, v, res, *, causal, bq, bk, splits, ln_lam, tiles=None, out_bf16=False):
+    o, lse, mask, crit, cnt = res
+    mh, ch = mask.cpu().numpy(), crit.cpu().numpy()
+    B, Hq, Lq, _ = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    nqt = mh.shape[2]
+    rep = Report()
+    full = tiles is None
+    if full:
+        tiles = [(b, h, t) for b in range(B) for h in range(Hq) for t in range(nqt)]
+        qh, kh, vh = host64(q), host64(k), host64(v)
+    for (b, h, t) in tiles:
+        r0, r1 = t * bq, min((t + 1) * bq, Lq)
+        if full:
+            qt_, kt_, vt_, bb, hh, tt = qh, kh, vh, b, h, t
+        else:
+            # host copies of this tile's rows and of its kv head only
+            qt_ = host64(q[b:b + 1, h:h + 1])
+            kt_ = host64(k[b:b + 1, h // G:h // G + 1])
+            vt_ = host64(v[b:b + 1, h // G:h // G + 1])
+            bb, hh, tt = 0, 0, t
+        kw = dict(causal=causal, block_q=bq, block_k=bk, num_splits=splits, ln_lam=ln_lam)
+        ref = oracle.prefill_tile(qt_, kt_, vt_, bb, hh, tt, **kw)
+        gpu_o = None if o is None else host64(o[b, h, r0:r1])
+        gpu_l = None if o is None else lse[b, h, r0:r1].cpu().double().numpy()
+        check_tile(rep, ref, mh[b, h, t], ch[b, h, t], ln_lam,
+                   lambda f: oracle.prefill_tile(qt_, kt_, vt_, bb, hh, tt, force=f, **kw),
+                   gpu_o, gpu_l, out_bf16=out_bf16)
+    # counters agree with the mask
+    live = int((mh != 2).sum())
+    assert int(cnt[0]) == live and int(cnt[1]) == int((mh == 1).sum())
+    return rep
+
+
+@pytest.mark.parametrize("a", [0.0, 0.5, 2.0, 8.0])
+def test_tiny_mha_fp32(a):
+    """fp32 MHA prefill, batch 1, 2 heads, L = 512, d = 64, causal, 64 x 64 blocks, lambda = a / L."""
+    m = _lib()
+    inp = synth.prefill_inputs(batch=1, hq=2, hkv=2, L=512, d=64, dtype=torch.float32, block_k=64,
+                               window=False, seed=synth.config_seed(1), device="cuda")
+    res = _run(m, inp.q, inp.k, inp.v, causal=True, bq=64, bk=64, splits=1, a=a)
+    ln_lam = oracle.ln_threshold(a=a, L=512)
+    rep = _compare_all(inp.q, inp.k, inp.v, res, causal=True, bq=64, bk=64, splits=1, ln_lam=ln_lam)
+    print(f"a={a}: {rep}")
+    assert rep.max_err < 1e-4
+    if a == 0.0:
+        assert rep.skipped == 0
+
+
+@pytest.mark.parametrize("a", [0.0, 1.0, 4.0, 16.0])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_gqa_bf16_ragged(a, out_dtype):
+    """bf16 GQA prefill with a ragged last tile (L = 600, 128 x 128 blocks), two sequences."""
+    m = _lib()
+    L = 600
+    inp = synth.prefill_inputs(batch=2, hq=4, hkv=2, L=L, d=128, block_k=128, window=True, seed=77,
+                               device="cuda")
+    res = _run(m, inp.q, inp.k, inp.v, causal=True, bq=128, bk=128, splits=1, a=a, out_dtype=out_dtype)
+    rep = _compare_all(inp.q, inp.k, inp.v, res, causal=True, bq=128, bk=128, splits=1,
+                       ln_lam=oracle.ln_threshold(a=a, L=L), out_bf16=out_dtype == torch.bfloat16)
+    print(f"a={a} {out_dtype}: {rep}")
+
+
+@pytest.mark.parametrize("D,blk", [(64, 64), (128, 128), (128, 64), (64, 128)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_bf16_shapes_splits_and_offsets(D, blk, causal):
+    """Lq != Lk (bottom-right causal), num_splits = 3, every head-dim / block-size kernel."""
+    m = _lib()
+    inp = synth.prefill_inputs(batch=1, hq=4, hkv=1, L=700, d=D, block_k=blk, window=True, seed=5,
+                               device="cuda", Lq=250)
+    lam = 0.004
+    res = _run(m, inp.q, inp.k, inp.v, causal=causal, bq=blk, bk=blk, splits=3, lam=lam)
+    rep = _compare_all(inp.q, inp.k, inp.v, res, causal=causal, bq=blk, bk=blk, splits=3,
+                       ln_lam=math.log(lam))
+    print(rep)
+
+
+def test_strided_layout_matches_contiguous():
+    """q/k/v/o given as [B, L, H, D] storage viewed as [B, H, L, D] (token-major) give the same result."""
+    m = _lib()
+    inp = synth.prefill_inputs(batch=2, hq=8, hkv=2, L=384, d=128, block_k=128, seed=9, device="cuda")
+    kw = dict(causal=True, bq=128, bk=128, splits=1, lam=0.01)
+    ref = _run(m, inp.q, inp.k, inp.v, **kw)
+    qs = inp.q.transpose(1, 2).contiguous().transpose(1, 2)
+    ks = inp.k.transpose(1, 2).contiguous().transpose(1, 2)
+    vs = inp.v.transpose(1, 2).contiguous().transpose(1, 2)
+    got = _run(m, qs, ks, vs, **kw)
+    assert torch.equal(ref[2], got[2])
+    assert torch.equal(ref[0], got[0])
+
+
+def test_stats_only_matches_full_pass():
+    m = _lib()
+    inp = synth.prefill_inputs(batch=1, hq=8, hkv=2, L=1024, d=128, block_k=128, seed=10, device="cuda")
+    kw = dict(causal=True, bq=128, bk=128, splits=1, lam=0.003)
+    full = _run(m, inp.q, inp.k, inp.v, **kw)
+    st = _run(m, inp.q, inp.k, inp.v, stats_only=True, **kw)
+    assert torch.equal(full[2], st[2])
+    assert torch.equal(full[3], st[3])
+    assert torch.equal(full[4], st[4])
+
+
+def test_llama8b_gqa_32k_sampled_tiles():
+    """Full-size GQA prefill (32 q / 8 kv heads, d = 128, L = 32768, causal, 128 x 128 blocks) in the
+    launch configuration the benchmark times; sampled tiles against the oracle, and for every tile
+    the mask is the critical value compared with ln(lambda)."""
+    m = _lib()
+    L = 32768
+    inp = synth.prefill_inputs(batch=1, hq=32, hkv=8, L=L, d=128, block_k=128, window=True,
+                               seed=synth.config_seed(2), device="cuda")
+    lam = 0.02   # a sparse operating point (about 3/4 of the blocks skipped on this generator)
+    res = _run(m, inp.q, inp.k, inp.v, causal=True, bq=128, bk=128, splits=1, lam=lam)
+    o, lse, mask, crit, cnt = res
+    ln_lam = math.log(lam)
+    mh, ch = mask.cpu().numpy(), crit.cpu().numpy()
+    live = mh != 2
+    assert live.sum() == 32 * 256 * 257 // 2
+    decided = np.where(live, np.where(ch < ln_lam, 1, 0), 2)
+    band = live & (np.abs(ch - ln_lam) < 1e-3)
+    assert np.array_equal(decided[~band], mh[~band])
+    tiles = [(0, 0, 255), (0, 13, 128), (0, 31, 0), (0, 7, 201), (0, 20, 64)]
+    rep = _compare_all(inp.q, inp.k, inp.v, res, causal=True, bq=128, bk=128, splits=1, ln_lam=ln_lam,
+                       tiles=tiles)
+    print(f"sparsity {float((mh == 1).sum()) / live.sum():.3f}; {rep}")
