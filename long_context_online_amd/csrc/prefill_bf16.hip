@@ -7,72 +7,89 @@
 // 2. Methodik / Kernidee and 3. Kernel-Design).
 //
 // MI355X design:
-//   * one workgroup = one query tile of BR = 32 * NW rows of one q head (NW waves, 32 rows each);
+//   * a workgroup owns TPW query tiles that read the same K/V stream (two q heads of one GQA group
+//     at the same query position), so every staged K/V block serves 2 * BR query rows; each tile
+//     has BR = 32 * WPT rows, one wave per 32 rows, and votes on its own;
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the A operand
 //     (K) comes from LDS, the B operand (Q) stays in registers for the whole tile, and each lane
-//     ends up holding 64 scores of ONE query row, so the block row max is an in-lane max plus one
+//     ends up holding all scores of ONE query row, so the block row max is an in-lane max plus one
 //     exchange with lane l ^ 32;
 //   * P^T is packed to bf16 straight from the score registers and used as the B operand of
 //     O^T = V^T P^T; V is written to LDS transposed (key-contiguous rows, keys permuted to match
 //     the score register layout) so that every MFMA operand read is one 16-byte LDS read;
-//   * the skip vote: per-row predicate -> wave ballot -> one LDS flag per wave -> workgroup OR,
-//     folded into a barrier the tile loop needs anyway; the skip is a uniform branch, so a skipped
-//     block issues no v_exp and no P.V MFMA;
-//   * the next block's K and V are prefetched into registers while the current block computes;
-//   * heavy (late, long causal) tiles launch first, and workgroups that share a kv head are
-//     mapped to the same XCD (blocks are dispatched round-robin over the 8 XCDs) for L2 reuse.
+//   * K goes global -> LDS directly (global_load_lds_dwordx4, no registers), V goes through
+//     registers for the transpose; both are prefetched one block ahead into double-buffered LDS,
+//     so a block costs two barriers: the vote barrier and the buffer-swap barrier;
+//   * the skip vote: per-row predicate -> wave ballot -> one LDS flag per wave -> OR over the
+//     tile's waves after the vote barrier; the skip is a uniform branch, so a skipped block issues
+//     no v_exp and no P.V MFMA;
+//   * every LDS row carries one 16-byte pad chunk, so the 32 rows an MFMA operand read touches fall
+//     on distinct banks and every read address is one per-lane base plus an immediate;
+//   * heavy (late, long causal) tiles launch first, and workgroups of one kv head are mapped to the
+//     same XCD (workgroups are dispatched round-robin over the 8 XCDs) for L2 reuse.
 #include "common.hpp"
 
 namespace blasst {
 
-template <int D, int BC, int NW, bool OUT_F32>
-__global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(PrefillArgs a) {
-  constexpr int BR = 32 * NW;
-  constexpr int NT = 64 * NW;
-  constexpr int KCH = D / 8;        // 16-byte chunks per K row
-  constexpr int KROW = D * 2 + 16;  // bytes per K row in LDS (one 16-byte pad chunk per row)
-  constexpr int VROW = BC * 2 + 16; // bytes per V^T row in LDS
-  constexpr int MT = BC / 32;       // key m-tiles of S^T
-  constexpr int KS = D / 16;        // k-steps over the head dim
-  constexpr int MTV = D / 32;       // dv m-tiles of O^T
-  constexpr int KSV = BC / 16;      // k-steps over the keys of a block
-  constexpr int K_LOADS = BC * KCH / NT;          // 16-byte K chunks per thread
-  constexpr int LPO = D / 2;                      // lanes per key octet (one dv pair per lane)
-  constexpr int OPW = 64 / LPO;                   // key octets per wave instruction
-  constexpr int V_TASKS = (BC / 8) / (NW * OPW);  // octet groups per wave
-  static_assert(BC * KCH % NT == 0 && (BC / 8) % (NW * OPW) == 0, "tile/thread mismatch");
-  static_assert(BR == BC, "square tiles");
+typedef __attribute__((address_space(3))) void lds_void;
 
-  __shared__ __attribute__((aligned(16))) unsigned char sK[BC * KROW];
-  __shared__ __attribute__((aligned(16))) unsigned char sV[D * VROW];
+template <int D, int BC, int TPW, bool OUT_F32, bool STATS>
+__global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(PrefillArgs a) {
+  constexpr int WPT = BC / 32;       // waves per tile (32 rows each)
+  constexpr int BR = BC;             // rows per tile
+  constexpr int NW = WPT * TPW;      // waves per workgroup
+  constexpr int KCH = D / 8;         // 16-byte chunks per K row
+  constexpr int KCP = KCH + 1;       // ... plus the pad chunk
+  constexpr int KROW = KCP * 16;     // bytes per K row in LDS
+  constexpr int VROW = BC * 2 + 16;  // bytes per V^T row in LDS
+  constexpr int MT = BC / 32;        // key m-tiles of S^T
+  constexpr int KS = D / 16;         // k-steps over the head dim
+  constexpr int MTV = D / 32;        // dv m-tiles of O^T
+  constexpr int KSV = BC / 16;       // k-steps over the keys of a block
+  constexpr int KPOS = BC * KCP;     // 16-byte positions of a K tile (pads included)
+  constexpr int KINS = (KPOS + 63) / 64;            // wave-wide direct loads per K tile
+  constexpr int KINS_W = (KINS + NW - 1) / NW;      // ... per wave
+  constexpr int KBUF = KINS_W * NW * 64 * 16;       // bytes per K buffer (covers every wave's writes)
+  constexpr int VBUF = D * VROW;
+  constexpr int LPO = D / 2;                        // lanes per key octet (one dv pair per lane)
+  constexpr int OPW = 64 / LPO;                     // key octets per wave instruction
+  constexpr int V_TASKS = (BC / 8) / (NW * OPW);    // octet groups per wave
+  static_assert((BC / 8) % (NW * OPW) == 0, "tile/thread mismatch");
+
+  __shared__ __attribute__((aligned(16))) unsigned char sK[2][KBUF];
+  __shared__ __attribute__((aligned(16))) unsigned char sV[2][VBUF];
   __shared__ int sVote[2][NW];
   __shared__ float sCrit[2][NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = wave / WPT;       // tile of this wave inside the workgroup
+  const int wit = wave % WPT;        // wave index inside its tile
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
   // ---- tile coordinates: heavy causal tiles first, kv-head groups kept on one XCD ----------------
-  const int per_level = a.B * a.Hq;
+  const int groups = a.Hq / TPW;               // head groups of TPW heads sharing a kv head
+  const int per_level = a.B * groups;
   const int bid = blockIdx.x;
   const int level = bid / per_level;
   int rem = bid - level * per_level;
   if ((per_level & 7) == 0) rem = (rem & 7) * (per_level >> 3) + (rem >> 3);
   const int qt = a.causal ? (a.nqt - 1 - level) : level;
-  const int b = rem / a.Hq;
-  const int hq = rem - b * a.Hq;
-  const int g = hq / a.G;
+  const int b = rem / groups;
+  const int hq0 = (rem - b * groups) * TPW;    // first head of the group
+  const int hq = hq0 + tile;
+  const int g = hq0 / a.G;                     // TPW divides G, so the group shares kv head g
   const int r0 = qt * BR;
-  const int off = a.Lk - a.Lq;  // bottom-right causal alignment
+  const int off = a.Lk - a.Lq;                 // bottom-right causal alignment
 
   const __bf16 *qp = (const __bf16 *)a.q + b * a.qs[0] + hq * a.qs[1];
   const __bf16 *kp = (const __bf16 *)a.k + b * a.ks[0] + g * a.ks[1];
   const __bf16 *vp = (const __bf16 *)a.v + b * a.vs[0] + g * a.vs[1];
 
   const int last_row = min(r0 + BR, a.Lq) - 1;
-  int J;  // live blocks of this tile
+  int J;  // live blocks (the same for every tile of the workgroup)
   if (a.causal) {
     const int lim = last_row + off;
     J = lim < 0 ? 0 : min(a.nkb, lim / BC + 1);
@@ -82,42 +99,41 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(PrefillArgs a)
   const int chunk = J > 0 ? (J + a.num_splits - 1) / a.num_splits : 1;
 
   // ---- Q fragments (B operand of S^T = K Q^T): row l32 of this wave, 8 dims per k-step ----------
-  const int my_row = r0 + wave * 32 + l32;
+  const int my_row = r0 + wit * 32 + l32;
   const bool row_ok = my_row < a.Lq;
   bf16x8 qf[KS];
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    if (row_ok)
-      qf[kk] = *(const bf16x8 *)(qp + (int64_t)my_row * a.qs[2] + kk * 16 + hi * 8);
-    else
-      qf[kk] = bf16x8{};
-  }
+  for (int kk = 0; kk < KS; ++kk)
+    qf[kk] = row_ok ? *(const bf16x8 *)(qp + (int64_t)my_row * a.qs[2] + kk * 16 + hi * 8) : bf16x8{};
 
-  // ---- register staging of the K and V tiles (global -> registers -> LDS) ----------------------
-  // K is stored row-major with a 16-byte pad per row: the 32 rows one MFMA operand read touches
-  // fall on distinct banks, and every read address is one per-lane base plus an immediate.
-  // V is stored transposed (V^T, one row per dv) with the keys of each 16-key chunk in the order
-  // 0-3, 8-11, 4-7, 12-15: "octet" o (16 bytes at byte 16*o of a row) then holds exactly the 8
-  // keys that lane half (o % 2) of P^T k-step (o / 2) carries.  A lane loads one dv pair (4 bytes)
-  // of each of the octet's 8 keys, so every global load instruction reads whole 256-byte rows.
-  u32x4 kreg[K_LOADS];
-  uint32_t vreg[V_TASKS][8];
-  const int v_dp = lane % LPO;              // dv pair of this lane
-  const int v_sub = lane / LPO;             // octet within the wave instruction
-  auto load_k = [&](int j) {
+  // ---- staging ---------------------------------------------------------------------------------
+  // K: direct global -> LDS.  Position p of a K buffer is (row p / KCP, chunk p % KCP); pad chunks
+  // and positions past the tile load row 0 / the last valid key so every lane reads valid memory.
+  auto load_k = [&](int j, int buf) {
     const int key0 = j * BC;
 #pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int idx = tid + i * NT;
-      const int row = idx / KCH, c = idx % KCH;
-      const int key = key0 + row;
-      kreg[i] = key < a.Lk ? *(const u32x4 *)(kp + (int64_t)key * a.ks[2] + c * 8) : u32x4{};
+    for (int i = 0; i < KINS_W; ++i) {
+      const int ins = i * NW + wave;
+      const int p = ins * 64 + lane;
+      int row = p / KCP, c = p - (p / KCP) * KCP;
+      if (c == KCH) c = 0;
+      if (row >= BC) row = 0;
+      const int key = min(key0 + row, a.Lk - 1);
+      __builtin_amdgcn_global_load_lds((const void *)(kp + (int64_t)key * a.ks[2] + c * 8),
+                                       (lds_void *)(sK[buf] + ins * 1024), 16, 0, 0);
     }
   };
+  // V: a lane loads one dv pair (4 bytes) of each of the 8 keys of a key octet, so every load
+  // instruction reads whole rows; it then writes two 16-byte V^T pieces.  Key order inside each
+  // 16-key chunk is 0-3, 8-11, 4-7, 12-15: octet o (16 bytes at byte 16*o of a V^T row) holds the
+  // 8 keys that lane half (o % 2) of P^T k-step (o / 2) carries.
+  uint32_t vreg[V_TASKS][8];
+  const int v_dp = lane % LPO;
+  const int v_sub = lane / LPO;
   auto load_v = [&](int j) {
 #pragma unroll
     for (int t = 0; t < V_TASKS; ++t) {
-      const int o = (t * NW + wave) * OPW + v_sub;           // octet index in the block
+      const int o = (t * NW + wave) * OPW + v_sub;
       const int kb = j * BC + (o >> 1) * 16 + (o & 1) * 4;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -126,15 +142,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(PrefillArgs a)
       }
     }
   };
-  auto store_k = [&]() {
-#pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int idx = tid + i * NT;
-      const int row = idx / KCH, c = idx % KCH;
-      *(u32x4 *)(sK + row * KROW + c * 16) = kreg[i];
-    }
-  };
-  auto store_v = [&]() {
+  auto store_v = [&](int buf) {
 #pragma unroll
     for (int t = 0; t < V_TASKS; ++t) {
       const int o = (t * NW + wave) * OPW + v_sub;
@@ -145,8 +153,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(PrefillArgs a)
         lo[i] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
         hi2[i] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
       }
-      *(u32x4 *)(sV + (2 * v_dp) * VROW + o * 16) = lo;
-      *(u32x4 *)(sV + (2 * v_dp + 1) * VROW + o * 16) = hi2;
+      *(u32x4 *)(sV[buf] + (2 * v_dp) * VROW + o * 16) = lo;
+      *(u32x4 *)(sV[buf] + (2 * v_dp + 1) * VROW + o * 16) = hi2;
     }
   };
 
@@ -159,32 +167,36 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(PrefillArgs a)
   for (int i = 0; i < MTV; ++i) o_acc[i] = f32x16{};
   unsigned live_cnt = 0, skip_cnt = 0;
   const int mask_row = ((b * a.Hq + hq) * a.nqt + qt) * a.nkb;
+  const bool tile_leader = wit == 0 && lane == 0;
 
-  // Per block j, with single LDS buffers and three barriers:
-  //   K_{j+1} -> regs | S^T from sK | vote -> barrier A | K_{j+1} -> sK, V_{j+1} -> regs |
-  //   (kept) softmax, P.V from sV | barrier B | V_{j+1} -> sV | barrier C
-  // so the K registers are dead before the softmax and the V registers are only live during it.
   if (J > 0) {
-    load_k(0);
-    load_v(0);
-    store_k();
-    store_v();
+    load_k(0, 0);
+    if (!STATS) {
+      load_v(0);
+      store_v(0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
   for (int j = 0; j < J; ++j) {
+    const int buf = j & 1;
     const bool has_next = j + 1 < J;
-    if (has_next) load_k(j + 1);
+    if (has_next) {
+      load_k(j + 1, buf ^ 1);
+      if (!STATS) load_v(j + 1);
+    }
     if ((j % chunk) == 0) m_dec = kNegInf;
 
     // ---- S^T = K_j Q^T ----
     f32x16 s[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) s[mt] = f32x16{};
+    const unsigned char *kb = sK[buf] + l32 * KROW + hi * 16;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 kf = *(const bf16x8 *)(sK + (mt * 32 + l32) * KROW + (kk * 2 + hi) * 16);
+        const bf16x8 kf = *(const bf16x8 *)(kb + mt * 32 * KROW + kk * 32);
         s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[mt], 0, 0, 0);
       }
     }
@@ -216,79 +228,75 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(PrefillArgs a)
     float wcrit = 0.f;
     if (a.crit) wcrit = max_lanes32(row_crit(mx, m_dec));
     if (lane == 0) {
-      sVote[j & 1][wave] = wave_keep ? 1 : 0;
-      sCrit[j & 1][wave] = wcrit;
+      sVote[buf][wave] = wave_keep ? 1 : 0;
+      sCrit[buf][wave] = wcrit;
     }
-    __syncthreads();  // barrier A: votes visible, every wave is done reading sK
-    if (has_next) {
-      store_k();
-      load_v(j + 1);
-    }
+    __syncthreads();  // vote barrier
     int keep = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) keep |= sVote[j & 1][w];
+    for (int w = 0; w < WPT; ++w) keep |= sVote[buf][tile * WPT + w];
     m_dec = fmaxf(m_dec, mx);
     ++live_cnt;
     if (!keep) ++skip_cnt;
-    if (tid == 0) {
+    if (tile_leader) {
       if (a.mask) a.mask[mask_row + j] = keep ? kKept : kSkipped;
       if (a.crit) {
-        float c = sCrit[j & 1][0];
+        float c = sCrit[buf][tile * WPT];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) c = fmaxf(c, sCrit[j & 1][w]);
+        for (int w = 1; w < WPT; ++w) c = fmaxf(c, sCrit[buf][tile * WPT + w]);
         a.crit[mask_row + j] = c * a.scale;
       }
     }
-    if (keep && !a.stats_only) {
 
-    // ---- kept block: online-softmax update and O^T += V^T P^T ----
-    const float m_new = fmaxf(m_acc, mx);
-    const bool grow = m_new > m_acc;
-    if (__ballot(grow) != 0ull) {
-      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_acc - m_new) * a.scale_log2);
-      l_part *= alpha;
+    if (!STATS && keep) {
+      // ---- kept block: online-softmax update and O^T += V^T P^T ----
+      const float m_new = fmaxf(m_acc, mx);
+      if (__ballot(m_new > m_acc) != 0ull) {
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_acc - m_new) * a.scale_log2);
+        l_part *= alpha;
 #pragma unroll
-      for (int i = 0; i < MTV; ++i) o_acc[i] *= alpha;
-      m_acc = m_new;
-    }
-    const float base = (m_acc == kNegInf) ? 0.f : m_acc * a.scale_log2;
-    // P^T for k-step kk (16 keys) is formed right before its MFMAs: keys of score registers
-    // s[kk/2][8*(kk%2) .. +7], i.e. key 16*kk + 8*(e/4) + 4*hi + e%4 for element e.
-#pragma unroll
-    for (int kk = 0; kk < KSV; ++kk) {
-      bf16x8 pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = fast_exp2(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + e], a.scale_log2, -base));
-        l_part += p;
-        pf[e] = (__bf16)p;
+        for (int i = 0; i < MTV; ++i) o_acc[i] *= alpha;
+        m_acc = m_new;
       }
+      const float base = (m_acc == kNegInf) ? 0.f : m_acc * a.scale_log2;
+      const unsigned char *vb = sV[buf] + l32 * VROW + hi * 16;
+      // P^T for k-step kk (16 keys) is formed right before its MFMAs: keys of score registers
+      // s[kk/2][8*(kk%2) .. +7], i.e. key 16*kk + 8*(e/4) + 4*hi + e%4 for element e.
 #pragma unroll
-      for (int mv = 0; mv < MTV; ++mv) {
-        const bf16x8 vf = *(const bf16x8 *)(sV + (mv * 32 + l32) * VROW + (kk * 2 + hi) * 16);
-        o_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o_acc[mv], 0, 0, 0);
+      for (int kk = 0; kk < KSV; ++kk) {
+        bf16x8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + e], a.scale_log2, -base));
+          l_part += p;
+          pf[e] = (__bf16)p;
+        }
+#pragma unroll
+        for (int mv = 0; mv < MTV; ++mv) {
+          const bf16x8 vf = *(const bf16x8 *)(vb + mv * 32 * VROW + kk * 32);
+          o_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o_acc[mv], 0, 0, 0);
+        }
       }
     }
-    }  // kept block
     if (has_next) {
-      __syncthreads();  // barrier B: every wave is done reading sV
-      store_v();
-      __syncthreads();  // barrier C: K_{j+1} and V_{j+1} visible
+      if (!STATS) store_v(buf ^ 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the direct K loads have landed in LDS
+      __syncthreads();  // buffer-swap barrier
     }
   }
 
   // ---- diagnostics for blocks that are not live ----
   if (a.mask || a.crit) {
-    for (int j = J + tid; j < a.nkb; j += NT) {
+    for (int j = J + wit * 64 + lane; j < a.nkb; j += WPT * 64) {
       if (a.mask) a.mask[mask_row + j] = kNotLive;
       if (a.crit) a.crit[mask_row + j] = __builtin_nanf("");
     }
   }
-  if (a.counters && tid == 0) {
+  if (a.counters && tile_leader) {
     atomicAdd(&a.counters[0], (unsigned long long)live_cnt);
     atomicAdd(&a.counters[1], (unsigned long long)skip_cnt);
   }
-  if (a.stats_only) return;
+  if (STATS) return;
 
   // ---- epilogue: O = O^T / l, LSE = m * scale + ln l ----
   const float l_row = l_part + __shfl_xor(l_part, 32);
@@ -323,20 +331,32 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(PrefillArgs a)
   }
 }
 
-template <int D, int BC, bool OUT_F32>
-static hipError_t launch_one(const PrefillArgs &a, hipStream_t st) {
-  constexpr int NW = BC / 32;
-  const int grid = a.B * a.Hq * a.nqt;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, NW, OUT_F32>), dim3(grid), dim3(64 * NW), 0, st, a);
+template <int D, int BC, int TPW>
+static hipError_t launch_tpw(const PrefillArgs &a, bool out_f32, hipStream_t st) {
+  constexpr int NT = 64 * (BC / 32) * TPW;
+  const int grid = a.B * (a.Hq / TPW) * a.nqt;
+  if (a.stats_only)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, TPW, false, true>), dim3(grid), dim3(NT), 0, st, a);
+  else if (out_f32)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, TPW, true, false>), dim3(grid), dim3(NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, TPW, false, false>), dim3(grid), dim3(NT), 0, st, a);
   return hipGetLastError();
+}
+
+template <int D, int BC>
+static hipError_t launch_one(const PrefillArgs &a, bool out_f32, hipStream_t st) {
+  // two q heads of one GQA group share each staged K/V block when the group has an even size
+  if (a.G % 2 == 0) return launch_tpw<D, BC, 2>(a, out_f32, st);
+  return launch_tpw<D, BC, 1>(a, out_f32, st);
 }
 
 // Returns hipErrorNotSupported when no instantiation matches.
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int D, int BC, bool out_f32, hipStream_t st) {
-  if (D == 128 && BC == 128) return out_f32 ? launch_one<128, 128, true>(a, st) : launch_one<128, 128, false>(a, st);
-  if (D == 128 && BC == 64) return out_f32 ? launch_one<128, 64, true>(a, st) : launch_one<128, 64, false>(a, st);
-  if (D == 64 && BC == 128) return out_f32 ? launch_one<64, 128, true>(a, st) : launch_one<64, 128, false>(a, st);
-  if (D == 64 && BC == 64) return out_f32 ? launch_one<64, 64, true>(a, st) : launch_one<64, 64, false>(a, st);
+  if (D == 128 && BC == 128) return launch_one<128, 128>(a, out_f32, st);
+  if (D == 128 && BC == 64) return launch_one<128, 64>(a, out_f32, st);
+  if (D == 64 && BC == 128) return launch_one<64, 128>(a, out_f32, st);
+  if (D == 64 && BC == 64) return launch_one<64, 64>(a, out_f32, st);
   return hipErrorNotSupported;
 }
 
