@@ -79,6 +79,7 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
   const __bf16 *vc = (const __bf16 *)a.vc;
   const int32_t *table = a.table + (int64_t)b * a.max_pages;
   const int64_t page_stride = (int64_t)a.Hkv * PAGE * D;  // elements per physical page (all heads)
+  const int npg = (L + PAGE - 1) / PAGE;                   // pages of this sequence (>= 1)
 
   float m_dec = kNegInf, m_acc = kNegInf, l_part = 0.f;
   f32x4 o_acc[D / 16];
@@ -87,20 +88,35 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
   unsigned live_cnt = 0, skip_cnt = 0;
   const int mask_row = ((b * a.Hkv + g) * a.n_rt + rt) * a.nkb;
 
+  // Page ids of a batch: lane l (< 16) holds the id of page jb*4 + l, i.e. page (l % 4) of block
+  // jb + l / 4; a wave picks its pages with readlane.  Pages past the sequence use its last page
+  // (their keys are masked and their V is zeroed), so every load is unconditional and in bounds.
+  auto load_table = [&](int jb) -> int {
+    const int pg = min(jb * (BK / PAGE) + (lane & 15), npg - 1);
+    return table[pg];
+  };
   u32x4 kreg[NB][4];
-  auto load_k = [&](int jb) {
+  int pid_cur[NB];
+  auto load_k = [&](const int (&pid)[NB]) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int pg = (jb + i) * (BK / PAGE) + wave;
-      const bool ok = (jb + i) < j1 && pg * PAGE < L;
-      const int pid = ok ? table[pg] : 0;
-      const __bf16 *src = kc + (int64_t)pid * page_stride + ((int64_t)g * PAGE + n) * D + grp * 8;
+      const __bf16 *src = kc + (int64_t)pid[i] * page_stride + ((int64_t)g * PAGE + n) * D + grp * 8;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kreg[i][kk] = ok ? *(const u32x4 *)(src + kk * 32) : u32x4{};
+      for (int kk = 0; kk < 4; ++kk) kreg[i][kk] = *(const u32x4 *)(src + kk * 32);
     }
   };
+  auto pick = [&](int tabv, int (&pid)[NB]) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) pid[i] = __builtin_amdgcn_readlane(tabv, i * 4 + wave);
+  };
 
-  if (j0 < j1) load_k(j0);
+  int tab_next = 0;
+  if (j0 < j1) {
+    const int tab0 = load_table(j0);
+    pick(tab0, pid_cur);
+    load_k(pid_cur);
+    tab_next = load_table(j0 + NB);
+  }
   for (int jb = j0; jb < j1; jb += NB) {
     const int nb = min(NB, j1 - jb);
     // ---- scores of this wave's page of each block in the batch ----
@@ -120,6 +136,8 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
       pm = max_xor16_32(pm);
       if (grp == 0) sPmax[i][wave][n] = pm;
     }
+    int pid_next[NB];
+    pick(tab_next, pid_next);
     __syncthreads();
     // ---- in-batch sequential decisions (identical in every wave) ----
     int keep_bits = 0;
@@ -131,7 +149,6 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
       mblk[i] = mb;
       if (i < nb) {
         const int j = jb + i;
-        if (j == j0) m_dec = kNegInf;
         const bool skip_row = row_votes_skip(mb, m_dec, thr);
         const bool keep = __ballot(!skip_row) != 0ull;
         if (a.crit) {
@@ -150,21 +167,23 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
       }
     }
     if (a.stats_only) keep_bits = 0;
-    // ---- V loads of the surviving blocks only ----
+    // ---- next batch's K loads and the page ids of the batch after it, then the V loads of the
+    // surviving blocks only; all are in flight together and the PV products wait for all of them
+    // (vector loads return in order) ----
+    const bool more = jb + NB < j1;
+    if (more) {
+      load_k(pid_next);
+      tab_next = load_table(jb + 2 * NB);
+    }
     u32x2 vreg[NB][D / 16];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (keep_bits & (1 << i)) {
-        const int pg = (jb + i) * (BK / PAGE) + wave;
-        const bool ok = pg * PAGE < L;
-        const int pid = ok ? table[pg] : 0;
-        const __bf16 *src = vc + (int64_t)pid * page_stride + (int64_t)g * D * PAGE + n * PAGE + grp * 4;
+        const __bf16 *src = vc + (int64_t)pid_cur[i] * page_stride + (int64_t)g * D * PAGE + n * PAGE + grp * 4;
 #pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt) vreg[i][mt] = ok ? *(const u32x2 *)(src + mt * 16 * PAGE) : u32x2{};
+        for (int mt = 0; mt < D / 16; ++mt) vreg[i][mt] = *(const u32x2 *)(src + mt * 16 * PAGE);
       }
     }
-    // ---- prefetch the next batch's K while the PV products run ----
-    if (jb + NB < j1) load_k(jb + NB);
     // ---- kept blocks: online softmax and O^T += V^T P^T ----
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -200,6 +219,8 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
         o_acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vv), pf, o_acc[mt], 0, 0, 0);
       }
     }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) pid_cur[i] = pid_next[i];
     __syncthreads();  // sPmax is rewritten by the next batch
   }
 
@@ -265,46 +286,62 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
   }
 }
 
-// Log-sum-exp merge of the per-split partials: one workgroup per (sequence, q head), one thread
-// per 4 output channels.
+// Log-sum-exp merge of the per-split partials: one wave per (sequence, q head), four per
+// workgroup.  Lane s < S reads lse_s; the split weights exp(lse_s - LSE) are shared with shuffles,
+// and each lane accumulates Dv/64 output channels, so every partial row is read coalesced.
 template <bool OUT_F32>
-__global__ __launch_bounds__(128) void decode_combine_kernel(const float *ws_o, const float *ws_lse, void *o,
-                                                              float *lse_out, int S, int Dv) {
-  const int bh = blockIdx.x;
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float *ws_o, const float *ws_lse, void *o,
+                                                              float *lse_out, int BH, int S, int Dv) {
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= BH) return;
   const float *pl = ws_lse + (int64_t)bh * S;
-  float mx = kNegInf;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, pl[s]);
+  float my = kNegInf;
+  for (int s = lane; s < S; s += 64) my = fmaxf(my, pl[s]);
+  float mx = my;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   float tot = 0.f;
-  for (int s = 0; s < S; ++s) tot += (pl[s] == kNegInf) ? 0.f : __expf(pl[s] - mx);
+  for (int s = lane; s < S; s += 64) tot += (pl[s] == kNegInf) ? 0.f : __expf(pl[s] - mx);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  for (int c = threadIdx.x * 4; c < Dv; c += blockDim.x * 4) {
-    f32x4 acc = f32x4{};
+  for (int c0 = 0; c0 < Dv; c0 += 128) {
+    const int c = c0 + lane * 2;
+    float acc0 = 0.f, acc1 = 0.f;
     for (int s = 0; s < S; ++s) {
-      if (pl[s] == kNegInf) continue;
-      const float w = __expf(pl[s] - mx);
-      acc += w * *(const f32x4 *)(ws_o + ((int64_t)bh * S + s) * Dv + c);
+      const float ls = pl[s];
+      if (ls == kNegInf) continue;
+      const float w = __expf(ls - mx);
+      if (c < Dv) {
+        const float2 v = *(const float2 *)(ws_o + ((int64_t)bh * S + s) * Dv + c);
+        acc0 += w * v.x;
+        acc1 += w * v.y;
+      }
     }
-    acc *= inv;
-    if (OUT_F32) {
-      *(f32x4 *)((float *)o + (int64_t)bh * Dv + c) = acc;
-    } else {
-      u32x2 w;
-      w[0] = pack_bf16x2(acc[0], acc[1]);
-      w[1] = pack_bf16x2(acc[2], acc[3]);
-      *(u32x2 *)((__bf16 *)o + (int64_t)bh * Dv + c) = w;
+    if (c < Dv) {
+      if (OUT_F32) {
+        float2 r;
+        r.x = acc0 * inv;
+        r.y = acc1 * inv;
+        *(float2 *)((float *)o + (int64_t)bh * Dv + c) = r;
+      } else {
+        *(uint32_t *)((__bf16 *)o + (int64_t)bh * Dv + c) = pack_bf16x2(acc0 * inv, acc1 * inv);
+      }
     }
   }
-  if (lse_out && threadIdx.x == 0) lse_out[bh] = tot > 0.f ? mx + __logf(tot) : kNegInf;
+  if (lse_out && lane == 0) lse_out[bh] = tot > 0.f ? mx + __logf(tot) : kNegInf;
 }
 
 hipError_t launch_decode_combine(const DecodeArgs &a, int Dv, hipStream_t st) {
-  const int grid = a.B * a.Hq;
+  const int BH = a.B * a.Hq;
+  const int grid = (BH + 3) / 4;
   if (a.out_f32)
-    hipLaunchKernelGGL(decode_combine_kernel<true>, dim3(grid), dim3(128), 0, st, a.ws_o, a.ws_lse, a.o, a.lse,
-                       a.num_splits, Dv);
+    hipLaunchKernelGGL(decode_combine_kernel<true>, dim3(grid), dim3(256), 0, st, a.ws_o, a.ws_lse, a.o, a.lse,
+                       BH, a.num_splits, Dv);
   else
-    hipLaunchKernelGGL(decode_combine_kernel<false>, dim3(grid), dim3(128), 0, st, a.ws_o, a.ws_lse, a.o, a.lse,
-                       a.num_splits, Dv);
+    hipLaunchKernelGGL(decode_combine_kernel<false>, dim3(grid), dim3(256), 0, st, a.ws_o, a.ws_lse, a.o, a.lse,
+                       BH, a.num_splits, Dv);
   return hipGetLastError();
 }
 
