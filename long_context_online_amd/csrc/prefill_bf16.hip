@@ -15,23 +15,30 @@
 //     ends up holding all scores of ONE query row, so the block row max is an in-lane max plus one
 //     exchange with lane l ^ 32;
 //   * P^T is packed to bf16 straight from the score registers and used as the B operand of
-//     O^T = V^T P^T; V is written to LDS transposed (key-contiguous rows, keys permuted to match
-//     the score register layout) so that every MFMA operand read is one 16-byte LDS read;
-//   * K goes global -> LDS directly (global_load_lds_dwordx4, no registers), V goes through
-//     registers for the transpose; both are prefetched one block ahead into double-buffered LDS,
-//     so a block costs two barriers: the vote barrier and the buffer-swap barrier;
+//     O^T = V^T P^T; the V^T operand is read from a row-major V tile with the gfx950 transpose
+//     read ds_read_b64_tr_b16 (within a 16-lane group, output lane i, element k is element i%4 of
+//     source lane 4k + i/4's 8-byte read), so no transpose pass is needed anywhere;
+//   * K and V both go global -> LDS directly (global_load_lds_dwordx4, no registers, no VALU) and
+//     are prefetched one block ahead into double-buffered LDS, so a block costs two barriers: the
+//     vote barrier and the buffer-swap barrier, and staging a skipped block's V costs only the
+//     load instructions;
 //   * the skip vote: per-row predicate -> wave ballot -> one LDS flag per wave -> OR over the
 //     tile's waves after the vote barrier; the skip is a uniform branch, so a skipped block issues
 //     no v_exp and no P.V MFMA;
-//   * every LDS row carries one 16-byte pad chunk, so the 32 rows an MFMA operand read touches fall
-//     on distinct banks and every read address is one per-lane base plus an immediate;
+//   * LDS rows are padded (K: 16 bytes, so the 8 rows of one 16-byte read pass fall on distinct
+//     banks; V: 32 bytes, so the 4 row segments of one transpose-read pass do), and every read
+//     address is one per-lane base plus an immediate;
 //   * heavy (late, long causal) tiles launch first, and workgroups of one kv head are mapped to the
 //     same XCD (workgroups are dispatched round-robin over the 8 XCDs) for L2 reuse.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace blasst {
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((ext_vector_type(4))) short v4i16;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 template <int D, int BC, int TPW, bool OUT_F32, bool STATS>
 __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(PrefillArgs a) {
@@ -41,20 +48,17 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   constexpr int KCH = D / 8;         // 16-byte chunks per K row
   constexpr int KCP = KCH + 1;       // ... plus the pad chunk
   constexpr int KROW = KCP * 16;     // bytes per K row in LDS
-  constexpr int VROW = BC * 2 + 16;  // bytes per V^T row in LDS
+  constexpr int VCH = D / 8;         // 16-byte chunks per V row
+  constexpr int VCP = VCH + 2;       // ... plus two pad chunks
+  constexpr int VROW = VCP * 16;     // bytes per V row in LDS
   constexpr int MT = BC / 32;        // key m-tiles of S^T
   constexpr int KS = D / 16;         // k-steps over the head dim
   constexpr int MTV = D / 32;        // dv m-tiles of O^T
   constexpr int KSV = BC / 16;       // k-steps over the keys of a block
-  constexpr int KPOS = BC * KCP;     // 16-byte positions of a K tile (pads included)
-  constexpr int KINS = (KPOS + 63) / 64;            // wave-wide direct loads per K tile
-  constexpr int KINS_W = (KINS + NW - 1) / NW;      // ... per wave
-  constexpr int KBUF = KINS_W * NW * 64 * 16;       // bytes per K buffer (covers every wave's writes)
-  constexpr int VBUF = D * VROW;
-  constexpr int LPO = D / 2;                        // lanes per key octet (one dv pair per lane)
-  constexpr int OPW = 64 / LPO;                     // key octets per wave instruction
-  constexpr int V_TASKS = (BC / 8) / (NW * OPW);    // octet groups per wave
-  static_assert((BC / 8) % (NW * OPW) == 0, "tile/thread mismatch");
+  constexpr int KINS = (BC * KCP + 63) / 64;        // wave-wide direct loads per K tile
+  constexpr int VINS = (BC * VCP + 63) / 64;        // ... per V tile
+  constexpr int KBUF = KINS * 1024;
+  constexpr int VBUF = VINS * 1024;
 
   __shared__ __attribute__((aligned(16))) unsigned char sK[2][KBUF];
   __shared__ __attribute__((aligned(16))) unsigned char sV[2][VBUF];
@@ -106,57 +110,42 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   for (int kk = 0; kk < KS; ++kk)
     qf[kk] = row_ok ? *(const bf16x8 *)(qp + (int64_t)my_row * a.qs[2] + kk * 16 + hi * 8) : bf16x8{};
 
-  // ---- staging ---------------------------------------------------------------------------------
-  // K: direct global -> LDS.  Position p of a K buffer is (row p / KCP, chunk p % KCP); pad chunks
-  // and positions past the tile load row 0 / the last valid key so every lane reads valid memory.
-  auto load_k = [&](int j, int buf) {
+  // ---- staging: direct global -> LDS ---------------------------------------------------------
+  // One wave instruction fills 1 KB = 64 consecutive 16-byte positions of a buffer; position p is
+  // (row p / CP, chunk p % CP).  Pad chunks and rows past the tile load a valid chunk of row 0 and
+  // keys past the end load the last key, so every lane reads valid memory (those keys are masked).
+  auto load_tile = [&](const __bf16 *base, int64_t stride, int j, unsigned char *dst, auto CPc, auto CHc,
+                       auto INSc) {
+    constexpr int CP = decltype(CPc)::value, CH = decltype(CHc)::value, INS = decltype(INSc)::value;
     const int key0 = j * BC;
 #pragma unroll
-    for (int i = 0; i < KINS_W; ++i) {
+    for (int i = 0; i < (INS + NW - 1) / NW; ++i) {
       const int ins = i * NW + wave;
-      const int p = ins * 64 + lane;
-      int row = p / KCP, c = p - (p / KCP) * KCP;
-      if (c == KCH) c = 0;
-      if (row >= BC) row = 0;
-      const int key = min(key0 + row, a.Lk - 1);
-      __builtin_amdgcn_global_load_lds((const void *)(kp + (int64_t)key * a.ks[2] + c * 8),
-                                       (lds_void *)(sK[buf] + ins * 1024), 16, 0, 0);
-    }
-  };
-  // V: a lane loads one dv pair (4 bytes) of each of the 8 keys of a key octet, so every load
-  // instruction reads whole rows; it then writes two 16-byte V^T pieces.  Key order inside each
-  // 16-key chunk is 0-3, 8-11, 4-7, 12-15: octet o (16 bytes at byte 16*o of a V^T row) holds the
-  // 8 keys that lane half (o % 2) of P^T k-step (o / 2) carries.
-  uint32_t vreg[V_TASKS][8];
-  const int v_dp = lane % LPO;
-  const int v_sub = lane / LPO;
-  auto load_v = [&](int j) {
-#pragma unroll
-    for (int t = 0; t < V_TASKS; ++t) {
-      const int o = (t * NW + wave) * OPW + v_sub;
-      const int kb = j * BC + (o >> 1) * 16 + (o & 1) * 4;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = kb + (e >> 2) * 8 + (e & 3);
-        vreg[t][e] = key < a.Lk ? *(const uint32_t *)(vp + (int64_t)key * a.vs[2] + 2 * v_dp) : 0u;
+      if (ins < INS) {
+        const int p = ins * 64 + lane;
+        int row = p / CP, c = p - (p / CP) * CP;
+        if (c >= CH) c = 0;
+        if (row >= BC) row = 0;
+        const int key = min(key0 + row, a.Lk - 1);
+        __builtin_amdgcn_global_load_lds((const void *)(base + (int64_t)key * stride + c * 8),
+                                         (lds_void *)(dst + ins * 1024), 16, 0, 0);
       }
     }
   };
-  auto store_v = [&](int buf) {
-#pragma unroll
-    for (int t = 0; t < V_TASKS; ++t) {
-      const int o = (t * NW + wave) * OPW + v_sub;
-      u32x4 lo, hi2;  // dv 2*v_dp (low halves) and 2*v_dp+1 (high halves) of the 8 keys
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t x0 = vreg[t][2 * i], x1 = vreg[t][2 * i + 1];
-        lo[i] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-        hi2[i] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-      }
-      *(u32x4 *)(sV[buf] + (2 * v_dp) * VROW + o * 16) = lo;
-      *(u32x4 *)(sV[buf] + (2 * v_dp + 1) * VROW + o * 16) = hi2;
-    }
+  auto load_k = [&](int j, int buf) {
+    load_tile(kp, a.ks[2], j, sK[buf], std::integral_constant<int, KCP>{}, std::integral_constant<int, KCH>{},
+              std::integral_constant<int, KINS>{});
   };
+  auto load_v = [&](int j, int buf) {
+    load_tile(vp, a.vs[2], j, sV[buf], std::integral_constant<int, VCP>{}, std::integral_constant<int, VCH>{},
+              std::integral_constant<int, VINS>{});
+  };
+  // Transpose-read addressing for the V^T operand of k-step kk, dv m-tile mv: source lane
+  // j = 4k + q of 16-lane group G points at V[16 kk + 4 (G / 2) + k][32 mv + 16 (G % 2) + 4 q ...+3];
+  // the second read covers keys + 8.  Output lane l then holds dv 32 mv + l % 32 and the keys of
+  // its lane half, in the order of its P^T fragment.
+  const int tr_g = lane >> 4, tr_j = lane & 15;
+  const int tr_off = ((tr_g >> 1) * 4 + (tr_j >> 2)) * VROW + (16 * (tr_g & 1) + 4 * (tr_j & 3)) * 2;
 
   // ---- online-softmax state (per lane: query row l32 of this wave) -----------------------------
   float m_dec = kNegInf;  // running max used by the skip rule (restarts at each split)
@@ -171,10 +160,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
 
   if (J > 0) {
     load_k(0, 0);
-    if (!STATS) {
-      load_v(0);
-      store_v(0);
-    }
+    if (!STATS) load_v(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
@@ -183,7 +169,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     const bool has_next = j + 1 < J;
     if (has_next) {
       load_k(j + 1, buf ^ 1);
-      if (!STATS) load_v(j + 1);
+      if (!STATS) load_v(j + 1, buf ^ 1);
     }
     if ((j % chunk) == 0) m_dec = kNegInf;
 
@@ -259,7 +245,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
         m_acc = m_new;
       }
       const float base = (m_acc == kNegInf) ? 0.f : m_acc * a.scale_log2;
-      const unsigned char *vb = sV[buf] + l32 * VROW + hi * 16;
+      const unsigned char *vb = sV[buf] + tr_off;
       // P^T for k-step kk (16 keys) is formed right before its MFMAs: keys of score registers
       // s[kk/2][8*(kk%2) .. +7], i.e. key 16*kk + 8*(e/4) + 4*hi + e%4 for element e.
 #pragma unroll
@@ -273,14 +259,17 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
         }
 #pragma unroll
         for (int mv = 0; mv < MTV; ++mv) {
-          const bf16x8 vf = *(const bf16x8 *)(vb + mv * 32 * VROW + kk * 32);
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16 *)(vb + kk * 16 * VROW + mv * 64));
+          const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16 *)(vb + (kk * 16 + 8) * VROW + mv * 64));
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
           o_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o_acc[mv], 0, 0, 0);
         }
       }
     }
     if (has_next) {
-      if (!STATS) store_v(buf ^ 1);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the direct K loads have landed in LDS
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the direct K/V loads have landed in LDS
       __syncthreads();  // buffer-swap barrier
     }
   }
