@@ -136,7 +136,8 @@ typedef struct {
  * memory, 256-byte aligned.
  * Supported kernels: bf16 in, bf16/fp32 out; page_size 16; block_k 64;
  *   GQA/MHA/MQA: head_dim_qk == head_dim_v == 128, tile_rows <= 16;
- *   latent (v_cache NULL): head_dim_qk == 576, head_dim_v == 512, tile_rows == 128 (MLA-shaped).
+ *   latent (v_cache NULL): 128 q heads on 1 kv head, head_dim_qk == 576, head_dim_v == 512,
+ *   tile_rows 128 (one tile of all heads) or 64 (MLA-shaped).
  */
 typedef struct {
   size_t struct_size;        /* sizeof(blasst_decode_params) */

@@ -185,8 +185,10 @@ static blasst_status validate_decode(const blasst_decode_params *p, bool need_pt
   if (p->page_size != 16 || p->block_k != 64) return fail(BLASST_ERR_UNSUPPORTED, "decode supports page 16, block 64");
   const bool latent = p->v_cache == nullptr;
   if (latent) {
-    if (p->num_kv_heads != 1 || p->head_dim_qk != 576 || p->head_dim_v != 512 || tr != 128)
-      return fail(BLASST_ERR_UNSUPPORTED, "latent decode supports 1 kv head, dims 576/512, tile_rows 128");
+    if (p->num_kv_heads != 1 || p->num_q_heads != 128 || p->head_dim_qk != 576 || p->head_dim_v != 512 ||
+        (tr != 128 && tr != 64))
+      return fail(BLASST_ERR_UNSUPPORTED,
+                  "latent decode supports 128 q heads on 1 kv head, dims 576/512, tile_rows 128 or 64");
   } else {
     if (p->head_dim_qk != 128 || p->head_dim_v != 128 || tr > 16)
       return fail(BLASST_ERR_UNSUPPORTED, "decode supports head dim 128 and tile_rows <= 16");

@@ -150,3 +150,41 @@ def test_gqa_decode_full_size_sampled(ctx):
     tiles = [(0, 0, 0), (5, 3, 0), (17, 7, 0), (31, 4, 0)]
     rep = _compare(d, res, splits=16, a=a, tiles=tiles)
     print(f"sparsity {float((mh == 1).sum()) / live.sum():.3f}; {rep}")
+
+
+@pytest.mark.parametrize("tile_rows", [128, 64])
+@pytest.mark.parametrize("splits", [1, 4])
+@pytest.mark.parametrize("a", [0.0, 2.0, 20.0])
+def test_latent_mla_ragged(tile_rows, splits, a):
+    """Latent attention: 128 q heads on one 576-channel latent head, V = first 512 channels, ragged
+    sequence lengths, NaN-poisoned spare pages and tail slots."""
+    m = _lib()
+    lens = [1000, 64, 17]
+    d = synth.decode_inputs(batch=3, hq=128, hkv=1, ctx=None, d=576, dv=512, seq_lens=lens, seed=8,
+                            device="cuda", latent=True)
+    res = _run(m, d, splits=splits, a=a, tile_rows=tile_rows)
+    rep = _compare(d, res, splits=splits, a=a, tile_rows=tile_rows)
+    print(f"tile_rows={tile_rows} S={splits} a={a}: {rep}")
+    if a == 0.0:
+        assert rep.skipped == 0
+
+
+def test_latent_mla_full_size_sampled():
+    """Batch 64, 128 q heads on one latent head (576 / 512), context 32768, 16-token pages, 64-token
+    blocks, 16 splits, 128-head tiles: sampled sequences against the oracle."""
+    m = _lib()
+    d = synth.decode_inputs(batch=64, hq=128, hkv=1, ctx=32768, d=576, dv=512, seed=synth.config_seed(5),
+                            device="cuda", latent=True)
+    a = 0.02 * 32768
+    res = _run(m, d, splits=16, a=a, tile_rows=128, out_dtype=torch.bfloat16)
+    o, lse, mask, crit, cnt = res
+    ln_lam = math.log(min(1.0, a / 32768))
+    mh, ch = mask.cpu().numpy(), crit.cpu().numpy()
+    live = mh != 2
+    decided = np.where(live, np.where(ch < ln_lam, 1, 0), 2)
+    band = live & (np.abs(ch - ln_lam) < 1e-3)
+    assert np.array_equal(decided[~band], mh[~band])
+    assert torch.isfinite(o.float()).all()
+    rep = _compare(d, res, splits=16, a=a, tiles=[(0, 0, 0), (37, 0, 0), (63, 0, 0)], tile_rows=128,
+                   out_bf16=True)
+    print(f"sparsity {float((mh == 1).sum()) / live.sum():.3f}; {rep}")
