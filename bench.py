@@ -8,7 +8,11 @@ d = 128, context 32768, 16-token pages, 64-token blocks, 16 splits) at the thres
 
 Printed (one JSON line): prefill dense-equivalent TFLOP/s as `value`, decode HBM GB/s (bytes the
 kernel actually has to read and write), the speedups over the same kernels at lambda = 0, roofline
-fractions, and the fp64 oracle's throughput on the host cores as a baseline.
+fractions, and the fp64 oracle's throughput on the host cores as a baseline.  Untimed extras in the
+same line (skipped with --quick): prefill at 50 % sparsity, decode at context 131072, the latent
+(MLA-shaped) decode at 50 % and 73 % sparsity, and the calibration sweep (lambda * L = alpha *
+exp(beta * s) fitted over L = 4K..128K and s = 0.3/0.5/0.7, achieved-vs-target sparsity, and the
+prefill at L = 131072, s = 0.75).
 """
 
 from __future__ import annotations
@@ -34,6 +38,12 @@ P_TARGET = 0.75
 D_B, D_HQ, D_HKV, D_CTX, D_D, D_PAGE, D_BLK, D_SPLITS = 32, 32, 8, 32768, 128, 16, 64, 16
 D_TARGET = 0.73
 CALIB_TILES = 8  # prefill calibration sample: 8 query tiles of 128 rows (1024 rows)
+# latent (MLA-shaped) decode
+M_B, M_HQ, M_D, M_DV, M_CTX, M_TARGETS = 64, 128, 576, 512, 32768, (0.5, 0.73)
+# calibration sweep
+C_L_VALUES = (4096, 8192, 16384, 32768, 65536, 131072)
+C_S_VALUES = (0.3, 0.5, 0.7)
+C_FINAL_L, C_FINAL_S = 131072, 0.75
 
 
 def parse():
@@ -45,6 +55,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
                     help="restrict the timed step (for profiling runs)")
+    ap.add_argument("--quick", action="store_true",
+                    help="only the timed step (no 128K decode, latent decode or calibration sweep)")
     return ap.parse_args()
 
 
@@ -114,85 +126,144 @@ def cpu_baseline(seconds: float):
 # GPU side
 # ------------------------------------------------------------------------------------------------
 
+def stratified_tiles(torch, nqt, n_heads, count, seed):
+    """Seeded calibration sample: random heads, query tiles spread evenly over the sequence."""
+    g = torch.Generator().manual_seed(seed)
+    heads = torch.randint(0, n_heads, (count,), generator=g).tolist()
+    tiles = [int((i + 0.5) * nqt / count) for i in range(count)]
+    return list(zip(heads, tiles))
+
+
 class Prefill:
-    def __init__(self, m, torch, synth):
+    def __init__(self, m, torch, synth, L=P_L, seed=None):
         self.m = m
         self.torch = torch
         dev = "cuda"
-        self.inp = synth.prefill_inputs(batch=P_B, hq=P_HQ, hkv=P_HKV, L=P_L, d=P_D, block_k=P_BLK,
-                                        window=True, seed=synth.config_seed(2), device=dev)
-        self.nqt = P_L // P_BLK
-        self.nkb = P_L // P_BLK
-        self.o = torch.empty(P_B, P_HQ, P_L, P_D, dtype=torch.bfloat16, device=dev)
-        self.lse = torch.empty(P_B, P_HQ, P_L, dtype=torch.float32, device=dev)
+        self.L = L
+        seed = synth.config_seed(2) if seed is None else seed
+        self.inp = synth.prefill_inputs(batch=P_B, hq=P_HQ, hkv=P_HKV, L=L, d=P_D, block_k=P_BLK,
+                                        window=True, seed=seed, device=dev)
+        self.nqt = L // P_BLK
+        self.nkb = L // P_BLK
+        self.o = torch.empty(P_B, P_HQ, L, P_D, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(P_B, P_HQ, L, dtype=torch.float32, device=dev)
         self.live = P_B * P_HQ * self.nqt * (self.nqt + 1) // 2
-        self.dense_flops = 4.0 * P_B * P_HQ * P_D * P_L * (P_L + 1) / 2
+        self.dense_flops = 4.0 * P_B * P_HQ * P_D * L * (L + 1) / 2
 
     def run(self, lam, **diag):
         self.m.blasst_prefill(self.inp.q, self.inp.k, self.inp.v, self.o, causal=True, block_q=P_BLK,
                               block_k=P_BLK, lam=lam, lse=self.lse, **diag)
 
-    def calibrate(self, target):
-        """Stats pass (QK^T, block maxima and decisions only) -> critical values of a sample of
-        8 query tiles (1024 rows) -> ln(lambda) at the target sparsity."""
+    def stats(self):
+        """Stats pass (QK^T, block maxima and decisions only): critical values of every tile."""
         torch = self.torch
         crit = torch.empty(P_B, P_HQ, self.nqt, self.nkb, dtype=torch.float32, device="cuda")
         self.m.blasst_prefill(self.inp.q, self.inp.k, self.inp.v, None, causal=True, block_q=P_BLK,
                               block_k=P_BLK, lam=0.0, crit=crit, stats_only=True)
         torch.cuda.synchronize()
-        # seeded heads, query tiles spread evenly over the sequence (short and long rows alike)
-        g = torch.Generator().manual_seed(4242)
-        heads = torch.randint(0, P_HQ, (CALIB_TILES,), generator=g).tolist()
-        tiles = [int((i + 0.5) * self.nqt / CALIB_TILES) for i in range(CALIB_TILES)]
-        sample = torch.stack([crit[0, h, t] for h, t in zip(heads, tiles)]).cpu().numpy()
-        ln_lam = self.m.blasst_calib_quantile(sample, target)
-        return math.exp(ln_lam)
+        return crit
+
+    def calibrate(self, target, crit=None):
+        """ln(lambda) at the target sparsity from the critical values of an 8-tile (1024-row) sample."""
+        crit = self.stats() if crit is None else crit
+        sample = self.torch.stack([crit[0, h, t] for h, t in stratified_tiles(self.torch, self.nqt, P_HQ,
+                                                                               CALIB_TILES, 4242)])
+        return math.exp(self.m.blasst_calib_quantile(sample.cpu().numpy(), target))
+
+    def measure(self, lam, steps):
+        torch = self.torch
+        cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+        self.run(lam, counters=cnt)
+        torch.cuda.synchronize()
+        live, skipped = int(cnt[0]), int(cnt[1])
+        sparse_ms = timed(torch, lambda: self.run(lam), steps)
+        dense_ms = timed(torch, lambda: self.run(0.0), steps)
+        return {"ms": round(sparse_ms, 4), "dense_ms": round(dense_ms, 4),
+                "speedup_vs_dense": round(dense_ms / sparse_ms, 3),
+                "dense_equiv_tflops": round(self.dense_flops / (sparse_ms * 1e-3) / 1e12, 2),
+                "dense_tflops": round(self.dense_flops / (dense_ms * 1e-3) / 1e12, 2),
+                "lambda": lam, "sparsity": round(skipped / live, 4)}
 
 
 class Decode:
-    def __init__(self, m, torch, synth):
+    def __init__(self, m, torch, synth, ctx=D_CTX, latent=False, seed=None):
         self.m = m
         self.torch = torch
+        self.latent = latent
+        self.ctx = ctx
         dev = "cuda"
-        self.d = synth.decode_inputs(batch=D_B, hq=D_HQ, hkv=D_HKV, ctx=D_CTX, d=D_D, page_size=D_PAGE,
-                                     block_k=D_BLK, window=True, seed=synth.config_seed(3), device=dev)
-        self.o = torch.empty(D_B, D_HQ, D_D, dtype=torch.bfloat16, device=dev)
-        self.lse = torch.empty(D_B, D_HQ, dtype=torch.float32, device=dev)
+        if latent:
+            self.B, self.Hq, self.Hkv, self.D, self.Dv, self.tile_rows = M_B, M_HQ, 1, M_D, M_DV, M_HQ
+        else:
+            self.B, self.Hq, self.Hkv, self.D, self.Dv, self.tile_rows = D_B, D_HQ, D_HKV, D_D, D_D, 0
+        seed = (synth.config_seed(5) if latent else synth.config_seed(3)) if seed is None else seed
+        self.d = synth.decode_inputs(batch=self.B, hq=self.Hq, hkv=self.Hkv, ctx=ctx, d=self.D, dv=self.Dv,
+                                     page_size=D_PAGE, block_k=D_BLK, window=True, seed=seed, device=dev,
+                                     latent=latent)
+        self.o = torch.empty(self.B, self.Hq, self.Dv, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(self.B, self.Hq, dtype=torch.float32, device=dev)
         self.nkb = -(-(self.d.block_table.shape[1] * D_PAGE) // D_BLK)
-        kw = self._kw(0.0)
+        self.n_rt = 1
         n = m.blasst_decode_workspace_size(self.d.q, self.d.k_cache, self.d.v_cache_t, self.d.block_table,
-                                           self.d.seq_lens, self.o, **kw)
+                                           self.d.seq_lens, self.o, **self._kw(0.0))
         self.ws = torch.empty(n, dtype=torch.uint8, device=dev)
 
     def _kw(self, lam):
-        return dict(page_size=D_PAGE, block_k=D_BLK, num_splits=D_SPLITS, lam=lam, lse=self.lse)
+        return dict(page_size=D_PAGE, block_k=D_BLK, num_splits=D_SPLITS, lam=lam, lse=self.lse,
+                    tile_rows=self.tile_rows, head_dim_v=self.Dv)
 
     def run(self, lam, **diag):
         d = self.d
         self.m.blasst_decode(d.q, d.k_cache, d.v_cache_t, d.block_table, d.seq_lens, self.o, workspace=self.ws,
                              **self._kw(lam), **diag)
 
+    def mask_shape(self):
+        return (self.B, self.Hkv, self.n_rt, self.nkb)
+
     def calibrate(self, target):
+        """ln(lambda) at the target sparsity from the critical values of every tile of the batch
+        (32 x 8 tiles of 4 rows, or 64 tiles of 128 rows: the ~1000-row sample)."""
         torch = self.torch
-        crit = torch.empty(D_B, D_HKV, 1, self.nkb, dtype=torch.float32, device="cuda")
+        crit = torch.empty(*self.mask_shape(), dtype=torch.float32, device="cuda")
         self.run(0.0, crit=crit, stats_only=True)
         torch.cuda.synchronize()
         return math.exp(self.m.blasst_calib_quantile(crit.cpu().numpy(), target))
 
     def bytes_moved(self, mask):
-        """HBM bytes the kernel must move: all K of every sequence, V of kept blocks, q, the page
-        table, the per-split partials (written and read back) and the output."""
-        import numpy as np
+        """HBM bytes the kernel has to move: all K of every sequence, V of kept blocks (none extra
+        for latent attention, where V is part of K), q, the page table, the per-split partials
+        (written and read back) and the output."""
         kept = int((mask == 0).sum())
-        live = int((mask != 2).sum())
-        k_bytes = D_B * D_HKV * D_CTX * D_D * 2
-        v_bytes = kept * D_BLK * D_D * 2          # every block is full at this context length
-        q_bytes = D_B * D_HQ * D_D * 2
+        k_bytes = self.B * self.Hkv * self.ctx * self.D * 2
+        v_bytes = 0 if self.latent else kept * D_BLK * self.Dv * 2     # every block is full here
+        q_bytes = self.B * self.Hq * self.D * 2
         table = self.d.block_table.numel() * 4
-        parts = D_B * D_HQ * D_SPLITS * (D_D + 1) * 4 * 2
-        out = D_B * D_HQ * D_D * 2 + D_B * D_HQ * 4
-        dense = k_bytes * 2 + q_bytes + table + parts + out
-        return k_bytes + v_bytes + q_bytes + table + parts + out, dense, kept, live
+        parts = self.B * self.Hq * D_SPLITS * (self.Dv + 1) * 4 * 2
+        out = self.B * self.Hq * self.Dv * 2 + self.B * self.Hq * 4
+        dense_v = 0 if self.latent else self.B * self.Hkv * self.ctx * self.Dv * 2
+        return (k_bytes + v_bytes + q_bytes + table + parts + out,
+                k_bytes + dense_v + q_bytes + table + parts + out)
+
+    def measure(self, lam, steps, ms=None):
+        torch = self.torch
+        mask = torch.empty(*self.mask_shape(), dtype=torch.uint8, device="cuda")
+        self.run(lam, skip_mask=mask)
+        torch.cuda.synchronize()
+        mh = mask.cpu().numpy()
+        kept, live = int((mh == 0).sum()), int((mh != 2).sum())
+        moved, dense_bytes = self.bytes_moved(mh)
+        sparse_ms = timed(torch, lambda: self.run(lam), steps) if ms is None else ms
+        dense_ms = timed(torch, lambda: self.run(0.0), steps)
+        r = {"ms": round(sparse_ms, 4), "dense_ms": round(dense_ms, 4),
+             "speedup_vs_dense": round(dense_ms / sparse_ms, 3),
+             "hbm_gbps": round(moved / (sparse_ms * 1e-3) / 1e9, 1),
+             "dense_hbm_gbps": round(dense_bytes / (dense_ms * 1e-3) / 1e9, 1),
+             "bytes_moved": moved, "lambda": lam, "a": lam * self.ctx, "sparsity": round(1.0 - kept / live, 4)}
+        if self.latent:
+            blocks = live
+            flops = blocks * D_BLK * self.Hq * (self.D * 2) + kept * D_BLK * self.Hq * (self.Dv * 2)
+            r["mfma_tflops"] = round(flops / (sparse_ms * 1e-3) / 1e12, 2)
+        return r
 
 
 def timed(torch, fn, steps):
@@ -208,6 +279,50 @@ def timed(torch, fn, steps):
     return start.elapsed_time(end) / steps
 
 
+def calibration_sweep(m, torch, synth, steps):
+    """Calibration: stats pass per L, 8-tile sample, quantile inversion per target s, least-squares
+    fit of lambda * L = alpha * exp(beta * s), achieved-vs-target sparsity of the fitted thresholds on
+    every tile, and the long prefill at L = 131072, s = 0.75."""
+    import numpy as np
+    pts, crits = [], {}
+    final = None
+    for i, L in enumerate(C_L_VALUES):
+        p = Prefill(m, torch, synth, L=L, seed=synth.config_seed(4, i))
+        crit = p.stats()
+        for s in C_S_VALUES:
+            pts.append((L, s, p.calibrate(s, crit=crit)))
+        c = crit.cpu().numpy().ravel()
+        crits[L] = c[~np.isnan(c)]
+        if L == C_FINAL_L:
+            final = p
+        else:
+            del p
+        del crit
+        torch.cuda.empty_cache()
+    L_arr, s_arr, lam_arr = (np.array([x[k] for x in pts], dtype=np.float64) for k in range(3))
+    alpha, beta, rmse = m.blasst_calibrate(L_arr, s_arr, lam_arr)
+    table = []
+    errs = []
+    for L in C_L_VALUES:
+        row = {"L": L}
+        for s in C_S_VALUES:
+            lam = m.blasst_lambda_for(alpha, beta, s, L)
+            ach = float(np.mean(crits[L] < math.log(lam)))
+            row[f"s{s}"] = round(ach, 4)
+            errs.append(abs(ach - s))
+        table.append(row)
+    lam_final = m.blasst_lambda_for(alpha, beta, C_FINAL_S, C_FINAL_L)
+    fin = final.measure(lam_final, max(2, steps // 3))
+    fin["target_sparsity"] = C_FINAL_S
+    return {"alpha": alpha, "beta": beta, "fit_rmse_ln_lambdaL": round(rmse, 4),
+            "points": [{"L": int(L), "s": s, "lambda": lam} for (L, s, lam) in pts],
+            "achieved_sparsity_with_fit": table, "mean_abs_sparsity_error": round(float(np.mean(errs)), 4),
+            "max_abs_sparsity_error": round(float(np.max(errs)), 4),
+            "prefill_131072_s075": fin,
+            "workload": "GQA 32 q / 8 kv heads, d 128, bf16, causal, 128x128 blocks; L in 4K..128K; "
+                        "s in {0.3, 0.5, 0.7}; 8-tile (1024-row) sample per L"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -218,7 +333,6 @@ def main():
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
-    import numpy as np
     import torch
 
     import long_context_online_amd as m
@@ -265,51 +379,66 @@ def main():
               "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
     config = {"workload": "", "parallelism": "none (1 GPU)"}
     if pre:
-        mask = torch.empty(P_B, P_HQ, pre.nqt, pre.nkb, dtype=torch.uint8, device="cuda")
+        r = pre.measure(lam_p, max(3, args.steps // 2))
         cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
-        pre.run(lam_p, skip_mask=mask, counters=cnt)
+        pre.run(lam_p, counters=cnt)
         torch.cuda.synchronize()
         live, skipped = int(cnt[0]), int(cnt[1])
         kept = live - skipped
-        dense_ms = timed(torch, lambda: pre.run(0.0), max(3, args.steps // 2))
         alg_flops = (live + kept) * 2.0 * P_BLK * P_BLK * P_D
         tflops = pre.dense_flops / (pre_ms * 1e-3) / 1e12
         achieved = alg_flops / (pre_ms * 1e-3) / 1e12
         result.update({"value": round(tflops, 2), "unit": "TFLOP/s (dense-equivalent)"})
-        result["prefill"] = {
-            "ms": round(pre_ms, 4), "dense_ms": round(dense_ms, 4), "speedup_vs_dense": round(dense_ms / pre_ms, 3),
-            "dense_equiv_tflops": round(tflops, 2), "dense_tflops": round(pre.dense_flops / (dense_ms * 1e-3) / 1e12, 2),
-            "lambda": lam_p, "target_sparsity": P_TARGET, "sparsity": round(skipped / live, 4),
-            "live_tile_blocks": live, "frac_of_bf16_peak_dense_equiv": round(tflops / PEAK_BF16_TFLOPS, 4),
-        }
+        r.update({"ms": round(pre_ms, 4), "speedup_vs_dense": round(r["dense_ms"] / pre_ms, 3),
+                  "dense_equiv_tflops": round(tflops, 2), "target_sparsity": P_TARGET,
+                  "live_tile_blocks": live, "frac_of_bf16_peak_dense_equiv": round(tflops / PEAK_BF16_TFLOPS, 4)})
+        result["prefill"] = r
         result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                              "kernel": "prefill_bf16_kernel<128,128,4,bf16 out>",
-                              "algorithmic": "QK^T on every live 128x128 tile-block + PV on kept ones, 4.19 MFLOP each"}
+                              "kernel": "prefill_bf16_kernel<128, 128, 2, bf16 out>",
+                              "algorithmic": "QK^T on every live 128x128 tile-block + PV on kept ones, "
+                                             "4.19 MFLOP each; launch average from HIP events in the timed region"}
         config["workload"] = ("GQA prefill, Llama-3.1-8B-shaped: batch 1, 32 q / 8 kv heads, d 128, L 32768, causal, "
                               "128x128 blocks, bf16 in/out, lambda calibrated for 75% sparsity")
         config.update({"batch": P_B, "seq_len": P_L, "q_heads": P_HQ, "kv_heads": P_HKV, "head_dim": P_D})
+        if not args.quick:
+            lam50 = pre.calibrate(0.5)
+            result["prefill_s050"] = pre.measure(lam50, max(3, args.steps // 2))
+            result["prefill_s050"]["target_sparsity"] = 0.5
     if dec:
-        mask = torch.empty(D_B, D_HKV, 1, dec.nkb, dtype=torch.uint8, device="cuda")
-        dec.run(lam_d, skip_mask=mask)
-        torch.cuda.synchronize()
-        mh = mask.cpu().numpy()
-        moved, dense_bytes, kept, live = dec.bytes_moved(mh)
-        dense_ms = timed(torch, lambda: dec.run(0.0), max(3, args.steps))
-        gbps = moved / (dec_ms * 1e-3) / 1e9
-        result["decode"] = {
-            "ms": round(dec_ms, 4), "dense_ms": round(dense_ms, 4), "speedup_vs_dense": round(dense_ms / dec_ms, 3),
-            "hbm_gbps": round(gbps, 1), "dense_hbm_gbps": round(dense_bytes / (dense_ms * 1e-3) / 1e9, 1),
-            "bytes_moved": moved, "lambda": lam_d, "a": lam_d * D_CTX, "target_sparsity": D_TARGET,
-            "sparsity": round(1.0 - kept / live, 4), "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
-            "workload": "paged GQA decode: batch 32, 32 q / 8 kv heads, d 128, context 32768, 16-token pages, "
-                        "64-token blocks, 16 splits, bf16",
-        }
-        result["roofline_decode"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
-                                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None}
+        r = dec.measure(lam_d, args.steps, ms=dec_ms)
+        r.update({"target_sparsity": D_TARGET, "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
+                  "workload": "paged GQA decode: batch 32, 32 q / 8 kv heads, d 128, context 32768, 16-token "
+                              "pages, 64-token blocks, 16 splits, bf16"})
+        result["decode"] = r
+        result["roofline_decode"] = {"bound": "hbm", "achieved": r["hbm_gbps"], "peak": PEAK_HBM_GBPS,
+                                     "unit": "GB/s", "frac": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
+                                     "traffic": None, "kernel": "decode_gqa_kernel + decode_combine_kernel"}
         if not pre:
-            result.update({"value": round(gbps, 1), "unit": "GB/s"})
-            config["workload"] = result["decode"]["workload"]
+            result.update({"value": r["hbm_gbps"], "unit": "GB/s"})
+            config["workload"] = r["workload"]
+    del pre, dec
+    torch.cuda.empty_cache()
+    if not args.quick and args.only == "all":
+        d128 = Decode(m, torch, synth, ctx=131072, seed=synth.config_seed(3, 1))
+        lam = d128.calibrate(D_TARGET)
+        r = d128.measure(lam, args.steps)
+        r.update({"target_sparsity": D_TARGET, "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4)})
+        result["decode_131072"] = r
+        del d128
+        torch.cuda.empty_cache()
+        mla = Decode(m, torch, synth, ctx=M_CTX, latent=True)
+        result["mla_decode"] = {"workload": "latent decode, DeepSeek-shaped: batch 64, 128 q heads on one latent "
+                                            "head, 576-dim scores, V = first 512 channels, context 32768, 16-token "
+                                            "pages, 64-token blocks, 16 splits, 128-head tiles, bf16"}
+        for tgt in M_TARGETS:
+            lam = mla.calibrate(tgt)
+            r = mla.measure(lam, args.steps)
+            r.update({"target_sparsity": tgt, "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4)})
+            result["mla_decode"][f"s{tgt}"] = r
+        del mla
+        torch.cuda.empty_cache()
+        result["calibration"] = calibration_sweep(m, torch, synth, args.steps)
     result["config"] = config
     result["context"] = {"pages_prefill_speedup": "1.62x at 74.7% sparsity (B200/H200, pages' abstract)",
                          "pages_decode_speedup": "1.48x at 73.2% sparsity"}
