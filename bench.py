@@ -57,6 +57,10 @@ def parse():
                     help="restrict the timed step (for profiling runs)")
     ap.add_argument("--quick", action="store_true",
                     help="only the timed step (no 128K decode, latent decode or calibration sweep)")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="profiling run: calibration pass, warm-up and timed steps only (no dense or diagnostic "
+                         "launches, so each kernel's profiler average is the timed average), plus a plain "
+                         "256 MiB device copy per step whose byte counters scale the profiler's traffic counters")
     return ap.parse_args()
 
 
@@ -314,11 +318,17 @@ def calibration_sweep(m, torch, synth, steps):
     lam_final = m.blasst_lambda_for(alpha, beta, C_FINAL_S, C_FINAL_L)
     fin = final.measure(lam_final, max(2, steps // 3))
     fin["target_sparsity"] = C_FINAL_S
+    fin["threshold"] = "fitted model alpha * exp(beta * s) / L"
+    lam_direct = final.calibrate(C_FINAL_S)
+    fin_direct = final.measure(lam_direct, max(2, steps // 3))
+    fin_direct["target_sparsity"] = C_FINAL_S
+    fin_direct["threshold"] = "quantile of the 8-tile sample at L = 131072"
     return {"alpha": alpha, "beta": beta, "fit_rmse_ln_lambdaL": round(rmse, 4),
             "points": [{"L": int(L), "s": s, "lambda": lam} for (L, s, lam) in pts],
             "achieved_sparsity_with_fit": table, "mean_abs_sparsity_error": round(float(np.mean(errs)), 4),
             "max_abs_sparsity_error": round(float(np.max(errs)), 4),
             "prefill_131072_s075": fin,
+            "prefill_131072_s075_sample_calibrated": fin_direct,
             "workload": "GQA 32 q / 8 kv heads, d 128, bf16, causal, 128x128 blocks; L in 4K..128K; "
                         "s in {0.3, 0.5, 0.7}; 8-tile (1024-row) sample per L"}
 
@@ -356,6 +366,9 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.profile_only:
+        ref_src = torch.empty(128 * 1024 * 1024, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        ref_dst = torch.empty_like(ref_src)
     # timed region: exactly `steps` steps, with per-kernel events inside
     ev = []
     t0 = time.perf_counter()
@@ -373,6 +386,15 @@ def main():
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     dec_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    if args.profile_only:
+        for _ in range(args.steps):
+            ref_dst.copy_(ref_src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_only": True, "steps": args.steps, "warmup": args.warmup,
+                          "prefill_ms": round(pre_ms, 4) if pre else None, "decode_ms": round(dec_ms, 4) if dec else None,
+                          "prefill_lambda": lam_p, "decode_lambda": lam_d,
+                          "reference_copy_bytes": 2 * ref_src.numel() * ref_src.element_size()}))
+        return
 
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "ms_per_step": round(wall_ms, 4), "higher_is_better": True, "scaling": "weak",
