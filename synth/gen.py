@@ -184,6 +184,10 @@ def decode_inputs(*, batch, hq, hkv, ctx, d, dv=None, dtype=torch.bfloat16, page
     P = live + spare
     gen = _gen(seed, device)
     perm = torch.randperm(P, generator=gen, device=device).to(torch.int32)
+    # equal lengths: one AR(1) scan for the whole batch (far fewer small kernels than one per sequence)
+    batched = window and len(set(lens)) == 1
+    if batched:
+        z_all, z_last_all = _ar1(gen, (batch, hkv), lens[0], dc, device)
     block_table = torch.empty(batch, max_pages, dtype=torch.int32, device=device)
     spare_ids = perm[live:]
     k_cache = torch.full((P, hkv, page_size, d), float("nan"), dtype=dtype, device=device)
@@ -199,7 +203,9 @@ def decode_inputs(*, batch, hq, hkv, ctx, d, dv=None, dtype=torch.bfloat16, page
         if npg < max_pages:
             block_table[b, npg:] = spare_ids[0]
         n_blocks = -(-n // block_k)
-        if window:
+        if batched:
+            z, z_last = z_all[b], z_last_all[b]
+        elif window:
             z, z_last = _ar1(gen, (hkv,), n, dc, device)                 # [Hkv, n, dc]
         else:
             z = torch.randn(hkv, n, dc, generator=gen, device=device)
