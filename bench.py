@@ -341,7 +341,7 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
+    cpu = None if (args.no_cpu_baseline or args.profile_only) else cpu_baseline(args.cpu_seconds)
 
     import torch
 

@@ -72,6 +72,14 @@ __device__ __forceinline__ float row_crit(float m_blk, float m_run) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroup barrier that waits only for this wave's LDS operations.  __syncthreads() also waits for
+// every outstanding global load (vmcnt(0)), which would stall on the next block's direct-to-LDS
+// prefetch; here those loads stay in flight and are waited for explicitly before the buffer swap.
+// Must be reached by every wave of the workgroup (uniform control flow).
+__device__ __forceinline__ void barrier_lds_only() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // max over lanes l and l ^ 32
 __device__ __forceinline__ float max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 
@@ -103,15 +111,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
-}
-
-// 16-byte chunk swizzle used by the LDS tiles: chunk c of row r is stored at chunk c ^ swz(r).
-// For 8 consecutive rows starting at a multiple of 8 the swizzle takes 8 distinct values, and for
-// rows 8*i + e (i = 0..NCH-1, fixed e) it is a bijection of i, so both the MFMA operand reads and the
-// transposed tile writes spread over the banks.
-template <int NCH>
-__device__ __forceinline__ int swz(int row) {
-  return (row ^ (row >> 3)) & (NCH - 1);
 }
 
 }  // namespace blasst

@@ -16,6 +16,8 @@
 //   * O^T = V^T P^T with v_mfma_f32_16x16x32_bf16: P^T comes from the score registers; the V^T
 //     operand is read from the same LDS tile with ds_read_b64_tr_b16 (transpose read), so V never
 //     needs a second copy; the wave's 16 heads x 512 channels of O live in 128 registers.
+//   * the latent row stride (1168 bytes = 144 mod 256) keeps the 16-row score-operand reads free of
+//     bank conflicts on the 64-bank LDS (the transpose reads see at most a 2-way conflict);
 //   * registers are the scarce resource (q and O of 128 heads are 400 KB of the CU's 512 KB
 //     register file), so loops that would hoist every LDS read carry scheduling barriers.
 #include "common.hpp"
@@ -25,7 +27,7 @@ namespace blasst {
 namespace {
 constexpr int DQK = 576, DV = 512, PAGE = 16, BK = 64, HPW = 16;
 constexpr int CH = DQK / 8;                 // 16-byte chunks per latent row (72)
-constexpr int CP = CH + 2;                  // with two pad chunks (row = 1184 bytes, 32 mod 128)
+constexpr int CP = CH + 1;                  // with one pad chunk (row = 1168 bytes = 16 x odd mod 256)
 constexpr int ROW = CP * 16;
 constexpr int INS = (BK * CP + 63) / 64;    // wave-wide direct loads per block (74)
 constexpr int BUF = INS * 1024;
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(TR / HPW * 64, 1) void decode_latent_kernel(DecodeA
       sVote[buf][wave] = wave_keep ? 1 : 0;
       sCrit[buf][wave] = wcrit;
     }
-    __syncthreads();  // vote barrier
+    barrier_lds_only();  // vote barrier (the next block's loads stay in flight)
     int keep = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) keep |= sVote[buf][w];

@@ -25,9 +25,11 @@
 //   * the skip vote: per-row predicate -> wave ballot -> one LDS flag per wave -> OR over the
 //     tile's waves after the vote barrier; the skip is a uniform branch, so a skipped block issues
 //     no v_exp and no P.V MFMA;
-//   * LDS rows are padded (K: 16 bytes, so the 8 rows of one 16-byte read pass fall on distinct
-//     banks; V: 32 bytes, so the 4 row segments of one transpose-read pass do), and every read
-//     address is one per-lane base plus an immediate;
+//   * LDS rows are padded so that reads are free of bank conflicts on the 64-bank (256-byte) LDS:
+//     K rows are 16 mod 256 bytes apart (16 rows x 16 bytes of one read pass fall on distinct
+//     banks), V rows 64 mod 256 bytes apart (the two 16-lane groups of a transpose-read pass read
+//     4 rows x 32 bytes each at column offsets 0 and 32); every read address is one per-lane base
+//     plus an immediate;
 //   * heavy (late, long causal) tiles launch first, and workgroups of one kv head are mapped to the
 //     same XCD (workgroups are dispatched round-robin over the 8 XCDs) for L2 reuse.
 #include <type_traits>
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   constexpr int KCP = KCH + 1;       // ... plus the pad chunk
   constexpr int KROW = KCP * 16;     // bytes per K row in LDS
   constexpr int VCH = D / 8;         // 16-byte chunks per V row
-  constexpr int VCP = VCH + 2;       // ... plus two pad chunks
+  constexpr int VCP = VCH + 4;       // ... plus four pad chunks (row stride = 64 mod 256 bytes)
   constexpr int VROW = VCP * 16;     // bytes per V row in LDS
   constexpr int MT = BC / 32;        // key m-tiles of S^T
   constexpr int KS = D / 16;         // k-steps over the head dim
@@ -178,13 +180,22 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) s[mt] = f32x16{};
     const unsigned char *kb = sK[buf] + l32 * KROW + hi * 16;
+    // K fragments are read one k-step ahead of the MFMAs that consume them, so LDS latency overlaps
+    // the previous k-step's MFMAs instead of stalling every MFMA
+    bf16x8 kf[2][MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) kf[0][mt] = *(const bf16x8 *)(kb + mt * 32 * KROW);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
+      if (kk + 1 < KS) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 kf = *(const bf16x8 *)(kb + mt * 32 * KROW + kk * 32);
-        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[mt], 0, 0, 0);
+        for (int mt = 0; mt < MT; ++mt)
+          kf[(kk + 1) & 1][mt] = *(const bf16x8 *)(kb + mt * 32 * KROW + (kk + 1) * 32);
       }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk & 1][mt], qf[kk], s[mt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // keep the next k-step's reads ahead of these MFMAs
     }
 
     // ---- causal / tail mask (only blocks that need it) ----
@@ -217,7 +228,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       sVote[buf][wave] = wave_keep ? 1 : 0;
       sCrit[buf][wave] = wcrit;
     }
-    __syncthreads();  // vote barrier
+    barrier_lds_only();  // vote barrier (the next block's loads stay in flight)
     int keep = 0;
 #pragma unroll
     for (int w = 0; w < WPT; ++w) keep |= sVote[buf][tile * WPT + w];
