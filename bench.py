@@ -18,6 +18,7 @@ prefill at L = 131072, s = 0.75).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -44,6 +45,20 @@ M_B, M_HQ, M_D, M_DV, M_CTX, M_TARGETS = 64, 128, 576, 512, 32768, (0.5, 0.73)
 C_L_VALUES = (4096, 8192, 16384, 32768, 65536, 131072)
 C_S_VALUES = (0.3, 0.5, 0.7)
 C_FINAL_L, C_FINAL_S = 131072, 0.75
+
+
+def profiled_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by what the counter reads for a plain device copy of known size), or None
+    when the kernel's sources have changed since those counters were taken."""
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[kernel]
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
 
 
 def parse():
@@ -153,6 +168,8 @@ class Prefill:
         self.lse = torch.empty(P_B, P_HQ, L, dtype=torch.float32, device=dev)
         self.live = P_B * P_HQ * self.nqt * (self.nqt + 1) // 2
         self.dense_flops = 4.0 * P_B * P_HQ * P_D * L * (L + 1) / 2
+        # every input read once and every output written once (bf16 q, k, v, o; fp32 lse)
+        self.min_bytes = 2 * P_B * L * P_D * (2 * P_HQ + 2 * P_HKV) + 4 * P_B * P_HQ * L
 
     def run(self, lam, **diag):
         self.m.blasst_prefill(self.inp.q, self.inp.k, self.inp.v, self.o, causal=True, block_q=P_BLK,
@@ -416,7 +433,10 @@ def main():
                   "live_tile_blocks": live, "frac_of_bf16_peak_dense_equiv": round(tflops / PEAK_BF16_TFLOPS, 4)})
         result["prefill"] = r
         result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                              "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                              "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                              "traffic": profiled_traffic("prefill_bf16_kernel<128, 128, 2, false, false>"),
+                              "traffic_unit": "HBM bytes per launch",
+                              "min_bytes": pre.min_bytes,
                               "kernel": "prefill_bf16_kernel<128, 128, 2, bf16 out>",
                               "algorithmic": "QK^T on every live 128x128 tile-block + PV on kept ones, "
                                              "4.19 MFLOP each; launch average from HIP events in the timed region"}
@@ -435,7 +455,9 @@ def main():
         result["decode"] = r
         result["roofline_decode"] = {"bound": "hbm", "achieved": r["hbm_gbps"], "peak": PEAK_HBM_GBPS,
                                      "unit": "GB/s", "frac": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
-                                     "traffic": None, "kernel": "decode_gqa_kernel + decode_combine_kernel"}
+                                     "traffic": profiled_traffic("decode_gqa_kernel<false>"),
+                                     "traffic_unit": "HBM bytes per launch of decode_gqa_kernel",
+                                     "kernel": "decode_gqa_kernel + decode_combine_kernel"}
         if not pre:
             result.update({"value": r["hbm_gbps"], "unit": "GB/s"})
             config["workload"] = r["workload"]
