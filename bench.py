@@ -350,6 +350,28 @@ def calibration_sweep(m, torch, synth, steps):
                         "s in {0.3, 0.5, 0.7}; 8-tile (1024-row) sample per L"}
 
 
+def practical_ceilings(torch):
+    """Measured ceilings on this GPU, as context for the roofline fractions: a bf16 GEMM through the
+    vendor BLAS (torch.matmul, 8192^3) and a plain device-to-device copy of 4 GiB."""
+    out = {}
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    ms = timed(torch, lambda: torch.matmul(a, b), 10)
+    out["bf16_gemm_8192_tflops"] = round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+    del a, b
+    x = torch.empty(2 * 1024 ** 3, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    ms = timed(torch, lambda: y.copy_(x), 5)
+    out["copy_4gib_gbps_read_plus_write"] = round(2 * x.numel() * 2 / (ms * 1e-3) / 1e9, 1)
+    del x, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -483,6 +505,7 @@ def main():
         del mla
         torch.cuda.empty_cache()
         result["calibration"] = calibration_sweep(m, torch, synth, args.steps)
+        result["ceilings"] = practical_ceilings(torch)
     result["config"] = config
     result["context"] = {"pages_prefill_speedup": "1.62x at 74.7% sparsity (B200/H200, pages' abstract)",
                          "pages_decode_speedup": "1.48x at 73.2% sparsity"}

@@ -287,11 +287,13 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
 }
 
 // Log-sum-exp merge of the per-split partials: one wave per (sequence, q head), four per
-// workgroup.  Lane s < S reads lse_s; the split weights exp(lse_s - LSE) are shared with shuffles,
-// and each lane accumulates Dv/64 output channels, so every partial row is read coalesced.
-template <bool OUT_F32>
+// workgroup.  Lane s < S reads lse_s to form the global max and sum; each lane then owns CPL output
+// channels (pairs 2 * lane + 128 k), and the partial rows of SC splits are loaded together before
+// any is used, so the loads of a chunk overlap instead of paying one memory latency per split.
+template <bool OUT_F32, int CPL>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float *ws_o, const float *ws_lse, void *o,
-                                                              float *lse_out, int BH, int S, int Dv) {
+                                                              float *lse_out, int BH, int S) {
+  constexpr int Dv = CPL * 64, NP = CPL / 2, SC = CPL == 2 ? 16 : 8;
   const int lane = threadIdx.x & 63;
   const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (bh >= BH) return;
@@ -306,42 +308,64 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *ws_o, 
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  for (int c0 = 0; c0 < Dv; c0 += 128) {
-    const int c = c0 + lane * 2;
-    float acc0 = 0.f, acc1 = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float ls = pl[s];
-      if (ls == kNegInf) continue;
-      const float w = __expf(ls - mx);
-      if (c < Dv) {
-        const float2 v = *(const float2 *)(ws_o + ((int64_t)bh * S + s) * Dv + c);
-        acc0 += w * v.x;
-        acc1 += w * v.y;
+  float2 acc[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) acc[k] = make_float2(0.f, 0.f);
+  const float *po = ws_o + (int64_t)bh * S * Dv + lane * 2;
+  for (int s0 = 0; s0 < S; s0 += SC) {
+    float ls[SC];
+    float2 v[SC][NP];
+#pragma unroll
+    for (int u = 0; u < SC; ++u) {
+      const bool ok = s0 + u < S;
+      ls[u] = ok ? pl[s0 + u] : kNegInf;
+#pragma unroll
+      for (int k = 0; k < NP; ++k)
+        v[u][k] = ok ? *(const float2 *)(po + (int64_t)(s0 + u) * Dv + 128 * k) : make_float2(0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < SC; ++u) {
+      const float w = ls[u] == kNegInf ? 0.f : __expf(ls[u] - mx);
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        acc[k].x += w * v[u][k].x;
+        acc[k].y += w * v[u][k].y;
       }
     }
-    if (c < Dv) {
-      if (OUT_F32) {
-        float2 r;
-        r.x = acc0 * inv;
-        r.y = acc1 * inv;
-        *(float2 *)((float *)o + (int64_t)bh * Dv + c) = r;
-      } else {
-        *(uint32_t *)((__bf16 *)o + (int64_t)bh * Dv + c) = pack_bf16x2(acc0 * inv, acc1 * inv);
-      }
+  }
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int c = lane * 2 + 128 * k;
+    if (OUT_F32) {
+      *(float2 *)((float *)o + (int64_t)bh * Dv + c) = make_float2(acc[k].x * inv, acc[k].y * inv);
+    } else {
+      *(uint32_t *)((__bf16 *)o + (int64_t)bh * Dv + c) = pack_bf16x2(acc[k].x * inv, acc[k].y * inv);
     }
   }
   if (lse_out && lane == 0) lse_out[bh] = tot > 0.f ? mx + __logf(tot) : kNegInf;
 }
 
+// Dv is 128 (GQA / MHA / MQA) or 512 (latent attention).
 hipError_t launch_decode_combine(const DecodeArgs &a, int Dv, hipStream_t st) {
   const int BH = a.B * a.Hq;
   const int grid = (BH + 3) / 4;
-  if (a.out_f32)
-    hipLaunchKernelGGL(decode_combine_kernel<true>, dim3(grid), dim3(256), 0, st, a.ws_o, a.ws_lse, a.o, a.lse,
-                       BH, a.num_splits, Dv);
-  else
-    hipLaunchKernelGGL(decode_combine_kernel<false>, dim3(grid), dim3(256), 0, st, a.ws_o, a.ws_lse, a.o, a.lse,
-                       BH, a.num_splits, Dv);
+  if (Dv == 128) {
+    if (a.out_f32)
+      hipLaunchKernelGGL((decode_combine_kernel<true, 2>), dim3(grid), dim3(256), 0, st, a.ws_o, a.ws_lse, a.o, a.lse,
+                         BH, a.num_splits);
+    else
+      hipLaunchKernelGGL((decode_combine_kernel<false, 2>), dim3(grid), dim3(256), 0, st, a.ws_o, a.ws_lse, a.o, a.lse,
+                         BH, a.num_splits);
+  } else if (Dv == 512) {
+    if (a.out_f32)
+      hipLaunchKernelGGL((decode_combine_kernel<true, 8>), dim3(grid), dim3(256), 0, st, a.ws_o, a.ws_lse, a.o, a.lse,
+                         BH, a.num_splits);
+    else
+      hipLaunchKernelGGL((decode_combine_kernel<false, 8>), dim3(grid), dim3(256), 0, st, a.ws_o, a.ws_lse, a.o, a.lse,
+                         BH, a.num_splits);
+  } else {
+    return hipErrorNotSupported;
+  }
   return hipGetLastError();
 }
 

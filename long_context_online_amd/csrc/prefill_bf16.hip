@@ -152,7 +152,9 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   // ---- online-softmax state (per lane: query row l32 of this wave) -----------------------------
   float m_dec = kNegInf;  // running max used by the skip rule (restarts at each split)
   float m_acc = kNegInf;  // running max of the accumulation
-  float l_part = 0.f;     // partial row sum over the keys this lane holds
+  // partial row sums over the keys this lane holds, of the bf16-rounded probabilities that also
+  // enter P.V (two accumulators, summed in the epilogue, to shorten the dependency chain)
+  float l_part = 0.f, l_part2 = 0.f;
   f32x16 o_acc[MTV];
 #pragma unroll
   for (int i = 0; i < MTV; ++i) o_acc[i] = f32x16{};
@@ -251,6 +253,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       if (__ballot(m_new > m_acc) != 0ull) {
         const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_acc - m_new) * a.scale_log2);
         l_part *= alpha;
+        l_part2 *= alpha;
 #pragma unroll
         for (int i = 0; i < MTV; ++i) o_acc[i] *= alpha;
         m_acc = m_new;
@@ -263,11 +266,14 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       for (int kk = 0; kk < KSV; ++kk) {
         bf16x8 pf;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = fast_exp2(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + e], a.scale_log2, -base));
-          l_part += p;
-          pf[e] = (__bf16)p;
-        }
+        for (int e = 0; e < 8; ++e)
+          pf[e] = (__bf16)fast_exp2(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + e], a.scale_log2, -base));
+        // row sum: one bf16 dot2 with (1, 1) per pair of probabilities
+        const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), one2, l_part, false);
+        l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), one2, l_part2, false);
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), one2, l_part, false);
+        l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, l_part2, false);
 #pragma unroll
         for (int mv = 0; mv < MTV; ++mv) {
           const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -299,6 +305,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   if (STATS) return;
 
   // ---- epilogue: O = O^T / l, LSE = m * scale + ln l ----
+  l_part += l_part2;
   const float l_row = l_part + __shfl_xor(l_part, 32);
   const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
   if (row_ok) {
