@@ -18,10 +18,11 @@
 //     O^T = V^T P^T; the V^T operand is read from a row-major V tile with the gfx950 transpose
 //     read ds_read_b64_tr_b16 (within a 16-lane group, output lane i, element k is element i%4 of
 //     source lane 4k + i/4's 8-byte read), so no transpose pass is needed anywhere;
-//   * K and V both go global -> LDS directly (global_load_lds_dwordx4, no registers, no VALU) and
-//     are prefetched one block ahead into double-buffered LDS, so a block costs two barriers: the
-//     vote barrier and the buffer-swap barrier, and staging a skipped block's V costs only the
-//     load instructions;
+//   * K and V both go global -> LDS directly (global_load_lds_dwordx4, no registers, no VALU) into
+//     double-buffered LDS; the block loop is software-pipelined by one block (the P.V product of
+//     block t - 1 runs in the same iteration as QK^T of block t), so ONE barrier per block both
+//     publishes the votes and makes the next K block and this V block visible, and staging a
+//     skipped block's V costs only the load instructions;
 //   * the skip vote: per-row predicate -> wave ballot -> one LDS flag per wave -> OR over the
 //     tile's waves after the vote barrier; the skip is a uniform branch, so a skipped block issues
 //     no v_exp and no P.V MFMA;
@@ -162,25 +163,67 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   const int mask_row = ((b * a.Hq + hq) * a.nqt + qt) * a.nkb;
   const bool tile_leader = wit == 0 && lane == 0;
 
+  // ---- block loop, software-pipelined by one block: iteration t does the P.V product of block
+  // t - 1 (its scores are still in registers) and then QK^T, row max and vote of block t.  One
+  // barrier per iteration both publishes block t's votes and makes K_{t+1} and V_t (prefetched at
+  // the top of the iteration into the buffers that iteration t - 1 finished with) visible. ----
+  f32x16 s[MT];            // scores of the block whose P.V is pending
+  float mx_pend = kNegInf; // its row max
+  bool keep_pend = false;  // its decision
   if (J > 0) {
     load_k(0, 0);
-    if (!STATS) load_v(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-  for (int j = 0; j < J; ++j) {
-    const int buf = j & 1;
-    const bool has_next = j + 1 < J;
-    if (has_next) {
-      load_k(j + 1, buf ^ 1);
-      if (!STATS) load_v(j + 1, buf ^ 1);
+  for (int t = 0; t <= J; ++t) {
+    const int buf = t & 1;
+    if (t < J) {
+      if (t + 1 < J) load_k(t + 1, buf ^ 1);
+      if (!STATS) load_v(t, buf);
     }
-    if ((j % chunk) == 0) m_dec = kNegInf;
 
-    // ---- S^T = K_j Q^T ----
-    f32x16 s[MT];
+    if (!STATS && keep_pend) {
+      // ---- kept block t - 1: online-softmax update and O^T += V^T P^T ----
+      const float m_new = fmaxf(m_acc, mx_pend);
+      if (__ballot(m_new > m_acc) != 0ull) {
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_acc - m_new) * a.scale_log2);
+        l_part *= alpha;
+        l_part2 *= alpha;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) s[mt] = f32x16{};
+        for (int i = 0; i < MTV; ++i) o_acc[i] *= alpha;
+        m_acc = m_new;
+      }
+      const float base = (m_acc == kNegInf) ? 0.f : m_acc * a.scale_log2;
+      const unsigned char *vb = sV[buf ^ 1] + tr_off;
+      // P^T for k-step kk (16 keys) is formed right before its MFMAs: keys of score registers
+      // s[kk/2][8*(kk%2) .. +7], i.e. key 16*kk + 8*(e/4) + 4*hi + e%4 for element e.
+#pragma unroll
+      for (int kk = 0; kk < KSV; ++kk) {
+        bf16x8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pf[e] = (__bf16)fast_exp2(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + e], a.scale_log2, -base));
+        // row sum: one bf16 dot2 with (1, 1) per pair of probabilities
+        const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), one2, l_part, false);
+        l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), one2, l_part2, false);
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), one2, l_part, false);
+        l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, l_part2, false);
+#pragma unroll
+        for (int mv = 0; mv < MTV; ++mv) {
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16 *)(vb + kk * 16 * VROW + mv * 64));
+          const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16 *)(vb + (kk * 16 + 8) * VROW + mv * 64));
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+          o_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o_acc[mv], 0, 0, 0);
+        }
+      }
+    }
+    if (t == J) break;
+    if ((t % chunk) == 0) m_dec = kNegInf;
+
+    // ---- S^T = K_t Q^T ----
     const unsigned char *kb = sK[buf] + l32 * KROW + hi * 16;
     // K fragments are read one k-step ahead of the MFMAs that consume them, so LDS latency overlaps
     // the previous k-step's MFMAs instead of stalling every MFMA
@@ -196,12 +239,13 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk & 1][mt], qf[kk], s[mt], 0, 0, 0);
+        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk & 1][mt], qf[kk], kk == 0 ? f32x16{} : s[mt], 0, 0,
+                                                        0);
       __builtin_amdgcn_sched_barrier(0);  // keep the next k-step's reads ahead of these MFMAs
     }
 
     // ---- causal / tail mask (only blocks that need it) ----
-    const int key0 = j * BC;
+    const int key0 = t * BC;
     const bool need_mask = (key0 + BC > a.Lk) || (a.causal && key0 + BC - 1 > r0 + off);
     if (need_mask) {
       const int lim = a.causal ? min(my_row + off, a.Lk - 1) : a.Lk - 1;
@@ -230,7 +274,8 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       sVote[buf][wave] = wave_keep ? 1 : 0;
       sCrit[buf][wave] = wcrit;
     }
-    barrier_lds_only();  // vote barrier (the next block's loads stay in flight)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K_{t+1} and V_t have landed in LDS
+    __syncthreads();
     int keep = 0;
 #pragma unroll
     for (int w = 0; w < WPT; ++w) keep |= sVote[buf][tile * WPT + w];
@@ -238,57 +283,16 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     ++live_cnt;
     if (!keep) ++skip_cnt;
     if (tile_leader) {
-      if (a.mask) a.mask[mask_row + j] = keep ? kKept : kSkipped;
+      if (a.mask) a.mask[mask_row + t] = keep ? kKept : kSkipped;
       if (a.crit) {
         float c = sCrit[buf][tile * WPT];
 #pragma unroll
         for (int w = 1; w < WPT; ++w) c = fmaxf(c, sCrit[buf][tile * WPT + w]);
-        a.crit[mask_row + j] = c * a.scale;
+        a.crit[mask_row + t] = c * a.scale;
       }
     }
-
-    if (!STATS && keep) {
-      // ---- kept block: online-softmax update and O^T += V^T P^T ----
-      const float m_new = fmaxf(m_acc, mx);
-      if (__ballot(m_new > m_acc) != 0ull) {
-        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_acc - m_new) * a.scale_log2);
-        l_part *= alpha;
-        l_part2 *= alpha;
-#pragma unroll
-        for (int i = 0; i < MTV; ++i) o_acc[i] *= alpha;
-        m_acc = m_new;
-      }
-      const float base = (m_acc == kNegInf) ? 0.f : m_acc * a.scale_log2;
-      const unsigned char *vb = sV[buf] + tr_off;
-      // P^T for k-step kk (16 keys) is formed right before its MFMAs: keys of score registers
-      // s[kk/2][8*(kk%2) .. +7], i.e. key 16*kk + 8*(e/4) + 4*hi + e%4 for element e.
-#pragma unroll
-      for (int kk = 0; kk < KSV; ++kk) {
-        bf16x8 pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pf[e] = (__bf16)fast_exp2(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + e], a.scale_log2, -base));
-        // row sum: one bf16 dot2 with (1, 1) per pair of probabilities
-        const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), one2, l_part, false);
-        l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), one2, l_part2, false);
-        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), one2, l_part, false);
-        l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, l_part2, false);
-#pragma unroll
-        for (int mv = 0; mv < MTV; ++mv) {
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16 *)(vb + kk * 16 * VROW + mv * 64));
-          const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16 *)(vb + (kk * 16 + 8) * VROW + mv * 64));
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
-          o_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o_acc[mv], 0, 0, 0);
-        }
-      }
-    }
-    if (has_next) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the direct K/V loads have landed in LDS
-      __syncthreads();  // buffer-swap barrier
-    }
+    mx_pend = mx;
+    keep_pend = keep != 0;
   }
 
   // ---- diagnostics for blocks that are not live ----
