@@ -80,6 +80,21 @@ __device__ __forceinline__ void barrier_lds_only() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4: lane i writes LDS bytes
+// [lds_base + 16 i, lds_base + 16 i + 16) with lds_base taken from M0; lds_base must be the same
+// in every lane).  Written out as assembly so that the compiler does not treat it as an LDS store
+// it must wait for (s_waitcnt vmcnt(0)) before every later LDS read: kernels that use it order
+// these loads themselves, with s_waitcnt vmcnt and a barrier before a buffer is read or refilled.
+// The instruction has no register results.
+__device__ __forceinline__ void direct_load16(const void *addr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds_base) : "m0");
+}
+
+// LDS byte address of a pointer into __shared__ memory
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
 // max over lanes l and l ^ 32
 __device__ __forceinline__ float max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 

@@ -9,8 +9,9 @@
 //   * one workgroup = (sequence, row tile, split); the row tile is TR = 64 or 128 q heads, one wave
 //     per 16 heads; the tile's vote is a ballot per wave and one LDS flag per wave;
 //   * the latent block (64 tokens x 576 channels = 72 KB) goes global -> LDS directly
-//     (global_load_lds_dwordx4), double-buffered and prefetched one block ahead, with the page ids
-//     of the next block prefetched as one vector load;
+//     (global_load_lds_dwordx4, issued as assembly so the compiler does not wait for it before the
+//     current block's LDS reads), double-buffered and prefetched one block ahead, with the page
+//     ids of the next block prefetched as one vector load;
 //   * S^T = K q^T with v_mfma_f32_16x16x32_bf16: K rows from LDS (A operand), the wave's 16 q heads
 //     in registers (B operand, 72 VGPRs); each lane holds 16 scores of one head;
 //   * O^T = V^T P^T with v_mfma_f32_16x16x32_bf16: P^T comes from the score registers; the V^T
@@ -85,6 +86,10 @@ __global__ __launch_bounds__(TR / HPW * 64, 1) void decode_latent_kernel(DecodeA
   const __bf16 *qp = (const __bf16 *)a.q + ((int64_t)b * a.Hq + h) * DQK;
 #pragma unroll
   for (int kk = 0; kk < KSQ; ++kk) qf[kk] = *(const bf16x8 *)(qp + kk * 32 + grp * 8);
+  // consume the q loads here, so their waits are not placed inside the block loop (where they
+  // would also wait for the block prefetch issued after them)
+#pragma unroll
+  for (int kk = 0; kk < KSQ; ++kk) asm volatile("" ::"v"(qf[kk]));
 
   const __bf16 *kc = (const __bf16 *)a.kc;
   const int32_t *table = a.table + (int64_t)b * a.max_pages;
@@ -107,8 +112,7 @@ __global__ __launch_bounds__(TR / HPW * 64, 1) void decode_latent_kernel(DecodeA
       if (row >= BK) row = 0;
       const int pid = __shfl(tabv, row >> 4);
       if (ins < INS)
-        __builtin_amdgcn_global_load_lds((const void *)(kc + (int64_t)pid * page_stride + (row & 15) * DQK + c * 8),
-                                         (lds_void *)(sK[buf] + ins * 1024), 16, 0, 0);
+        direct_load16(kc + (int64_t)pid * page_stride + (row & 15) * DQK + c * 8, lds_addr(sK[buf] + ins * 1024));
     }
   };
   // transpose-read base for the V^T operand: source lane j = 4k + q of 16-lane group G points at
