@@ -86,8 +86,12 @@ __device__ __forceinline__ void barrier_lds_only() {
 // it must wait for (s_waitcnt vmcnt(0)) before every later LDS read: kernels that use it order
 // these loads themselves, with s_waitcnt vmcnt and a barrier before a buffer is read or refilled.
 // The instruction has no register results.
+// M0 is saved and restored around it, so the compiler's own use of M0 is not disturbed.
 __device__ __forceinline__ void direct_load16(const void *addr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds_base) : "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(addr), "s"(lds_base));
 }
 
 // LDS byte address of a pointer into __shared__ memory

@@ -5,9 +5,10 @@
 // xllm-io review, 核心公式 and 核心思想 item 4 (MHA/GQA/MQA/MLA); fugumt.com abstract).  In latent
 // attention V is the same bytes as K, so a skip saves arithmetic, not HBM traffic.
 //
-// MI355X design:
-//   * one workgroup = (sequence, row tile, split); the row tile is TR = 64 or 128 q heads, one wave
-//     per 16 heads; the tile's vote is a ballot per wave and one LDS flag per wave;
+// MI355X design (64-head tiles; the 128-head tile runs the one-wave-per-SIMD kernel of
+// decode_mla.hip, which this file's launcher dispatches to):
+//   * one workgroup = (sequence, row tile, split); the row tile is TR = 64 q heads, one wave per 16
+//     heads; the tile's vote is a ballot per wave and one LDS flag per wave;
 //   * the latent block (64 tokens x 576 channels = 72 KB) goes global -> LDS directly
 //     (global_load_lds_dwordx4, issued as assembly so the compiler does not wait for it before the
 //     current block's LDS reads), double-buffered and prefetched one block ahead, with the page
@@ -297,10 +298,15 @@ static void launch_tr(const DecodeArgs &a, int grid, hipStream_t st) {
     hipLaunchKernelGGL((decode_latent_kernel<TR, false, false>), dim3(grid), dim3(NT), 0, st, a);
 }
 
+hipError_t launch_decode_mla128(const DecodeArgs &a, hipStream_t st);
+
 hipError_t launch_decode_latent(const DecodeArgs &a, hipStream_t st) {
   if (a.Hq != 128 || a.Hkv != 1 || a.page != PAGE || a.block_k != BK) return hipErrorNotSupported;
   if (a.tile_rows == 128) {
-    launch_tr<128>(a, a.B * a.num_splits, st);
+    // all 128 heads in one tile: the one-wave-per-SIMD kernel (decode_mla.hip)
+    const hipError_t e = launch_decode_mla128(a, st);
+    if (e != hipSuccess || a.num_splits == 1 || a.stats_only) return e;
+    return launch_decode_combine(a, DV, st);
   } else if (a.tile_rows == 64) {
     // two row tiles per (sequence, split): round the (sequence, split) count up to a multiple of 8
     const int pairs = (a.B * a.num_splits + 7) / 8 * 8;

@@ -1,0 +1,365 @@
+// BLASST decode over a paged latent cache, all 128 heads of a sequence in one workgroup
+// (MLA-shaped: 576-dim scores, V = the first 512 latent dims).
+//
+// Method: each 64-token block's row maxima are compared with the running maxima of the tile, and a
+// block that every row votes to skip gets no exp and no P.V product (pages: xllm-io review,
+// 核心公式 and 核心思想 item 4 (MHA/GQA/MQA/MLA); fugumt.com abstract).  In latent attention V is
+// the same bytes as K, so a skip saves arithmetic, not HBM traffic.
+//
+// MI355X design (the one-wave-per-SIMD layout; decode_latent.hip keeps the 16-heads-per-wave one
+// for 64-head tiles):
+//   * one workgroup = (sequence, split), 4 waves, one per SIMD, each with the full 512-register
+//     file; wave w owns heads 32 w .. 32 w + 31, so every operand fragment read from LDS feeds a
+//     32-wide MFMA (v_mfma_f32_32x32x16_bf16): 32 flops per LDS byte, twice what 16 heads per wave
+//     give, which is what bounds the latent decode on this chip (LDS, not MFMA or HBM);
+//   * S^T = K q^T: K rows (A operand) from LDS, the wave's 32 heads of q in 144 VGPRs (B operand);
+//     each lane holds the 32 scores of one head for its half of the keys, so the block row max is
+//     an in-lane max and one exchange with lane l ^ 32;
+//   * O^T = V^T P^T: P^T straight from the score registers (B operand), V^T read from the same LDS
+//     tile with ds_read_b64_tr_b16; O^T of 32 heads x 512 channels is 256 accumulators, held in the
+//     AGPRs: the P.V MFMAs are written out with AGPR accumulators (the scores, consumed by VALU code,
+//     stay in VGPRs; this file is built with the MFMA VGPR form for the score MFMAs);
+//   * the accumulators are never rescaled inside the loop: probabilities are taken relative to a
+//     per-head reference max fixed by the first kept block; a block max more than 2^64 (in
+//     probability) above it makes the workgroup redo its blocks with the reference raised (see the
+//     comment at the pass loop);
+//   * wave w loads page w of each block (one uniform page base per wave, loop-invariant per-lane
+//     offsets: the loads need no address arithmetic), global -> LDS directly, double-buffered and
+//     issued one block ahead; rows are 1168 bytes apart (576 channels + 16 bytes), which keeps both
+//     the 32-row score-operand reads and the transpose reads free of bank conflicts.
+#include "common.hpp"
+
+namespace blasst {
+
+namespace {
+constexpr int DQK = 576, DV = 512, PAGE = 16, BK = 64, HPW = 32, NW = 4, NT = NW * 64;
+constexpr int CH = DQK / 8;              // 16-byte chunks per latent row (72)
+constexpr int ROW = (CH + 1) * 16;       // LDS row stride with one pad chunk (1168 bytes)
+constexpr int PGB = PAGE * ROW;          // LDS bytes per page (18688)
+constexpr int BUF = BK * ROW;            // LDS bytes per block (74752)
+constexpr int NLD = (PGB + 1023) / 1024; // direct loads per page (19; the last one 256 bytes)
+constexpr int KS = DQK / 16;             // k-steps of S^T (36)
+constexpr int MT = BK / 32;              // key m-tiles of S^T (2)
+constexpr int MTV = DV / 32;             // dv m-tiles of O^T (16)
+constexpr int KSV = BK / 16;             // k-steps of O^T (4)
+constexpr float kRefWindowLog2 = 64.f;
+typedef __attribute__((ext_vector_type(4))) short v4i16;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+}  // namespace
+
+// global_load_lds_dwordx4 with a wave-uniform 64-bit base and a per-lane 32-bit offset
+// (M0 is saved and restored around it, so the compiler's use of M0 is not disturbed)
+__device__ __forceinline__ void direct_load16_saddr(const void *sbase, uint32_t voffset, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voffset), "s"(sbase), "s"(lds_base));
+}
+
+template <bool OUT_F32, bool STATS>
+__global__ __launch_bounds__(NT, 1) void decode_mla_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char sK[2][BUF];
+  __shared__ int sVote[2][NW];
+  __shared__ float sCrit[2][NW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int split = blockIdx.x % a.num_splits;
+  const int b = blockIdx.x / a.num_splits;
+  const int cap = a.max_pages * PAGE;
+  const int L = min(a.seq_lens[b], cap);
+  const int J = (L + BK - 1) / BK;
+  const int chunk = (J + a.num_splits - 1) / a.num_splits;
+  const int j0 = split * chunk;
+  const int j1 = min(J, j0 + chunk);
+  const int npg = (L + PAGE - 1) / PAGE;
+  const int h = wave * HPW + l32;  // head of this lane's score / output column
+
+  float thr = a.thr_raw;
+  if (a.thr_mode == 1) {
+    const float lam = fminf(1.f, a.a / (float)L);
+    thr = lam > 0.f ? __logf(lam) / a.scale : kNegInf;
+  }
+
+  // q fragments (B operand of S^T = K q^T): lane holds dims 16 kk + 8 hi .. +7 of head h
+  bf16x8 qf[KS];
+  const __bf16 *qp = (const __bf16 *)a.q + ((int64_t)b * a.Hq + h) * DQK;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) qf[kk] = *(const bf16x8 *)(qp + kk * 16 + hi * 8);
+  // consume the q loads here, so their waits are not placed inside the block loop
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) asm volatile("" ::"v"(qf[kk]));
+
+  // per-lane source offsets of the page loads: load k of a page writes LDS bytes
+  // [1024 k + 16 lane, +16) of the page region, i.e. padded row r = o / ROW, chunk c = (o % ROW) / 16
+  // (the pad chunk re-reads chunk 0), from byte r * 1152 + 16 c of the page; two 16-bit offsets per
+  // VGPR
+  uint32_t offp[(NLD + 1) / 2];
+#pragma unroll
+  for (int k = 0; k < (NLD + 1) / 2; ++k) offp[k] = 0;
+#pragma unroll
+  for (int k = 0; k < NLD; ++k) {
+    const int o = min(1024 * k + 16 * lane, PGB - 16);
+    const int r = o / ROW;
+    int c = (o - r * ROW) / 16;
+    if (c >= CH) c = 0;
+    offp[k >> 1] |= (uint32_t)(r * DQK * 2 + c * 16) << (16 * (k & 1));
+  }
+  const char *kc = (const char *)a.kc;
+  const int32_t *table = a.table + (int64_t)b * a.max_pages;
+  constexpr int64_t kPageBytes = (int64_t)PAGE * DQK * 2;  // one kv head
+  auto load_block = [&](int j, int buf) {
+    const int pid = __builtin_amdgcn_readfirstlane(table[min(j * (BK / PAGE) + wave, npg - 1)]);
+    const char *base = kc + (int64_t)pid * kPageBytes;  // wave-uniform
+    const uint32_t lbase = lds_addr(sK[buf] + wave * PGB);
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      const uint32_t off = (offp[k >> 1] >> (16 * (k & 1))) & 0xffffu;
+      if (k + 1 < NLD || 1024 * k + 16 * lane < PGB) direct_load16_saddr(base, off, lbase + 1024 * k);
+    }
+  };
+  // transpose-read base for the V^T operand (the layout of prefill_bf16.hip with BC = 64)
+  const int tr_g = lane >> 4, tr_j = lane & 15;
+  const int tr_off = ((tr_g >> 1) * 4 + (tr_j >> 2)) * ROW + (16 * (tr_g & 1) + 4 * (tr_j & 3)) * 2;
+
+  float m_ref = kNegInf;  // reference max of the accumulation (see the pass loop)
+  float m_seen, m_dec, l_part, l_part2;
+  f32x16 o_acc[MTV];
+  unsigned live_cnt, skip_cnt;
+  const int mask_row = b * a.nkb;  // one kv head, one row tile
+
+  // Pass loop: one pass over the split's blocks.  The accumulation takes probabilities relative to
+  // the reference m_ref, set by the first kept block with a finite max; while every block max
+  // stays within 2^64 (in probability) of it this is the usual online softmax (O / l does not depend
+  // on the reference; bf16 P and the fp32 sums keep their relative precision, and with at most 2^64
+  // per probability the sums stay far inside the fp32 range) and no accumulator is rescaled.  A
+  // block max beyond that window (a logit more than 44 above the first kept block's maximum) makes
+  // the whole workgroup restart the pass with the reference raised to the largest max seen.  (A
+  // 2^16 window was measured to trigger restarts on ordinary score distributions: a later block
+  // can easily be 11 logits above the first block of a split.)
+  for (;;) {
+    // orders the zeroing below after the previous pass's last P.V MFMA (XDL write -> VALU write)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    m_seen = kNegInf;
+    m_dec = kNegInf;
+    l_part = 0.f;
+    l_part2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < MTV; ++i) o_acc[i] = f32x16{};
+    live_cnt = 0;
+    skip_cnt = 0;
+    bool redo = false;
+
+    if (j0 < j1) {
+      load_block(j0, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    for (int j = j0; j < j1; ++j) {
+      const int buf = (j - j0) & 1;
+      const bool has_next = j + 1 < j1;
+      if (has_next) load_block(j + 1, buf ^ 1);
+      const int key0 = j * BK;
+      if (key0 + BK > L) {
+        // slots past the sequence end hold arbitrary bytes: zero them so that P = 0 meets V = 0
+        // (0 * NaN cannot appear); their scores are masked below
+        for (int o16 = (L - key0) * ROW + tid * 16; o16 < BUF; o16 += NT * 16) *(u32x4 *)(sK[buf] + o16) = u32x4{};
+        __syncthreads();
+      }
+
+      // ---- S^T = K_j q^T (keys 32 mt + 8 (r / 4) + 4 hi + r % 4 of register r) ----
+      f32x16 s[MT];
+      const unsigned char *kb = sK[buf] + l32 * ROW + hi * 16;
+      bf16x8 kf[2][MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) kf[0][mt] = *(const bf16x8 *)(kb + mt * 32 * ROW);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        if (kk + 1 < KS) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) kf[(kk + 1) & 1][mt] = *(const bf16x8 *)(kb + mt * 32 * ROW + (kk + 1) * 32);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk & 1][mt], qf[kk], kk == 0 ? f32x16{} : s[mt], 0, 0, 0);
+        if ((kk & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+      }
+      if (key0 + BK > L) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (key0 + mt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) >= L) s[mt][r] = kNegInf;
+      }
+
+      // ---- block row max, vote, critical value ----
+      float mx = kNegInf;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+      mx = max_xor32(mx);
+      const bool skip_row = row_votes_skip(mx, m_dec, thr);
+      const bool wave_keep = __ballot(!skip_row) != 0ull;
+      const bool over = m_ref != kNegInf && (mx - m_ref) * a.scale_log2 > kRefWindowLog2;
+      const bool wave_over = __ballot(over) != 0ull;
+      m_seen = fmaxf(m_seen, mx);
+      float wcrit = 0.f;
+      if (a.crit) wcrit = max_lanes32(row_crit(mx, m_dec));
+      if (lane == 0) {
+        sVote[buf][wave] = (wave_keep ? 1 : 0) | (wave_over ? 2 : 0);
+        sCrit[buf][wave] = wcrit;
+      }
+      barrier_lds_only();  // vote barrier (the next block's loads stay in flight)
+      int votes = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) votes |= sVote[buf][w];
+      if (votes & 2) {  // uniform over the workgroup
+        redo = true;
+        break;
+      }
+      const bool keep = (votes & 1) != 0;
+      m_dec = fmaxf(m_dec, mx);
+      ++live_cnt;
+      if (!keep) ++skip_cnt;
+      if (tid == 0) {
+        if (a.mask) a.mask[mask_row + j] = keep ? kKept : kSkipped;
+        if (a.crit) {
+          float c = sCrit[buf][0];
+#pragma unroll
+          for (int w = 1; w < NW; ++w) c = fmaxf(c, sCrit[buf][w]);
+          a.crit[mask_row + j] = c * a.scale;
+        }
+      }
+
+      if (!STATS && keep) {
+        // ---- kept block: O^T += V^T P^T with probabilities relative to the reference ----
+        if (m_ref == kNegInf) m_ref = mx;  // first kept block of this head: O and l are still zero
+        const float base = (m_ref == kNegInf) ? 0.f : m_ref * a.scale_log2;
+        const unsigned char *vb = sK[buf] + tr_off;
+        const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+        for (int kk = 0; kk < KSV; ++kk) {
+          bf16x8 pf;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pf[e] = (__bf16)fast_exp2(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + e], a.scale_log2, -base));
+          l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), one2, l_part, false);
+          l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), one2, l_part2, false);
+          l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), one2, l_part, false);
+          l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, l_part2, false);
+          // V^T fragments are read PF m-tiles ahead into a ring of PF + 1 slots (with one wave per
+          // SIMD nothing else hides the LDS latency; the written-out MFMAs keep their order, so the
+          // reads are placed ahead of them in program order)
+          constexpr int PF = 7;
+          bf16x8 vring[PF + 1];
+          auto read_v = [&](int mv) {
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + kk * 16 * ROW + mv * 64));
+            const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + (kk * 16 + 8) * ROW + mv * 64));
+            vring[mv % (PF + 1)] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+          };
+#pragma unroll
+          for (int mv = 0; mv < PF; ++mv) read_v(mv);
+#pragma unroll
+          for (int mv = 0; mv < MTV; ++mv) {
+            if (mv + PF < MTV) read_v(mv + PF);
+            // s_nop 3: wait states after the VALU writes of the operands (the compiler does not
+            // track hazards of inline assembly)
+            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                         : "+a"(o_acc[mv])
+                         : "v"(vring[mv % (PF + 1)]), "v"(pf));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (has_next) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // buffer-swap barrier
+      }
+    }
+    if (!redo) break;
+    // drain the prefetch of the aborted pass, then start over with the reference raised
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    m_ref = fmaxf(m_ref, m_seen);
+  }
+
+  if (tid == 0 && a.counters) {
+    atomicAdd(&a.counters[0], (unsigned long long)live_cnt);
+    atomicAdd(&a.counters[1], (unsigned long long)skip_cnt);
+  }
+  if ((a.mask || a.crit) && split == 0)
+    for (int j = J + tid; j < a.nkb; j += NT) {
+      if (a.mask) a.mask[mask_row + j] = kNotLive;
+      if (a.crit) a.crit[mask_row + j] = __builtin_nanf("");
+    }
+  if (STATS) return;
+
+  // XDL write -> VALU read of the accumulators: wait states after the last P.V MFMA (which the
+  // compiler does not know about) before the epilogue reads them
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(o_acc[0]), "+a"(o_acc[1]), "+a"(o_acc[2]), "+a"(o_acc[3]), "+a"(o_acc[4]), "+a"(o_acc[5]),
+                 "+a"(o_acc[6]), "+a"(o_acc[7]), "+a"(o_acc[8]), "+a"(o_acc[9]), "+a"(o_acc[10]), "+a"(o_acc[11]),
+                 "+a"(o_acc[12]), "+a"(o_acc[13]), "+a"(o_acc[14]), "+a"(o_acc[15]));
+
+  // ---- epilogue: O^T lane layout: head h, channels 32 mv + 8 (r / 4) + 4 hi + r % 4 ----
+  const float lp = l_part + l_part2;
+  const float l_tot = lp + __shfl_xor(lp, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse = l_tot > 0.f ? m_ref * a.scale + __logf(l_tot) : kNegInf;
+  if (a.num_splits == 1) {
+    const int64_t ob = ((int64_t)b * a.Hq + h) * DV + 4 * hi;
+#pragma unroll
+    for (int mv = 0; mv < MTV; ++mv)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int64_t oi = ob + 32 * mv + 8 * rg;
+        if (OUT_F32) {
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = o_acc[mv][4 * rg + e] * inv;
+          *(f32x4 *)((float *)a.o + oi) = v4;
+        } else {
+          u32x2 w;
+          w[0] = pack_bf16x2(o_acc[mv][4 * rg + 0] * inv, o_acc[mv][4 * rg + 1] * inv);
+          w[1] = pack_bf16x2(o_acc[mv][4 * rg + 2] * inv, o_acc[mv][4 * rg + 3] * inv);
+          *(u32x2 *)((__bf16 *)a.o + oi) = w;
+        }
+      }
+    if (a.lse && hi == 0) a.lse[(int64_t)b * a.Hq + h] = lse;
+  } else {
+    const int64_t pb = ((int64_t)b * a.Hq + h) * a.num_splits + split;
+    float *wo = a.ws_o + pb * DV + 4 * hi;
+#pragma unroll
+    for (int mv = 0; mv < MTV; ++mv)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = o_acc[mv][4 * rg + e] * inv;
+        *(f32x4 *)(wo + 32 * mv + 8 * rg) = v4;
+      }
+    if (hi == 0) a.ws_lse[pb] = lse;
+  }
+}
+
+// 128 q heads on one latent head, 576/512 dims, page 16, block 64, all heads in one tile.
+hipError_t launch_decode_mla128(const DecodeArgs &a, hipStream_t st) {
+  if (a.Hq != 128 || a.Hkv != 1 || a.page != PAGE || a.block_k != BK || a.tile_rows != 128)
+    return hipErrorNotSupported;
+  const int grid = a.B * a.num_splits;
+  if (a.stats_only)
+    hipLaunchKernelGGL((decode_mla_kernel<false, true>), dim3(grid), dim3(NT), 0, st, a);
+  else if (a.out_f32)
+    hipLaunchKernelGGL((decode_mla_kernel<true, false>), dim3(grid), dim3(NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_mla_kernel<false, false>), dim3(grid), dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace blasst
