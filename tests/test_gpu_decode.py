@@ -188,3 +188,24 @@ def test_latent_mla_full_size_sampled():
     rep = _compare(d, res, splits=16, a=a, tiles=[(0, 0, 0), (37, 0, 0), (63, 0, 0)], tile_rows=128,
                    out_bf16=True)
     print(f"sparsity {float((mh == 1).sum()) / live.sum():.3f}; {rep}")
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_latent_mla_late_large_logit_redo(splits):
+    """A key far above everything before it in its split (scaled logit +60 against a first-block
+    maximum near +10): the 128-head latent kernel must raise its reference max and redo the split
+    (its accumulation reference is fixed by the first kept block); the result still matches the
+    oracle."""
+    m = _lib()
+    lens = [1000, 300]
+    d = synth.decode_inputs(batch=2, hq=128, hkv=1, ctx=None, d=576, dv=512, seq_lens=lens, seed=11,
+                            device="cuda", latent=True)
+    scale = 1.0 / math.sqrt(576)
+    for b, key in ((0, 700), (1, 290)):
+        pid = int(d.block_table[b, key // d.page_size])
+        # channel 574 is the sink channel: q = 1 there, so this key's logit is 60 after scaling
+        d.k_cache[pid, 0, key % d.page_size, 574] = 60.0 / scale
+    res = _run(m, d, splits=splits, a=0.0, tile_rows=128)
+    rep = _compare(d, res, splits=splits, a=0.0, tile_rows=128)
+    print(f"S={splits}: {rep}")
+    assert rep.skipped == 0
