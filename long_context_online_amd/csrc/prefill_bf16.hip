@@ -184,9 +184,15 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
 
     if (!STATS && keep_pend) {
       // ---- kept block t - 1: online-softmax update and O^T += V^T P^T ----
-      const float m_new = fmaxf(m_acc, mx_pend);
-      if (__ballot(m_new > m_acc) != 0ull) {
-        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_acc - m_new) * a.scale_log2);
+      // Lazy rescaling: the accumulation reference m_acc is raised only when a row's block max
+      // exceeds it by more than 2^8 in probability (a row's first finite max just sets it: O and l
+      // are still zero); below that, probabilities relative to the stale reference are at most 256,
+      // which bf16 P and the fp32 sums hold with the same relative precision, and O / l and the
+      // LSE are unchanged.  So the accumulators are rescaled only when the max jumps.
+      if (m_acc == kNegInf) m_acc = mx_pend;
+      if (__ballot((mx_pend - m_acc) * a.scale_log2 > 8.f) != 0ull) {
+        const float m_new = fmaxf(m_acc, mx_pend);
+        const float alpha = fast_exp2((m_acc - m_new) * a.scale_log2);
         l_part *= alpha;
         l_part2 *= alpha;
 #pragma unroll
