@@ -175,6 +175,20 @@ class Prefill:
         self.m.blasst_prefill(self.inp.q, self.inp.k, self.inp.v, self.o, causal=True, block_q=P_BLK,
                               block_k=P_BLK, lam=lam, lse=self.lse, **diag)
 
+    def run_no_decision(self):
+        self.m.blasst_prefill(self.inp.q, self.inp.k, self.inp.v, self.o, causal=True, block_q=P_BLK,
+                              block_k=P_BLK, no_decision=True, lse=self.lse)
+
+    def decision_overhead(self, steps):
+        """The same dense work with and without the decision logic: lambda = 0 (votes taken, every
+        block kept) against threshold mode NONE (the kernel variant without votes)."""
+        t0 = timed(self.torch, lambda: self.run(0.0), steps)
+        t1 = timed(self.torch, self.run_no_decision, steps)
+        t0 = min(t0, timed(self.torch, lambda: self.run(0.0), steps))
+        t1 = min(t1, timed(self.torch, self.run_no_decision, steps))
+        return {"lambda0_ms": round(t0, 4), "no_decision_ms": round(t1, 4),
+                "no_decision_over_lambda0_throughput": round(t1 / t0, 4)}
+
     def stats(self):
         """Stats pass (QK^T, block maxima and decisions only): critical values of every tile."""
         torch = self.torch
@@ -350,6 +364,13 @@ def calibration_sweep(m, torch, synth, steps):
                         "s in {0.3, 0.5, 0.7}; 8-tile (1024-row) sample per L"}
 
 
+def percentiles(xs):
+    """p10 / p50 / p90 of per-launch times (ms) from the timed steps (nearest rank)."""
+    ys = sorted(xs)
+    pick = lambda q: ys[min(len(ys) - 1, max(0, int(math.ceil(q * len(ys))) - 1))]
+    return [round(pick(0.1), 4), round(pick(0.5), 4), round(pick(0.9), 4)]
+
+
 def practical_ceilings(torch):
     """Measured ceilings on this GPU, as context for the roofline fractions: a bf16 GEMM through the
     vendor BLAS (torch.matmul, 8192^3) and a plain device-to-device copy of 4 GiB."""
@@ -423,8 +444,10 @@ def main():
         ev.append(e)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    dec_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    pre_all = [e[0].elapsed_time(e[1]) for e in ev]
+    dec_all = [e[1].elapsed_time(e[2]) for e in ev]
+    pre_ms = sum(pre_all) / args.steps
+    dec_ms = sum(dec_all) / args.steps
     if args.profile_only:
         for _ in range(args.steps):
             ref_dst.copy_(ref_src)
@@ -453,6 +476,7 @@ def main():
         r.update({"ms": round(pre_ms, 4), "speedup_vs_dense": round(r["dense_ms"] / pre_ms, 3),
                   "dense_equiv_tflops": round(tflops, 2), "target_sparsity": P_TARGET,
                   "live_tile_blocks": live, "frac_of_bf16_peak_dense_equiv": round(tflops / PEAK_BF16_TFLOPS, 4)})
+        r["timed_step_ms_p10_p50_p90"] = percentiles(pre_all)
         result["prefill"] = r
         result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -469,11 +493,13 @@ def main():
             lam50 = pre.calibrate(0.5)
             result["prefill_s050"] = pre.measure(lam50, max(3, args.steps // 2))
             result["prefill_s050"]["target_sparsity"] = 0.5
+            result["prefill_decision_overhead"] = pre.decision_overhead(max(3, args.steps // 2))
     if dec:
         r = dec.measure(lam_d, args.steps, ms=dec_ms)
         r.update({"target_sparsity": D_TARGET, "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
                   "workload": "paged GQA decode: batch 32, 32 q / 8 kv heads, d 128, context 32768, 16-token "
                               "pages, 64-token blocks, 16 splits, bf16"})
+        r["timed_step_ms_p10_p50_p90"] = percentiles(dec_all)
         result["decode"] = r
         result["roofline_decode"] = {"bound": "hbm", "achieved": r["hbm_gbps"], "peak": PEAK_HBM_GBPS,
                                      "unit": "GB/s", "frac": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),

@@ -56,7 +56,12 @@ typedef enum { BLASST_BF16 = 0, BLASST_FP32 = 1 } blasst_dtype;
 
 typedef enum {
   BLASST_THR_LAMBDA = 0,   /* use `lambda` directly, must be in [0, 1] */
-  BLASST_THR_A_OVER_L = 1  /* lambda = min(1, a / L), L = seqlen_k (prefill) or seq_lens[b] (decode) */
+  BLASST_THR_A_OVER_L = 1, /* lambda = min(1, a / L), L = seqlen_k (prefill) or seq_lens[b] (decode) */
+  BLASST_THR_NONE = 2      /* no threshold: every live block is kept (the result of lambda = 0), and
+                              the bf16 prefill kernel for head dim 128, 128 x 128 blocks and an even
+                              GQA group runs without any decision logic (no vote); used to measure the
+                              cost of the decisions.  skip_mask and crit must be NULL and stats_only 0.
+                              Other kernels treat it as lambda = 0. */
 } blasst_threshold_mode;
 
 typedef struct {

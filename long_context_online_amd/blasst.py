@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libblasst.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
 BF16, FP32 = 0, 1
-THR_LAMBDA, THR_A_OVER_L = 0, 1
+THR_LAMBDA, THR_A_OVER_L, THR_NONE = 0, 1, 2
 KEPT, SKIPPED, NOT_LIVE = 0, 1, 2
 
 EXPORTED = [
@@ -135,7 +135,11 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _threshold(lam, a):
+def _threshold(lam, a, no_decision=False):
+    if no_decision:
+        if lam is not None or a is not None:
+            raise ValueError("no_decision takes neither lam nor a")
+        return Threshold(THR_NONE, 0, 0.0, 0.0)
     if (lam is None) == (a is None):
         raise ValueError("give exactly one of lam and a")
     if lam is not None:
@@ -159,7 +163,7 @@ def _strides3(t):
 
 def prefill_params(q, k, v, o, *, causal, block_q, block_k, num_splits=1, lam=None, a=None,
                    softmax_scale=0.0, lse=None, skip_mask=None, crit=None, counters=None,
-                   stats_only=False, out_dtype=None):
+                   stats_only=False, out_dtype=None, no_decision=False):
     """Fills the C params struct for blasst_prefill from tensors (no call)."""
     p = PrefillParams()
     p.struct_size = ctypes.sizeof(PrefillParams)
@@ -168,7 +172,7 @@ def prefill_params(q, k, v, o, *, causal, block_q, block_k, num_splits=1, lam=No
     p.lse, p.skip_mask, p.crit, p.counters = _ptr(lse), _ptr(skip_mask), _ptr(crit), _ptr(counters)
     p.q_stride, p.k_stride, p.v_stride = _strides3(q), _strides3(k), _strides3(v)
     p.o_stride = _strides3(o) if o is not None else (ctypes.c_int64 * 3)(0, 0, 0)
-    p.thr = _threshold(lam, a)
+    p.thr = _threshold(lam, a, no_decision)
     p.in_dtype = _dtype_code(q)
     p.out_dtype = _dtype_code(o) if o is not None else (p.in_dtype if out_dtype is None else out_dtype)
     p.batch, p.num_q_heads, p.seqlen_q, p.head_dim_qk = q.shape

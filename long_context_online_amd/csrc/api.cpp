@@ -44,6 +44,10 @@ bool resolve_threshold(const blasst_threshold &t, double L, double *ln_lam, cons
     *ln_lam = t.lambda == 0.0 ? -INFINITY : std::log(t.lambda);
     return true;
   }
+  if (t.mode == BLASST_THR_NONE) {
+    *ln_lam = -INFINITY;
+    return true;
+  }
   if (t.mode == BLASST_THR_A_OVER_L) {
     if (!(t.a >= 0.0) || !std::isfinite(t.a)) { *why = "a must be finite and >= 0"; return false; }
     if (L <= 0) { *why = "L must be > 0"; return false; }
@@ -105,6 +109,9 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *stream) {
   double ln_lam;
   const char *why = "";
   if (!resolve_threshold(p->thr, p->seqlen_k, &ln_lam, &why)) return fail(BLASST_ERR_INVALID_ARG, "%s", why);
+  const bool no_decision = p->thr.mode == BLASST_THR_NONE;
+  if (no_decision && (p->skip_mask || p->crit || p->stats_only))
+    return fail(BLASST_ERR_INVALID_ARG, "threshold mode NONE takes no skip_mask, crit or stats_only");
 
   // ---- kernel coverage ----
   const int D = p->head_dim_qk;
@@ -140,6 +147,7 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *stream) {
   a.scale = (float)scale;
   a.scale_log2 = (float)(scale * 1.4426950408889634);
   a.thr_raw = thr_raw_from(ln_lam, scale);
+  a.decide = no_decision ? 0 : 1;
   if ((double)a.B * a.Hq * a.nqt > 2147483647.0 || (double)a.B * a.Hq * a.nqt * a.nkb > 2147483647.0)
     return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
 

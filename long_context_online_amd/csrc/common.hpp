@@ -36,6 +36,7 @@ struct PrefillArgs {
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e): exp(scale*(s - m)) = exp2(scale_log2*(s - m))
   float thr_raw;     // ln(lambda) / scale: skip iff (m~ - m) < thr_raw on raw logits
+  int decide;        // 0: no threshold at all (every live block kept, no vote)
 };
 
 // Arguments of the paged decode kernels.

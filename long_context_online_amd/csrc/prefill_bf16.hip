@@ -43,7 +43,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((ext_vector_type(4))) short v4i16;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-template <int D, int BC, int TPW, bool OUT_F32, bool STATS>
+// DEC = false: no threshold at all (every live block kept, no vote); used to measure what the
+// decisions cost.
+template <int D, int BC, int TPW, bool OUT_F32, bool STATS, bool DEC = true>
 __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int WPT = BC / 32;       // waves per tile (32 rows each)
   constexpr int BR = BC;             // rows per tile
@@ -272,23 +274,28 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
     mx = max_xor32(mx);
     if (!row_ok) mx = kNegInf;
-    const bool skip_row = row_votes_skip(mx, m_dec, a.thr_raw);
-    const bool wave_keep = __ballot(!skip_row) != 0ull;
-    float wcrit = 0.f;
-    if (a.crit) wcrit = max_lanes32(row_crit(mx, m_dec));
-    if (lane == 0) {
-      sVote[buf][wave] = wave_keep ? 1 : 0;
-      sCrit[buf][wave] = wcrit;
+    if (DEC) {
+      const bool skip_row = row_votes_skip(mx, m_dec, a.thr_raw);
+      const bool wave_keep = __ballot(!skip_row) != 0ull;
+      float wcrit = 0.f;
+      if (a.crit) wcrit = max_lanes32(row_crit(mx, m_dec));
+      if (lane == 0) {
+        sVote[buf][wave] = wave_keep ? 1 : 0;
+        sCrit[buf][wave] = wcrit;
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K_{t+1} and V_t have landed in LDS
     __syncthreads();
-    int keep = 0;
+    int keep = 1;
+    if (DEC) {
+      keep = 0;
 #pragma unroll
-    for (int w = 0; w < WPT; ++w) keep |= sVote[buf][tile * WPT + w];
+      for (int w = 0; w < WPT; ++w) keep |= sVote[buf][tile * WPT + w];
+    }
     m_dec = fmaxf(m_dec, mx);
     ++live_cnt;
     if (!keep) ++skip_cnt;
-    if (tile_leader) {
+    if (DEC && tile_leader) {
       if (a.mask) a.mask[mask_row + t] = keep ? kKept : kSkipped;
       if (a.crit) {
         float c = sCrit[buf][tile * WPT];
@@ -363,6 +370,18 @@ static hipError_t launch_tpw(const PrefillArgs &a, bool out_f32, hipStream_t st)
 
 template <int D, int BC>
 static hipError_t launch_one(const PrefillArgs &a, bool out_f32, hipStream_t st) {
+  if constexpr (D == 128 && BC == 128) {
+    // no threshold: the variant without decision logic (other shapes run with lambda = 0)
+    if (!a.decide && a.G % 2 == 0 && !a.stats_only) {
+      constexpr int NT = 64 * (BC / 32) * 2;
+      const int grid = a.B * (a.Hq / 2) * a.nqt;
+      if (out_f32)
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, 2, true, false, false>), dim3(grid), dim3(NT), 0, st, a);
+      else
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, 2, false, false, false>), dim3(grid), dim3(NT), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   // two q heads of one GQA group share each staged K/V block when the group has an even size
   if (a.G % 2 == 0) return launch_tpw<D, BC, 2>(a, out_f32, st);
   return launch_tpw<D, BC, 1>(a, out_f32, st);

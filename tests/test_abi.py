@@ -75,6 +75,8 @@ PREFILL_BAD = [
     ({"thr": (0, 0, 1.5, 0.0)}, 1), ({"thr": (0, 0, -0.1, 0.0)}, 1), ({"thr": (1, 0, 0.0, -2.0)}, 1),
     ({"thr": (5, 0, 0.0, 0.0)}, 1), ({"thr": (0, 1, 0.5, 0.0)}, 1), ({"struct_size": 8}, 1),
     ({"softmax_scale": float("nan")}, 1),
+    ({"thr": (2, 0, 0.0, 0.0), "skip_mask": FAKE}, 1), ({"thr": (2, 0, 0.0, 0.0), "crit": FAKE}, 1),
+    ({"thr": (2, 0, 0.0, 0.0), "stats_only": 1}, 1),
     ({"head_dim_qk": 96, "head_dim_v": 96}, 2), ({"block_q": 64}, 2), ({"block_q": 32, "block_k": 32}, 2),
     ({"q": FAKE + 2}, 2), ({"in_dtype": 1, "out_dtype": 0}, 2), ({"in_dtype": 1, "out_dtype": 1}, 2),
 ]

@@ -161,3 +161,27 @@ def test_llama8b_gqa_32k_sampled_tiles():
     rep = _compare_all(inp.q, inp.k, inp.v, res, causal=True, bq=128, bk=128, splits=1, ln_lam=ln_lam,
                        tiles=tiles)
     print(f"sparsity {float((mh == 1).sum()) / live.sum():.3f}; {rep}")
+
+
+def test_no_decision_mode_equals_lambda_zero():
+    """Threshold mode NONE (the variant without any decision logic, for measuring what the decisions
+    cost) gives the same bits as lambda = 0 and the oracle's dense attention."""
+    import long_context_online_amd as m
+    m.lib()
+    inp = synth.prefill_inputs(batch=1, hq=4, hkv=2, L=640, d=128, block_k=128, window=True, seed=77,
+                               device="cuda")
+    outs = []
+    for kw in ({"lam": 0.0}, {"no_decision": True}):
+        o = torch.empty(1, 4, 640, 128, dtype=torch.float32, device="cuda")
+        lse = torch.empty(1, 4, 640, dtype=torch.float32, device="cuda")
+        cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+        m.blasst_prefill(inp.q, inp.k, inp.v, o, causal=True, block_q=128, block_k=128, lse=lse, counters=cnt, **kw)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu(), cnt.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert int(outs[1][2][1]) == 0 and int(outs[1][2][0]) == int(outs[0][2][0])
+    q, k, v = host64(inp.q), host64(inp.k), host64(inp.v)
+    from oracle.blasst_oracle import causal_visible
+    ref = oracle.softmax_attention(q[0, 1], k[0, 0], v[0, 0], causal_visible(np.arange(640), 640, 640, 640),
+                                  1 / math.sqrt(128))
+    assert np.max(np.abs(outs[1][0][0, 1].double().numpy() - ref[0])) < 1e-2
