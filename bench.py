@@ -41,6 +41,10 @@ D_TARGET = 0.73
 CALIB_TILES = 8  # prefill calibration sample: 8 query tiles of 128 rows (1024 rows)
 # latent (MLA-shaped) decode
 M_B, M_HQ, M_D, M_DV, M_CTX, M_TARGETS = 64, 128, 576, 512, 32768, (0.5, 0.73)
+DEC_KERNEL = {False: "decode_gqa_kernel<false>", True: "decode_mla_kernel<false, false>"}
+MLA_WORKLOAD = ("latent decode, DeepSeek-shaped: batch 64, 128 q heads on one latent head, 576-dim scores, "
+                "V = first 512 channels, context 32768, 16-token pages, 64-token blocks, 16 splits, 128-head "
+                "tiles, bf16")
 # calibration sweep
 C_L_VALUES = (4096, 8192, 16384, 32768, 65536, 131072)
 C_S_VALUES = (0.3, 0.5, 0.7)
@@ -68,7 +72,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "mla"], default="all",
                     help="restrict the timed step (for profiling runs)")
     ap.add_argument("--quick", action="store_true",
                     help="only the timed step (no 128K decode, latent decode or calibration sweep)")
@@ -411,11 +415,14 @@ def main():
     m.lib()
     torch.cuda.init()
     pre = Prefill(m, torch, synth) if args.only in ("all", "prefill") else None
-    dec = Decode(m, torch, synth) if args.only in ("all", "decode") else None
+    if args.only == "mla":  # the latent decode as the timed step (profiling runs)
+        dec = Decode(m, torch, synth, ctx=M_CTX, latent=True)
+    else:
+        dec = Decode(m, torch, synth) if args.only in ("all", "decode") else None
     torch.cuda.synchronize()
 
     lam_p = pre.calibrate(P_TARGET) if pre else None
-    lam_d = dec.calibrate(D_TARGET) if dec else None
+    lam_d = (dec.calibrate(M_TARGETS[-1] if dec.latent else D_TARGET)) if dec else None
 
     def step():
         if pre:
@@ -480,7 +487,7 @@ def main():
         result["prefill"] = r
         result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                              "traffic": profiled_traffic("prefill_bf16_kernel<128, 128, 2, false, false>"),
+                              "traffic": profiled_traffic("prefill_bf16_kernel<128, 128, 2, false, false, true>"),
                               "traffic_unit": "HBM bytes per launch",
                               "min_bytes": pre.min_bytes,
                               "kernel": "prefill_bf16_kernel<128, 128, 2, bf16 out>",
@@ -496,16 +503,18 @@ def main():
             result["prefill_decision_overhead"] = pre.decision_overhead(max(3, args.steps // 2))
     if dec:
         r = dec.measure(lam_d, args.steps, ms=dec_ms)
-        r.update({"target_sparsity": D_TARGET, "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
-                  "workload": "paged GQA decode: batch 32, 32 q / 8 kv heads, d 128, context 32768, 16-token "
-                              "pages, 64-token blocks, 16 splits, bf16"})
+        r.update({"target_sparsity": M_TARGETS[-1] if dec.latent else D_TARGET,
+                  "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
+                  "workload": (MLA_WORKLOAD if dec.latent else
+                               "paged GQA decode: batch 32, 32 q / 8 kv heads, d 128, context 32768, 16-token "
+                               "pages, 64-token blocks, 16 splits, bf16")})
         r["timed_step_ms_p10_p50_p90"] = percentiles(dec_all)
         result["decode"] = r
         result["roofline_decode"] = {"bound": "hbm", "achieved": r["hbm_gbps"], "peak": PEAK_HBM_GBPS,
                                      "unit": "GB/s", "frac": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
-                                     "traffic": profiled_traffic("decode_gqa_kernel<false>"),
-                                     "traffic_unit": "HBM bytes per launch of decode_gqa_kernel",
-                                     "kernel": "decode_gqa_kernel + decode_combine_kernel"}
+                                     "traffic": profiled_traffic(DEC_KERNEL[dec.latent]),
+                                     "traffic_unit": f"HBM bytes per launch of {DEC_KERNEL[dec.latent]}",
+                                     "kernel": f"{DEC_KERNEL[dec.latent]} + decode_combine_kernel"}
         if not pre:
             result.update({"value": r["hbm_gbps"], "unit": "GB/s"})
             config["workload"] = r["workload"]
@@ -520,13 +529,12 @@ def main():
         del d128
         torch.cuda.empty_cache()
         mla = Decode(m, torch, synth, ctx=M_CTX, latent=True)
-        result["mla_decode"] = {"workload": "latent decode, DeepSeek-shaped: batch 64, 128 q heads on one latent "
-                                            "head, 576-dim scores, V = first 512 channels, context 32768, 16-token "
-                                            "pages, 64-token blocks, 16 splits, 128-head tiles, bf16"}
+        result["mla_decode"] = {"workload": MLA_WORKLOAD}
         for tgt in M_TARGETS:
             lam = mla.calibrate(tgt)
             r = mla.measure(lam, args.steps)
-            r.update({"target_sparsity": tgt, "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4)})
+            r.update({"target_sparsity": tgt, "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
+                      "profiled_traffic_bytes_per_launch": profiled_traffic(DEC_KERNEL[True])})
             result["mla_decode"][f"s{tgt}"] = r
         del mla
         torch.cuda.empty_cache()
