@@ -158,14 +158,14 @@ def stratified_tiles(torch, nqt, n_heads, count, seed):
 
 
 class Prefill:
-    def __init__(self, m, torch, synth, L=P_L, seed=None):
+    def __init__(self, m, torch, synth, L=P_L, seed=None, head_strength=None):
         self.m = m
         self.torch = torch
         dev = "cuda"
         self.L = L
         seed = synth.config_seed(2) if seed is None else seed
         self.inp = synth.prefill_inputs(batch=P_B, hq=P_HQ, hkv=P_HKV, L=L, d=P_D, block_k=P_BLK,
-                                        window=True, seed=seed, device=dev)
+                                        window=True, seed=seed, device=dev, head_strength=head_strength)
         self.nqt = L // P_BLK
         self.nkb = L // P_BLK
         self.o = torch.empty(P_B, P_HQ, L, P_D, dtype=torch.bfloat16, device=dev)
@@ -192,6 +192,16 @@ class Prefill:
         t1 = min(t1, timed(self.torch, self.run_no_decision, steps))
         return {"lambda0_ms": round(t0, 4), "no_decision_ms": round(t1, 4),
                 "no_decision_over_lambda0_throughput": round(t1 / t0, 4)}
+
+    def head_stats(self, lam):
+        """Distribution over q heads of the sparsity one threshold gives each head (per-head counters)."""
+        from long_context_online_amd import analysis
+        h = self.torch.zeros(P_B, P_HQ, 2, dtype=self.torch.int64, device="cuda")
+        self.run(lam, head_counters=h)
+        self.torch.cuda.synchronize()
+        st = analysis.head_sparsity_stats(h)
+        return {k: (round(v, 4) if isinstance(v, float) else
+                    [round(x, 3) for x in v] if isinstance(v, list) else v) for k, v in st.items()}
 
     def stats(self):
         """Stats pass (QK^T, block maxima and decisions only): critical values of every tile."""
@@ -303,6 +313,25 @@ class Decode:
             flops = blocks * D_BLK * self.Hq * (self.D * 2) + kept * D_BLK * self.Hq * (self.Dv * 2)
             r["mfma_tflops"] = round(flops / (sparse_ms * 1e-3) / 1e12, 2)
         return r
+
+
+def head_heterogeneity(m, torch, synth, pre, lam_p, steps):
+    """Per-head sparsity under one threshold: the bench workload (heads alike) and the same shape
+    with heads of different peakedness (head strengths spread geometrically over 0.25 ... 2, in a
+    seeded order), each with lambda calibrated for 75% overall sparsity."""
+    out = {"homogeneous": pre.head_stats(lam_p)}
+    g = torch.Generator().manual_seed(synth.config_seed(2, 7))
+    perm = torch.randperm(P_HQ, generator=g).tolist()
+    strength = [0.25 * 8.0 ** (perm[h] / (P_HQ - 1)) for h in range(P_HQ)]
+    het = Prefill(m, torch, synth, seed=synth.config_seed(2, 7), head_strength=strength)
+    lam = het.calibrate(P_TARGET)
+    r = het.measure(lam, steps)
+    r["head_strength"] = [round(c, 3) for c in strength]
+    r["per_head"] = het.head_stats(lam)
+    out["heterogeneous"] = r
+    del het
+    torch.cuda.empty_cache()
+    return out
 
 
 def timed(torch, fn, steps):
@@ -501,6 +530,7 @@ def main():
             result["prefill_s050"] = pre.measure(lam50, max(3, args.steps // 2))
             result["prefill_s050"]["target_sparsity"] = 0.5
             result["prefill_decision_overhead"] = pre.decision_overhead(max(3, args.steps // 2))
+            result["prefill_heads"] = head_heterogeneity(m, torch, synth, pre, lam_p, max(3, args.steps // 2))
     if dec:
         r = dec.measure(lam_d, args.steps, ms=dec_ms)
         r.update({"target_sparsity": M_TARGETS[-1] if dec.latent else D_TARGET,

@@ -95,6 +95,10 @@ enum { BLASST_CNT_LIVE = 0, BLASST_CNT_SKIPPED = 1, BLASST_NUM_COUNTERS = 2 };
  *   skip_mask [batch][num_q_heads][ceil(seqlen_q/block_q)][ceil(seqlen_k/block_k)] uint8
  *   crit      same shape, fp32
  *   counters  BLASST_NUM_COUNTERS x uint64
+ *   head_counters [batch][num_q_heads][BLASST_NUM_COUNTERS] uint64: the same counts per q head
+ *             (accumulated with atomics like counters; the caller zeroes it), so that the sparsity
+ *             one threshold gives each head can be read off directly (the pages' analysis of how
+ *             sparsity varies across heads under a single threshold, "Sparsity distribution").
  * stats_only != 0: compute QK^T, block maxima, decisions, mask, crit and counters only; o and lse
  * are not written (calibration pass).
  * softmax_scale <= 0 selects 1/sqrt(head_dim_qk).
@@ -115,6 +119,7 @@ typedef struct {
   int32_t batch, seqlen_q, seqlen_k, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v;
   int32_t causal, block_q, block_k, num_splits, stats_only;
   float softmax_scale;
+  unsigned long long *head_counters; /* nullable, see above */
 } blasst_prefill_params;
 
 /*

@@ -57,6 +57,7 @@ class PrefillParams(ctypes.Structure):
         ("causal", ctypes.c_int32), ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
         ("num_splits", ctypes.c_int32), ("stats_only", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
+        ("head_counters", ctypes.c_void_p),
     ]
 
 
@@ -163,7 +164,7 @@ def _strides3(t):
 
 def prefill_params(q, k, v, o, *, causal, block_q, block_k, num_splits=1, lam=None, a=None,
                    softmax_scale=0.0, lse=None, skip_mask=None, crit=None, counters=None,
-                   stats_only=False, out_dtype=None, no_decision=False):
+                   stats_only=False, out_dtype=None, no_decision=False, head_counters=None):
     """Fills the C params struct for blasst_prefill from tensors (no call)."""
     p = PrefillParams()
     p.struct_size = ctypes.sizeof(PrefillParams)
@@ -181,13 +182,15 @@ def prefill_params(q, k, v, o, *, causal, block_q, block_k, num_splits=1, lam=No
     p.causal, p.block_q, p.block_k = int(bool(causal)), block_q, block_k
     p.num_splits, p.stats_only = num_splits, int(bool(stats_only))
     p.softmax_scale = float(softmax_scale)
+    p.head_counters = _ptr(head_counters)
     return p
 
 
 def blasst_prefill(q, k, v, o, *, stream=None, **kw):
     """BLASST prefill forward.  q [B, Hq, Lq, D], k/v [B, Hkv, Lk, D], o [B, Hq, Lq, Dv]
     (last dim contiguous).  Keyword args follow the C params (causal, block_q, block_k,
-    num_splits, lam or a, softmax_scale, lse, skip_mask, crit, counters, stats_only)."""
+    num_splits, lam or a, softmax_scale, lse, skip_mask, crit, counters, head_counters,
+    stats_only)."""
     p = prefill_params(q, k, v, o, **kw)
     _check(lib().blasst_prefill(ctypes.byref(p), _stream(stream)))
 

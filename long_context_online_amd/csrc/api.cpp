@@ -135,7 +135,7 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *stream) {
 
   blasst::PrefillArgs a{};
   a.q = p->q; a.k = p->k; a.v = p->v; a.o = p->o; a.lse = p->lse;
-  a.mask = p->skip_mask; a.crit = p->crit; a.counters = p->counters;
+  a.mask = p->skip_mask; a.crit = p->crit; a.counters = p->counters; a.head_counters = p->head_counters;
   for (int i = 0; i < 3; ++i) {
     a.qs[i] = p->q_stride[i]; a.ks[i] = p->k_stride[i]; a.vs[i] = p->v_stride[i]; a.os[i] = p->o_stride[i];
   }

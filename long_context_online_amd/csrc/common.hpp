@@ -29,6 +29,7 @@ struct PrefillArgs {
   uint8_t *mask;
   float *crit;
   unsigned long long *counters;
+  unsigned long long *head_counters;  // [B][Hq][2] or null
   int64_t qs[3], ks[3], vs[3], os[3];  // element strides: batch, head, token
   int B, Lq, Lk, Hq, Hkv, G;           // G = Hq / Hkv
   int nqt, nkb;                        // query tiles per head, key blocks per row of the mask

@@ -78,13 +78,25 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // ---- tile coordinates: heavy causal tiles first, kv-head groups kept on one XCD ----------------
+  // ---- tile coordinates: heavy causal tiles first, kv-head groups kept on one XCD per level -------
   const int groups = a.Hq / TPW;               // head groups of TPW heads sharing a kv head
   const int per_level = a.B * groups;
   const int bid = blockIdx.x;
   const int level = bid / per_level;
   int rem = bid - level * per_level;
-  if ((per_level & 7) == 0) rem = (rem & 7) * (per_level >> 3) + (rem >> 3);
+  // Workgroups go to the 8 XCDs round robin.  A level's head groups are cut into 8 contiguous
+  // chunks; the q heads of one kv head stay together and share its K/V in that XCD's L2, and an
+  // XCD keeps a chunk for a stripe of consecutive levels (about half the levels it holds at once,
+  // 512 / per_level), so tiles in flight on it still share one kv head.  The chunk rotates from
+  // stripe to stripe, forward over 8 stripes and back over the next 8, so every XCD takes every
+  // chunk on stripes of equal total causal work: heads whose sparsity differs then load all XCDs
+  // alike instead of one XCD getting every tile of the densest heads and finishing last.
+  if ((per_level & 7) == 0) {
+    const int stripe = level / max(1, 256 / per_level);
+    const int p = stripe & 15;
+    const int rot = p < 8 ? p : 15 - p;
+    rem = (((rem & 7) + rot) & 7) * (per_level >> 3) + (rem >> 3);
+  }
   const int qt = a.causal ? (a.nqt - 1 - level) : level;
   const int b = rem / groups;
   const int hq0 = (rem - b * groups) * TPW;    // first head of the group
@@ -318,6 +330,11 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   if (a.counters && tile_leader) {
     atomicAdd(&a.counters[0], (unsigned long long)live_cnt);
     atomicAdd(&a.counters[1], (unsigned long long)skip_cnt);
+  }
+  if (a.head_counters && tile_leader) {
+    unsigned long long *hc = a.head_counters + 2 * (b * a.Hq + hq);
+    atomicAdd(&hc[0], (unsigned long long)live_cnt);
+    atomicAdd(&hc[1], (unsigned long long)skip_cnt);
   }
   if (STATS) return;
 

@@ -189,6 +189,11 @@ __global__ __launch_bounds__(128, 2) void prefill_f32_kernel(PrefillArgs a) {
     atomicAdd(&a.counters[0], (unsigned long long)live_cnt);
     atomicAdd(&a.counters[1], (unsigned long long)skip_cnt);
   }
+  if (a.head_counters && tid == 0) {
+    unsigned long long *hc = a.head_counters + 2 * (b * a.Hq + hq);
+    atomicAdd(&hc[0], (unsigned long long)live_cnt);
+    atomicAdd(&hc[1], (unsigned long long)skip_cnt);
+  }
   if (a.stats_only) return;
 
   const float l_row = l_part + __shfl_xor(l_part, 32);

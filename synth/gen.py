@@ -107,8 +107,13 @@ class DecodeInputs:
 
 
 def prefill_inputs(*, batch, hq, hkv, L, d, dv=None, dtype=torch.bfloat16, block_k=128,
-                   window=True, seed=0, device="cpu", Lq=None):
-    """Q/K/V for a causal prefill (Lq = L unless given; queries are the last Lq positions)."""
+                   window=True, seed=0, device="cpu", Lq=None, head_strength=None):
+    """Q/K/V for a causal prefill (Lq = L unless given; queries are the last Lq positions).
+
+    head_strength: optional per-q-head factors c_h for heterogeneous heads: head h's query weights
+    the sink and aligned channels by c_h (boosts c_h * 10 and c_h * 6) and its window correlation is
+    c_h * gamma (boost about c_h * 3), so small c_h gives flat, hard-to-skip attention and large c_h
+    peaked attention.  None (all ones) reproduces the homogeneous inputs draw for draw."""
     dv = d if dv is None else dv
     Lq = L if Lq is None else Lq
     if hq % hkv:
@@ -142,13 +147,20 @@ def prefill_inputs(*, batch, hq, hkv, L, d, dv=None, dtype=torch.bfloat16, block
         k[b] = kf.to(dtype)
         del kf
         eta = torch.randn(hq, Lq, dc, generator=gen, device=device)
+        if head_strength is None:
+            cs = torch.ones(hq, 1, 1, device=device)
+        else:
+            if len(head_strength) != hq:
+                raise ValueError("head_strength needs one factor per q head")
+            cs = torch.tensor([float(c) for c in head_strength], device=device).view(hq, 1, 1)
         if window:
             zq = z[:, L - Lq:, :].repeat_interleave(G, dim=0)             # head h uses kv head h // G
-            qc = gamma * zq + math.sqrt(1.0 - gamma * gamma) * eta
+            gh = torch.clamp(gamma * cs, max=0.95)
+            qc = gh * zq + torch.sqrt(1.0 - gh * gh) * eta
             del zq
         else:
             qc = eta
-        qf = torch.ones(hq, Lq, d, device=device)
+        qf = cs.expand(hq, Lq, 1).repeat(1, 1, d)
         qf[..., :dc] = qc * qscale
         q[b] = qf.to(dtype)
         del qf, qc, eta, z

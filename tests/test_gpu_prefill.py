@@ -29,15 +29,26 @@ def _run(m, q, k, v, *, causal, bq, bk, splits, lam=None, a=None, out_dtype=torc
     mask = torch.full((B, Hq, nqt, nkb), 7, dtype=torch.uint8, device=dev)
     crit = torch.full((B, Hq, nqt, nkb), 12345.0, dtype=torch.float32, device=dev)
     cnt = torch.zeros(2, dtype=torch.int64, device=dev)
+    hcnt = torch.zeros(B, Hq, 2, dtype=torch.int64, device=dev)
     m.blasst_prefill(q, k, v, o, causal=causal, block_q=bq, block_k=bk, num_splits=splits, lam=lam, a=a,
                      lse=None if stats_only else lse, skip_mask=mask, crit=crit, counters=cnt,
-                     stats_only=stats_only)
+                     head_counters=hcnt, stats_only=stats_only)
     torch.cuda.synchronize()
-    return o, lse, mask, crit, cnt
+    _check_counters(mask, cnt, hcnt)
+    return o, lse, mask, crit, cnt, hcnt
+
+
+def _check_counters(mask, cnt, hcnt):
+    """The global and per-head counters are exactly the mask's counts (bit-exact integer work)."""
+    mh = mask.cpu().numpy()
+    h = hcnt.cpu().numpy()
+    assert np.array_equal(h[..., 0], (mh != 2).sum(axis=(2, 3))), "per-head live counts differ from the mask"
+    assert np.array_equal(h[..., 1], (mh == 1).sum(axis=(2, 3))), "per-head skip counts differ from the mask"
+    assert int(cnt[0]) == int(h[..., 0].sum()) and int(cnt[1]) == int(h[..., 1].sum())
 
 
 def _compare_all(q, k, v, res, *, causal, bq, bk, splits, ln_lam, tiles=None, out_bf16=False):
-    o, lse, mask, crit, cnt = res
+    o, lse, mask, crit, cnt, _ = res
     mh, ch = mask.cpu().numpy(), crit.cpu().numpy()
     B, Hq, Lq, _ = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
@@ -137,6 +148,7 @@ def test_stats_only_matches_full_pass():
     assert torch.equal(full[2], st[2])
     assert torch.allclose(full[3], st[3], rtol=0, atol=0, equal_nan=True)
     assert torch.equal(full[4], st[4])
+    assert torch.equal(full[5], st[5])
 
 
 def test_llama8b_gqa_32k_sampled_tiles():
@@ -149,7 +161,7 @@ def test_llama8b_gqa_32k_sampled_tiles():
                                seed=synth.config_seed(2), device="cuda")
     lam = 0.02   # a sparse operating point (about 3/4 of the blocks skipped on this generator)
     res = _run(m, inp.q, inp.k, inp.v, causal=True, bq=128, bk=128, splits=1, lam=lam)
-    o, lse, mask, crit, cnt = res
+    o, lse, mask, crit, cnt, _ = res
     ln_lam = math.log(lam)
     mh, ch = mask.cpu().numpy(), crit.cpu().numpy()
     live = mh != 2
@@ -185,3 +197,25 @@ def test_no_decision_mode_equals_lambda_zero():
     ref = oracle.softmax_attention(q[0, 1], k[0, 0], v[0, 0], causal_visible(np.arange(640), 640, 640, 640),
                                   1 / math.sqrt(128))
     assert np.max(np.abs(outs[1][0][0, 1].double().numpy() - ref[0])) < 1e-2
+
+
+@pytest.mark.parametrize("dtype,blk", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_heterogeneous_heads_per_head_sparsity(dtype, blk):
+    """Heads of very different peakedness (head strengths 0.25 ... 1.75) under ONE threshold: every
+    tile matches the oracle, the per-head counters match the oracle's per-head counts outside the
+    decision band, and the per-head sparsities spread out, more peaked heads skipping more."""
+    m = _lib()
+    L, hq = 768, 8
+    strength = [0.25, 1.75, 0.5, 1.5, 0.75, 1.25, 1.0, 0.35]
+    inp = synth.prefill_inputs(batch=1, hq=hq, hkv=2, L=L, d=128 if dtype == torch.bfloat16 else 64,
+                               dtype=dtype, block_k=blk, window=True, seed=31, device="cuda",
+                               head_strength=strength)
+    lam = 0.01
+    res = _run(m, inp.q, inp.k, inp.v, causal=True, bq=blk, bk=blk, splits=1, lam=lam)
+    rep = _compare_all(inp.q, inp.k, inp.v, res, causal=True, bq=blk, bk=blk, splits=1, ln_lam=math.log(lam))
+    h = res[5].cpu().numpy()[0]
+    sp = h[:, 1] / h[:, 0]
+    print(f"{rep}; per-head sparsity by strength: " +
+          ", ".join(f"{c}:{s:.3f}" for c, s in sorted(zip(strength, sp))))
+    order = np.argsort(strength)
+    assert sp[order[-1]] > sp[order[0]] + 0.2

@@ -90,3 +90,33 @@ def test_latent_cache_has_no_v():
     d = synth.decode_inputs(batch=2, hq=16, hkv=1, ctx=64, d=72, dv=64, page_size=16, block_k=64,
                             seed=1, latent=True)
     assert d.v_cache_t is None and d.head_dim_v == 64 and d.k_cache.shape[1] == 1
+
+
+def test_head_strength_scales_each_heads_boosts():
+    """head_strength c_h: sink boost 10 c_h, aligned boost 6 c_h, window boost 3 c_h per q head, unit
+    content-logit spread kept; None is the homogeneous draw, bit for bit."""
+    d, L, bk = 128, 4096, 128
+    base = synth.prefill_inputs(batch=1, hq=4, hkv=1, L=L, d=d, dtype=torch.float32, block_k=bk, seed=4)
+    ones = synth.prefill_inputs(batch=1, hq=4, hkv=1, L=L, d=d, dtype=torch.float32, block_k=bk, seed=4,
+                                head_strength=[1.0] * 4)
+    assert torch.equal(base.q, ones.q) and torch.equal(base.k, ones.k) and torch.equal(base.v, ones.v)
+    c = [0.5, 1.0, 1.5, 2.0]
+    p = synth.prefill_inputs(batch=1, hq=4, hkv=1, L=L, d=d, dtype=torch.float32, block_k=bk, seed=4,
+                             head_strength=c)
+    assert torch.equal(p.k, base.k) and torch.equal(p.v, base.v)
+    q, k = p.q[0].double(), p.k[0, 0].double()
+    j = min(p.aligned[0][0])
+    i = torch.arange(1024, L)
+    for h, ch in enumerate(c):
+        assert torch.allclose(p.scale * q[h, :, d - 2] * k[0, d - 2], torch.full((L,), 10.0 * ch, dtype=torch.float64),
+                              atol=1e-5)
+        assert abs(p.scale * q[h, 0, d - 1].item() * k[j * bk, d - 1].item() - 6.0 * ch) < 1e-5
+        content = p.scale * q[h, :, :d - 2] @ k[:, :d - 2].T
+        assert abs(content[i, i].mean().item() - 3.0 * ch) < 0.3, (h, content[i, i].mean().item())
+        assert 0.9 < content[i, i - 2048].std().item() < 1.1
+    try:
+        synth.prefill_inputs(batch=1, hq=4, hkv=1, L=256, d=64, block_k=64, seed=4, head_strength=[1.0])
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a wrong-length head_strength must be rejected")
