@@ -328,11 +328,31 @@ def gather_pages(k_cache, v_cache_t, block_table, b, g, seq_len, page_size, head
     return K, V
 
 
+def _decode_queries(q):
+    """q [B, Hq, Dqk] (one query token per sequence) or [B, T, Hq, Dqk] (T query tokens, the last T
+    positions of each sequence) as fp64 [B, T, Hq, Dqk], and whether it had the token axis."""
+    q = np.asarray(q, dtype=np.float64)
+    if q.ndim == 3:
+        return q[:, None], False
+    if q.ndim != 4:
+        raise ValueError("q must be [B, Hq, D] or [B, T, Hq, D]")
+    return q, True
+
+
 def decode_tile(q, k_cache, v_cache_t, block_table, seq_lens, b, g, rt, *, page_size, block_k,
                 num_splits, ln_lam, tile_rows, head_dim_v, scale=None, force=None):
     """One decode tile: the tile_rows q heads [g*G + rt*tile_rows, ...) of sequence b that share
-    kv head g (G = Hq/Hkv).  One query token per sequence sees all keys < seq_len."""
-    B, Hq, D = q.shape
+    kv head g (G = Hq/Hkv), for each of the sequence's T query tokens.
+
+    q [B, Hq, Dqk] has one query token per sequence, which sees every key < seq_len.  q
+    [B, T, Hq, Dqk] has T query tokens, the last T positions of the sequence (the tokens a decode
+    step verifies, or a chunk of a prefill continued against the paged cache: the pages' method
+    serves both phases, xllm-io review, 核心思想 item 2); token t sees keys
+    k <= seq_len - T + t (bottom-right causal, as in prefill).  The tile's rows are token-major:
+    row t * tile_rows + i is token t of head g*G + rt*tile_rows + i, and every row votes.
+    """
+    q4, _ = _decode_queries(q)
+    B, T, Hq, D = q4.shape
     Hkv = k_cache.shape[1]
     G = Hq // Hkv
     if scale is None:
@@ -340,19 +360,22 @@ def decode_tile(q, k_cache, v_cache_t, block_table, seq_lens, b, g, rt, *, page_
     L = int(seq_lens[b])
     K, V = gather_pages(k_cache, v_cache_t, block_table, b, g, L, page_size, head_dim_v)
     h0 = g * G + rt * tile_rows
-    rows = np.asarray(q[b, h0:h0 + tile_rows], dtype=np.float64)
-    vis = np.ones((rows.shape[0], L), dtype=bool)
+    rows = q4[b, :, h0:h0 + tile_rows].reshape(T * tile_rows, D)
+    tok = np.repeat(np.arange(T), tile_rows)
+    vis = np.arange(L)[None, :] <= (L - T + tok)[:, None]
     return tile_sequential(rows, K, V, vis, block_k, num_splits, ln_lam, scale, force=force)
 
 
 def decode(q, k_cache, v_cache_t, block_table, seq_lens, *, page_size, block_k, num_splits,
            lam=None, a=None, tile_rows=None, head_dim_v=None, scale=None):
-    """Whole paged decode.  q [B, Hq, Dqk].  With a given, lambda_b = min(1, a / seq_lens[b]).
+    """Whole paged decode.  q [B, Hq, Dqk], or [B, T, Hq, Dqk] for T query tokens per sequence
+    (see decode_tile).  With a given, lambda_b = min(1, a / seq_lens[b]).
 
-    Returns O [B, Hq, Dv], LSE [B, Hq], mask/crit [B, Hkv, Hq/Hkv/tile_rows, n_kblocks(max)].
+    Returns O [B, Hq, Dv] and LSE [B, Hq] ([B, T, Hq, Dv] and [B, T, Hq] with the token axis),
+    mask/crit [B, Hkv, Hq/Hkv/tile_rows, n_kblocks(max)].
     """
-    q = np.asarray(q, dtype=np.float64)
-    B, Hq, D = q.shape
+    q4, tokens = _decode_queries(q)
+    B, T, Hq, D = q4.shape
     Hkv = k_cache.shape[1]
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
@@ -364,21 +387,23 @@ def decode(q, k_cache, v_cache_t, block_table, seq_lens, *, page_size, block_k, 
         head_dim_v = v_cache_t.shape[2] if v_cache_t is not None else D
     n_rt = G // tile_rows
     nkb = -(-int(max(seq_lens)) // block_k)
-    O = np.zeros((B, Hq, head_dim_v))
-    LSE = np.full((B, Hq), NEG_INF)
+    O = np.zeros((B, T, Hq, head_dim_v))
+    LSE = np.full((B, T, Hq), NEG_INF)
     mask = np.full((B, Hkv, n_rt, nkb), NOT_LIVE, dtype=np.int8)
     crit = np.full((B, Hkv, n_rt, nkb), np.nan)
     for b in range(B):
         ln_lam = ln_threshold(lam=lam, a=a, L=int(seq_lens[b])) if lam is None else ln_threshold(lam=lam)
         for g in range(Hkv):
             for rt in range(n_rt):
-                r = decode_tile(q, k_cache, v_cache_t, block_table, seq_lens, b, g, rt,
+                r = decode_tile(q4, k_cache, v_cache_t, block_table, seq_lens, b, g, rt,
                                 page_size=page_size, block_k=block_k, num_splits=num_splits,
                                 ln_lam=ln_lam, tile_rows=tile_rows, head_dim_v=head_dim_v, scale=scale)
                 h0 = g * G + rt * tile_rows
-                O[b, h0:h0 + tile_rows] = r["o"]
-                LSE[b, h0:h0 + tile_rows] = r["lse"]
+                O[b, :, h0:h0 + tile_rows] = r["o"].reshape(T, tile_rows, head_dim_v)
+                LSE[b, :, h0:h0 + tile_rows] = r["lse"].reshape(T, tile_rows)
                 n = r["mask"].shape[0]
                 mask[b, g, rt, :n] = r["mask"]
                 crit[b, g, rt, :n] = r["crit"]
+    if not tokens:
+        O, LSE = O[:, 0], LSE[:, 0]
     return {"o": O, "lse": LSE, "mask": mask, "crit": crit}

@@ -113,7 +113,7 @@ def prefill_inputs(*, batch, hq, hkv, L, d, dv=None, dtype=torch.bfloat16, block
     head_strength: optional per-q-head factors c_h for heterogeneous heads: head h's query weights
     the sink and aligned channels by c_h (boosts c_h * 10 and c_h * 6) and its window correlation is
     c_h * gamma (boost about c_h * 3), so small c_h gives flat, hard-to-skip attention and large c_h
-    peaked attention.  None (all ones) reproduces the homogeneous inputs draw for draw."""
+    peaked attention.  None gives every head factor 1 (the homogeneous inputs)."""
     dv = d if dv is None else dv
     Lq = L if Lq is None else Lq
     if hq % hkv:
@@ -155,8 +155,11 @@ def prefill_inputs(*, batch, hq, hkv, L, d, dv=None, dtype=torch.bfloat16, block
             cs = torch.tensor([float(c) for c in head_strength], device=device).view(hq, 1, 1)
         if window:
             zq = z[:, L - Lq:, :].repeat_interleave(G, dim=0)             # head h uses kv head h // G
-            gh = torch.clamp(gamma * cs, max=0.95)
-            qc = gh * zq + torch.sqrt(1.0 - gh * gh) * eta
+            if head_strength is None:
+                qc = gamma * zq + math.sqrt(1.0 - gamma * gamma) * eta
+            else:
+                gh = torch.clamp(gamma * cs, max=0.95)
+                qc = gh * zq + torch.sqrt(1.0 - gh * gh) * eta
             del zq
         else:
             qc = eta

@@ -313,3 +313,77 @@ def test_decode_a_over_L_uses_each_sequence_length():
         rb = oracle.decode(q[b:b + 1], kc, vc, table[b:b + 1], lens[b:b + 1], page_size=4, block_k=4,
                            num_splits=1, lam=min(1.0, a / lens[b]), scale=0.4)
         assert np.array_equal(rb["o"][0], r["o"][b])
+
+
+def _token_queries(rng, B, T, Hq, D):
+    return rng.standard_normal((B, T, Hq, D))
+
+
+@pytest.mark.parametrize("T,S", [(1, 1), (3, 1), (4, 3), (7, 2)])
+def test_multi_token_decode_dense_is_causal_softmax(T, S):
+    """T query tokens per sequence at lambda = 0: token t of sequence b is softmax attention over keys
+    0 .. seq_len - T + t (written out here with scipy), whatever the splits."""
+    rng = np.random.default_rng(60 + T)
+    _, kc, vc, table, lens, Kc, Vc = _random_paged(rng)
+    B, Hq, Hkv = 3, 8, 2
+    G = Hq // Hkv
+    q = _token_queries(rng, B, T, Hq, 8)
+    r = oracle.decode(q, kc, vc, table, lens, page_size=4, block_k=8, num_splits=S, lam=0.0, scale=0.4)
+    assert r["o"].shape == (B, T, Hq, 6) and r["lse"].shape == (B, T, Hq)
+    for b in range(B):
+        for t in range(T):
+            n = lens[b] - T + t + 1
+            for h in range(Hq):
+                logits = 0.4 * Kc[b][h // G][:n] @ q[b, t, h]
+                assert np.max(np.abs(r["o"][b, t, h] - softmax(logits) @ Vc[b][h // G][:n])) < 1e-9
+                assert abs(r["lse"][b, t, h] - logsumexp(logits)) < 1e-9
+
+
+def test_multi_token_decode_one_token_is_single_token_decode():
+    rng = np.random.default_rng(61)
+    q, kc, vc, table, lens, _, _ = _random_paged(rng)
+    kw = dict(page_size=4, block_k=4, num_splits=2, lam=0.1, scale=0.4)
+    r1 = oracle.decode(q, kc, vc, table, lens, **kw)
+    r4 = oracle.decode(q[:, None], kc, vc, table, lens, **kw)
+    assert np.array_equal(r1["o"], r4["o"][:, 0]) and np.array_equal(r1["lse"], r4["lse"][:, 0])
+    assert np.array_equal(r1["mask"], r4["mask"])
+
+
+@pytest.mark.parametrize("T,S,lam", [(4, 1, 0.5), (5, 2, 0.7), (8, 1, 0.9)])
+def test_multi_token_decode_single_head_tile_is_prefill_tile(T, S, lam):
+    """With one q head per tile, a decode tile of T tokens is the prefill tile of Lq = T queries
+    over the sequence's keys (block_q = T, bottom-right causal): the same decisions and outputs,
+    reached through the paged gather on one side and contiguous tensors on the other."""
+    rng = np.random.default_rng(62 + T)
+    _, kc, vc, table, lens, Kc, Vc = _random_paged(rng, lens=(23, 16, 12))
+    q = _token_queries(rng, 3, T, 8, 8)
+    r = oracle.decode(q, kc, vc, table, lens, page_size=4, block_k=4, num_splits=S, lam=lam, tile_rows=1,
+                      scale=0.4)
+    G = 4
+    skipped = 0
+    for b in range(3):
+        for h in range(8):
+            p = oracle.prefill(q[b, :, h][None, None], Kc[b][h // G][None, None], Vc[b][h // G][None, None],
+                               causal=True, block_q=T, block_k=4, num_splits=S, lam=lam, scale=0.4)
+            n = p["mask"].shape[-1]
+            assert np.array_equal(p["mask"][0, 0, 0], r["mask"][b, h // G, h % G, :n])
+            assert np.max(np.abs(p["o"][0, 0] - r["o"][b, :, h])) < 1e-12
+            assert np.max(np.abs(p["lse"][0, 0] - r["lse"][b, :, h])) < 1e-12
+            skipped += int((p["mask"] == SKIPPED).sum())
+    assert skipped > 0
+
+
+def test_multi_token_decode_rows_without_keys():
+    """A sequence shorter than T: its first T - seq_len tokens see no key (o = 0, lse = -inf), the
+    rest are causal softmax over what they see."""
+    rng = np.random.default_rng(63)
+    _, kc, vc, table, lens, Kc, Vc = _random_paged(rng, lens=(23, 3, 9))
+    T = 5
+    q = _token_queries(rng, 3, T, 8, 8)
+    r = oracle.decode(q, kc, vc, table, lens, page_size=4, block_k=8, num_splits=1, lam=0.3, scale=0.4)
+    assert np.all(r["o"][1, :2] == 0.0) and np.all(r["lse"][1, :2] == -np.inf)
+    for t in (2, 3, 4):
+        n = 3 - T + t + 1
+        for h in range(8):
+            logits = 0.4 * Kc[1][h // 4][:n] @ q[1, t, h]
+            assert np.max(np.abs(r["o"][1, t, h] - softmax(logits) @ Vc[1][h // 4][:n])) < 1e-12
