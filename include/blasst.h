@@ -123,31 +123,36 @@ typedef struct {
 } blasst_prefill_params;
 
 /*
- * Decode: one query token per sequence attends to all seq_lens[b] keys of a paged KV cache,
- * split along the keys into num_splits chunks that run in parallel and are merged by a log-sum-exp
- * combine.
+ * Decode: the query tokens of each sequence attend to the keys of a paged KV cache, split along
+ * the keys into num_splits chunks that run in parallel and are merged by a log-sum-exp combine.
+ * With T = num_q_tokens (0 means 1) query tokens per sequence, they are the last T positions of
+ * the sequence: token t sees keys k <= seq_lens[b] - T + t (bottom-right causal, as in prefill), so
+ * T = 1 is ordinary decode and T > 1 serves a decode step that checks several tokens at once or a
+ * chunk of prefill continued against the cache (the method serves both phases: xllm-io review,
+ * 核心思想 item 2).  A token that sees no key (seq_lens[b] < T) gets o = 0 and lse = -inf.
  *
  * Layouts (contiguous):
- *   q           [batch][num_q_heads][head_dim_qk]
+ *   q           [batch][T][num_q_heads][head_dim_qk]
  *   k_cache     [num_pages][num_kv_heads][page_size][head_dim_qk]
  *   v_cache     [num_pages][num_kv_heads][head_dim_v][page_size]  (V transposed inside each page)
  *               NULL selects latent attention (MLA): V is the first head_dim_v channels of K.
  *   block_table [batch][max_pages_per_seq] int32 page ids; entries past a sequence's last page
  *               are never read
  *   seq_lens    [batch] int32, 1 <= seq_lens[b] <= max_pages_per_seq * page_size
- *   o           [batch][num_q_heads][head_dim_v], dtype out_dtype
- *   lse         [batch][num_q_heads] fp32, nullable
+ *   o           [batch][T][num_q_heads][head_dim_v], dtype out_dtype
+ *   lse         [batch][T][num_q_heads] fp32, nullable
  * Query tile = tile_rows q heads of one sequence that share a kv head (0 selects all
- * num_q_heads / num_kv_heads of them); KV block = block_k keys (a multiple of page_size).
+ * num_q_heads / num_kv_heads of them), for all T tokens: T * tile_rows rows, token-major, that
+ * vote together; KV block = block_k keys (a multiple of page_size).
  * Diagnostics (nullable):
  *   skip_mask/crit [batch][num_kv_heads][G / tile_rows][ceil(max_pages_per_seq*page_size/block_k)]
  *   counters as for prefill.
  * workspace: needed when num_splits > 1, at least blasst_decode_workspace_size() bytes, device
  * memory, 256-byte aligned.
  * Supported kernels: bf16 in, bf16/fp32 out; page_size 16; block_k 64;
- *   GQA/MHA/MQA: head_dim_qk == head_dim_v == 128, tile_rows <= 16;
+ *   GQA/MHA/MQA: head_dim_qk == head_dim_v == 128, T * tile_rows <= 16;
  *   latent (v_cache NULL): 128 q heads on 1 kv head, head_dim_qk == 576, head_dim_v == 512,
- *   tile_rows 128 (one tile of all heads) or 64 (MLA-shaped).
+ *   tile_rows 128 (one tile of all heads) or 64 (MLA-shaped), T == 1.
  */
 typedef struct {
   size_t struct_size;        /* sizeof(blasst_decode_params) */
@@ -166,7 +171,7 @@ typedef struct {
   int32_t page_size, max_pages_per_seq, num_pages;
   int32_t block_k, num_splits, tile_rows, stats_only;
   float softmax_scale;
-  int32_t reserved;          /* must be 0 */
+  int32_t num_q_tokens;      /* T, query tokens per sequence; 0 or 1: one */
 } blasst_decode_params;
 
 /* Prefill forward (see the struct comment).  stream: hipStream_t or NULL. */

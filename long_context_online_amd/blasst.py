@@ -76,7 +76,7 @@ class DecodeParams(ctypes.Structure):
         ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
         ("block_k", ctypes.c_int32), ("num_splits", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
         ("stats_only", ctypes.c_int32),
-        ("softmax_scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("num_q_tokens", ctypes.c_int32),
     ]
 
 
@@ -211,7 +211,11 @@ def decode_params(q, k_cache, v_cache, block_table, seq_lens, o, *, page_size, b
     p.thr = _threshold(lam, a)
     p.in_dtype = _dtype_code(q)
     p.out_dtype = _dtype_code(o) if o is not None else (p.in_dtype if out_dtype is None else out_dtype)
-    p.batch, p.num_q_heads, p.head_dim_qk = q.shape
+    if q.dim() == 4:
+        p.batch, p.num_q_tokens, p.num_q_heads, p.head_dim_qk = q.shape
+    else:
+        p.batch, p.num_q_heads, p.head_dim_qk = q.shape
+        p.num_q_tokens = 1
     p.num_pages, p.num_kv_heads, page, _ = k_cache.shape
     if page != page_size:
         raise ValueError("k_cache page dimension does not match page_size")
@@ -222,7 +226,6 @@ def decode_params(q, k_cache, v_cache, block_table, seq_lens, o, *, page_size, b
     p.block_k, p.num_splits, p.tile_rows = block_k, num_splits, tile_rows
     p.stats_only = int(bool(stats_only))
     p.softmax_scale = float(softmax_scale)
-    p.reserved = 0
     return p
 
 
@@ -236,9 +239,10 @@ def blasst_decode_workspace_size(*args, **kw) -> int:
 
 
 def blasst_decode(q, k_cache, v_cache, block_table, seq_lens, o, *, stream=None, **kw):
-    """BLASST paged split-KV decode.  q [B, Hq, D]; k_cache [P, Hkv, page, D]; v_cache
+    """BLASST paged split-KV decode.  q [B, Hq, D], or [B, T, Hq, D] for T query tokens per sequence
+    (the last T positions, bottom-right causal); k_cache [P, Hkv, page, D]; v_cache
     [P, Hkv, Dv, page] (V transposed per page) or None for latent attention (V = K[..., :Dv]);
-    block_table [B, max_pages] int32; seq_lens [B] int32; o [B, Hq, Dv]."""
+    block_table [B, max_pages] int32; seq_lens [B] int32; o [B, Hq, Dv] or [B, T, Hq, Dv]."""
     p = decode_params(q, k_cache, v_cache, block_table, seq_lens, o, **kw)
     _check(lib().blasst_decode(ctypes.byref(p), _stream(stream)))
 

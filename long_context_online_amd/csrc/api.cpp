@@ -164,7 +164,7 @@ static blasst_status validate_decode(const blasst_decode_params *p, bool need_pt
   if (!p) return fail(BLASST_ERR_INVALID_ARG, "params is NULL");
   if (p->struct_size != sizeof(blasst_decode_params))
     return fail(BLASST_ERR_INVALID_ARG, "struct_size %zu != %zu", p->struct_size, sizeof(blasst_decode_params));
-  if (p->reserved != 0) return fail(BLASST_ERR_INVALID_ARG, "reserved must be 0");
+  if (p->num_q_tokens < 0) return fail(BLASST_ERR_INVALID_ARG, "num_q_tokens must be >= 0");
   if (p->batch < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 || p->head_dim_qk < 1 || p->head_dim_v < 1)
     return fail(BLASST_ERR_INVALID_ARG, "sizes must be >= 1");
   if (p->num_q_heads % p->num_kv_heads)
@@ -192,19 +192,21 @@ static blasst_status validate_decode(const blasst_decode_params *p, bool need_pt
   if (p->in_dtype != BLASST_BF16) return fail(BLASST_ERR_UNSUPPORTED, "decode supports bf16 inputs");
   if (p->page_size != 16 || p->block_k != 64) return fail(BLASST_ERR_UNSUPPORTED, "decode supports page 16, block 64");
   const bool latent = p->v_cache == nullptr;
+  const int T = p->num_q_tokens == 0 ? 1 : p->num_q_tokens;
   if (latent) {
     if (p->num_kv_heads != 1 || p->num_q_heads != 128 || p->head_dim_qk != 576 || p->head_dim_v != 512 ||
-        (tr != 128 && tr != 64))
+        (tr != 128 && tr != 64) || T != 1)
       return fail(BLASST_ERR_UNSUPPORTED,
-                  "latent decode supports 128 q heads on 1 kv head, dims 576/512, tile_rows 128 or 64");
+                  "latent decode supports 128 q heads on 1 kv head, dims 576/512, tile_rows 128 or 64, one "
+                  "query token");
   } else {
-    if (p->head_dim_qk != 128 || p->head_dim_v != 128 || tr > 16)
-      return fail(BLASST_ERR_UNSUPPORTED, "decode supports head dim 128 and tile_rows <= 16");
+    if (p->head_dim_qk != 128 || p->head_dim_v != 128 || (int64_t)T * tr > 16)
+      return fail(BLASST_ERR_UNSUPPORTED, "decode supports head dim 128 and num_q_tokens * tile_rows <= 16");
   }
   if (need_ptrs && (!aligned16(p->q) || !aligned16(p->k_cache) || (p->v_cache && !aligned16(p->v_cache)) ||
                     (p->o && !aligned16(p->o))))
     return fail(BLASST_ERR_UNSUPPORTED, "q, caches and o must be 16-byte aligned");
-  const size_t parts = (size_t)p->batch * p->num_q_heads * p->num_splits;
+  const size_t parts = (size_t)p->batch * T * p->num_q_heads * p->num_splits;
   size_t bytes = 0;
   if (p->num_splits > 1) {
     const size_t o_bytes = (parts * p->head_dim_v * sizeof(float) + 255) / 256 * 256;
@@ -237,13 +239,15 @@ blasst_status blasst_decode(const blasst_decode_params *p, void *stream) {
   blasst::DecodeArgs a{};
   a.q = p->q; a.kc = p->k_cache; a.vc = p->v_cache; a.table = p->block_table; a.seq_lens = p->seq_lens;
   a.o = p->o; a.lse = p->lse; a.mask = p->skip_mask; a.crit = p->crit; a.counters = p->counters;
+  const int T = p->num_q_tokens == 0 ? 1 : p->num_q_tokens;
   if (ws > 0 && !p->stats_only) {
-    const size_t parts = (size_t)p->batch * p->num_q_heads * p->num_splits;
+    const size_t parts = (size_t)p->batch * T * p->num_q_heads * p->num_splits;
     const size_t o_bytes = (parts * p->head_dim_v * sizeof(float) + 255) / 256 * 256;
     a.ws_o = (float *)p->workspace;
     a.ws_lse = (float *)((char *)p->workspace + o_bytes);
   }
   a.B = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = G; a.tile_rows = tr; a.n_rt = G / tr;
+  a.T = T;
   a.page = p->page_size; a.max_pages = p->max_pages_per_seq; a.block_k = p->block_k;
   a.nkb = (int)(((int64_t)p->max_pages_per_seq * p->page_size + p->block_k - 1) / p->block_k);
   a.num_splits = p->num_splits; a.stats_only = p->stats_only ? 1 : 0; a.out_f32 = p->out_dtype == BLASST_FP32;

@@ -52,6 +52,7 @@ struct DecodeArgs {
   float *ws_o;    // [B][Hq][S][Dv] per-split normalised outputs (num_splits > 1)
   float *ws_lse;  // [B][Hq][S]
   int B, Hq, Hkv, G, tile_rows, n_rt;
+  int T;           // query tokens per sequence (the last T positions; token t sees keys <= L - T + t)
   int page, max_pages, block_k, nkb;
   int num_splits, stats_only, out_f32;
   int thr_mode;    // 0: fixed lambda (thr_raw valid); 1: lambda_b = min(1, a / seq_lens[b])

@@ -11,6 +11,9 @@
 // MI355X design:
 //   * one workgroup = (sequence, kv head, row tile, split); 4 waves; wave w owns the w-th 16-token
 //     page of every 64-token block, so each wave issues page-sized, page-aligned loads;
+//   * the tile's query columns are (token, head) pairs, token-major: with T query tokens per
+//     sequence (the last T positions) column t * tile_rows + i is token t of the tile's head i, and
+//     its keys past seq_len - T + t are masked like keys past the sequence end;
 //   * K-first batch of NB blocks: each wave loads its NB K pages straight into MFMA operand
 //     registers (16 bytes per lane per k-step), computes S^T = K q^T with
 //     v_mfma_f32_16x16x32_bf16 (the tile's <= 16 q heads are the N columns), and publishes its
@@ -60,8 +63,11 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
   const int chunk = (J + a.num_splits - 1) / a.num_splits;
   const int j0 = split * chunk;
   const int j1 = min(J, j0 + chunk);
-  const bool col_ok = n < a.tile_rows;
-  const int hq = g * a.G + rt * a.tile_rows + n;
+  const int ncol = a.T * a.tile_rows;       // query columns of the tile (<= 16)
+  const bool col_ok = n < ncol;
+  const int tok = col_ok ? n / a.tile_rows : 0;
+  const int hq = g * a.G + rt * a.tile_rows + (n - tok * a.tile_rows);
+  const int64_t qrow = ((int64_t)b * a.T + tok) * a.Hq + hq;  // row of q (and of o, lse)
 
   float thr = a.thr_raw;
   if (a.thr_mode == 1) {
@@ -71,7 +77,7 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
 
   // q fragments: B operand of S^T = K q^T; lane holds dims kk*32 + grp*8 .. +7 of query column n
   bf16x8 qf[4];
-  const __bf16 *qp = (const __bf16 *)a.q + ((int64_t)b * a.Hq + hq) * D;
+  const __bf16 *qp = (const __bf16 *)a.q + qrow * D;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qf[kk] = col_ok ? *(const bf16x8 *)(qp + kk * 32 + grp * 8) : bf16x8{};
 
@@ -80,6 +86,7 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
   const int32_t *table = a.table + (int64_t)b * a.max_pages;
   const int64_t page_stride = (int64_t)a.Hkv * PAGE * D;  // elements per physical page (all heads)
   const int npg = (L + PAGE - 1) / PAGE;                   // pages of this sequence (>= 1)
+  const int lim = L - a.T + tok;                           // last key this column sees
 
   float m_dec = kNegInf, m_acc = kNegInf, l_part = 0.f;
   f32x4 o_acc[D / 16];
@@ -127,11 +134,11 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         s[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[i][kk]), qf[kk], s[i], 0, 0, 0);
-      // keys past the sequence end (and blocks past the batch) are masked out
+      // keys past the column's last visible key (and blocks past the batch) are masked out
       const int keyb = (jb + i) * BK + wave * PAGE + grp * 4;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (i >= nb || keyb + r >= L) s[i][r] = kNegInf;
+        if (i >= nb || keyb + r > lim) s[i][r] = kNegInf;
       float pm = fmaxf(fmaxf(s[i][0], s[i][1]), fmaxf(s[i][2], s[i][3]));
       pm = max_xor16_32(pm);
       if (grp == 0) sPmax[i][wave][n] = pm;
@@ -251,7 +258,7 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
   const int dv0 = (tid & 15) * 8;    // 0..120
   // m_acc of column col lives in the lanes with n == col (the same value in every wave)
   const float m_col = __shfl(m_acc, col);
-  if (col < a.tile_rows) {
+  if (col < ncol) {
     const float l_tot = sL[0][col] + sL[1][col] + sL[2][col] + sL[3][col];
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float ov[8];
@@ -259,9 +266,11 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
     for (int e = 0; e < 8; ++e)
       ov[e] = (sRed[0][col][dv0 + e] + sRed[1][col][dv0 + e] + sRed[2][col][dv0 + e] + sRed[3][col][dv0 + e]) * inv;
     const float lse = l_tot > 0.f ? m_col * a.scale + __logf(l_tot) : kNegInf;
-    const int h = g * a.G + rt * a.tile_rows + col;
+    const int ctok = col / a.tile_rows;
+    const int h = g * a.G + rt * a.tile_rows + (col - ctok * a.tile_rows);
+    const int64_t orow = ((int64_t)b * a.T + ctok) * a.Hq + h;
     if (a.num_splits == 1) {
-      const int64_t ob = ((int64_t)b * a.Hq + h) * D + dv0;
+      const int64_t ob = orow * D + dv0;
       if (OUT_F32) {
         f32x4 w0 = {ov[0], ov[1], ov[2], ov[3]}, w1 = {ov[4], ov[5], ov[6], ov[7]};
         *(f32x4 *)((float *)a.o + ob) = w0;
@@ -274,9 +283,9 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
         w[3] = pack_bf16x2(ov[6], ov[7]);
         *(u32x4 *)((__bf16 *)a.o + ob) = w;
       }
-      if (a.lse && dv0 == 0) a.lse[(int64_t)b * a.Hq + h] = lse;
+      if (a.lse && dv0 == 0) a.lse[orow] = lse;
     } else {
-      const int64_t pb = (((int64_t)b * a.Hq + h) * a.num_splits + split);
+      const int64_t pb = orow * a.num_splits + split;
       float *wo = a.ws_o + pb * D + dv0;
       f32x4 w0 = {ov[0], ov[1], ov[2], ov[3]}, w1 = {ov[4], ov[5], ov[6], ov[7]};
       *(f32x4 *)wo = w0;
@@ -347,7 +356,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *ws_o, 
 
 // Dv is 128 (GQA / MHA / MQA) or 512 (latent attention).
 hipError_t launch_decode_combine(const DecodeArgs &a, int Dv, hipStream_t st) {
-  const int BH = a.B * a.Hq;
+  const int BH = a.B * a.T * a.Hq;  // rows of (sequence, token, q head)
   const int grid = (BH + 3) / 4;
   if (Dv == 128) {
     if (a.out_f32)

@@ -95,7 +95,7 @@ class PrefillInputs:
 
 @dataclass
 class DecodeInputs:
-    q: torch.Tensor            # [B, Hq, Dqk]
+    q: torch.Tensor            # [B, Hq, Dqk], or [B, T, Hq, Dqk] with T query tokens per sequence
     k_cache: torch.Tensor      # [P, Hkv, page, Dqk]
     v_cache_t: torch.Tensor | None   # [P, Hkv, Dv, page] (None: V = K[..., :Dv], latent attention)
     block_table: torch.Tensor  # [B, max_pages] int32
@@ -172,10 +172,14 @@ def prefill_inputs(*, batch, hq, hkv, L, d, dv=None, dtype=torch.bfloat16, block
 
 
 def decode_inputs(*, batch, hq, hkv, ctx, d, dv=None, dtype=torch.bfloat16, page_size=16,
-                  block_k=64, window=True, seed=0, device="cpu", latent=False, seq_lens=None):
+                  block_k=64, window=True, seed=0, device="cpu", latent=False, seq_lens=None,
+                  num_q_tokens=None):
     """One query token per sequence over a paged KV cache with randomly permuted pages.
 
     ctx: the context length of every sequence, unless seq_lens (a list) gives one per sequence.
+    num_q_tokens=T: q is [B, T, Hq, D] instead, T query tokens at the last T positions of each
+    sequence (their keys are in the cache); token t correlates with the key at its own position
+    seq_len - T + t, as a prefill query does.
     latent=True: one shared latent head; V is the first dv channels of K (no V cache).
     Pages beyond a sequence's length, the slots after its last key and 1/16 extra spare pages
     are filled with NaN, so a wrong gather poisons the result.  Unused block-table entries point
@@ -207,7 +211,10 @@ def decode_inputs(*, batch, hq, hkv, ctx, d, dv=None, dtype=torch.bfloat16, page
     spare_ids = perm[live:]
     k_cache = torch.full((P, hkv, page_size, d), float("nan"), dtype=dtype, device=device)
     v_cache_t = None if latent else torch.full((P, hkv, dv, page_size), float("nan"), dtype=dtype, device=device)
-    q = torch.empty(batch, hq, d, dtype=dtype, device=device)
+    T = num_q_tokens
+    if T is not None and (T < 1 or T > min(lens)):
+        raise ValueError("num_q_tokens must lie in [1, shortest sequence]")
+    q = torch.empty((batch, hq, d) if T is None else (batch, T, hq, d), dtype=dtype, device=device)
     aligned = []
     off = 0
     for b in range(batch):
@@ -239,18 +246,31 @@ def decode_inputs(*, batch, hq, hkv, ctx, d, dv=None, dtype=torch.bfloat16, page
         kpages = kf.to(dtype).view(hkv, npg, page_size, d).permute(1, 0, 2, 3)
         k_cache[ids.long()] = kpages
         del kf, kpages
-        eta = torch.randn(hq, dc, generator=gen, device=device)
-        if window:
-            rho = math.exp(-1.0 / WINDOW_LEN)
-            e_next = torch.randn(hkv, dc, generator=gen, device=device)
-            z_q = rho * z_last[:, 0, :] + math.sqrt(1.0 - rho * rho) * e_next   # position n
-            qc = gamma * z_q.repeat_interleave(G, dim=0) + math.sqrt(1.0 - gamma * gamma) * eta
+        if T is not None:
+            eta = torch.randn(T, hq, dc, generator=gen, device=device)
+            if window:
+                zt = z[:, n - T:n, :].permute(1, 0, 2).repeat_interleave(G, dim=1)   # [T, Hq, dc]
+                qc = gamma * zt + math.sqrt(1.0 - gamma * gamma) * eta
+            else:
+                qc = eta
+            qf = torch.ones(T, hq, d, device=device)
+            qf[..., :dc] = qc * qscale
+            q[b] = qf.to(dtype)
+            del qf, qc, eta
         else:
-            qc = eta
-        qf = torch.ones(hq, d, device=device)
-        qf[:, :dc] = qc * qscale
-        q[b] = qf.to(dtype)
-        del z, qf, qc, eta
+            eta = torch.randn(hq, dc, generator=gen, device=device)
+            if window:
+                rho = math.exp(-1.0 / WINDOW_LEN)
+                e_next = torch.randn(hkv, dc, generator=gen, device=device)
+                z_q = rho * z_last[:, 0, :] + math.sqrt(1.0 - rho * rho) * e_next   # position n
+                qc = gamma * z_q.repeat_interleave(G, dim=0) + math.sqrt(1.0 - gamma * gamma) * eta
+            else:
+                qc = eta
+            qf = torch.ones(hq, d, device=device)
+            qf[:, :dc] = qc * qscale
+            q[b] = qf.to(dtype)
+            del qf, qc, eta
+        del z
         if not latent:
             vf = torch.full((hkv, npg * page_size, dv), float("nan"), device=device)
             vf[:, :n] = torch.randn(hkv, n, dv, generator=gen, device=device)

@@ -112,11 +112,14 @@ def _decode(**over):
 
 DECODE_BAD = [
     ({"q": None}, 1), ({"seq_lens": None}, 1), ({"num_kv_heads": 5}, 1), ({"block_k": 40}, 1),
-    ({"num_splits": 0}, 1), ({"tile_rows": 3}, 1), ({"thr": (0, 0, 2.0, 0.0)}, 1), ({"reserved": 1}, 1),
+    ({"num_splits": 0}, 1), ({"tile_rows": 3}, 1), ({"thr": (0, 0, 2.0, 0.0)}, 1), ({"num_q_tokens": -1}, 1),
     ({"page_size": 0}, 1), ({"struct_size": 4}, 1),
     ({"in_dtype": 1}, 2), ({"page_size": 32, "block_k": 64}, 2), ({"block_k": 128}, 2),
     ({"head_dim_qk": 64, "head_dim_v": 64}, 2), ({"v_cache": None}, 2),
     ({"workspace": None}, 4),
+    ({"num_q_tokens": 5}, 2), ({"num_q_tokens": 9, "tile_rows": 2}, 2),
+    ({"v_cache": None, "num_kv_heads": 1, "num_q_heads": 128, "head_dim_qk": 576, "head_dim_v": 512,
+      "tile_rows": 128, "num_q_tokens": 2}, 2),
 ]
 
 
@@ -136,6 +139,8 @@ def test_decode_workspace_size(m):
     assert n >= parts * (128 + 1) * 4 and n % 256 == 0
     p1 = _decode(num_splits=1)
     assert lib.blasst_decode_workspace_size(ctypes.byref(p1)) == 0
+    p4 = _decode(num_q_tokens=4, tile_rows=4)
+    assert lib.blasst_decode_workspace_size(ctypes.byref(p4)) >= 4 * parts * (128 + 1) * 4
     bad = _decode(num_kv_heads=5)
     assert lib.blasst_decode_workspace_size(ctypes.byref(bad)) == 0 and lib.blasst_last_error()
 

@@ -20,15 +20,16 @@ def _lib():
 
 
 def _run(m, d, *, splits, lam=None, a=None, tile_rows=0, out_dtype=torch.float32, stats_only=False):
-    B, Hq, D = d.q.shape
+    B, Hq = d.q.shape[0], d.q.shape[-2]       # q [B, Hq, D] or [B, T, Hq, D]
     Hkv = d.k_cache.shape[1]
     G = Hq // Hkv
     tr = G if tile_rows == 0 else tile_rows
     dev = d.q.device
     max_pages = d.block_table.shape[1]
     nkb = -(-(max_pages * d.page_size) // 64)
-    o = None if stats_only else torch.full((B, Hq, d.head_dim_v), float("nan"), dtype=out_dtype, device=dev)
-    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=dev)
+    rows = tuple(d.q.shape[:-1])
+    o = None if stats_only else torch.full(rows + (d.head_dim_v,), float("nan"), dtype=out_dtype, device=dev)
+    lse = torch.full(rows, float("nan"), dtype=torch.float32, device=dev)
     mask = torch.full((B, Hkv, G // tr, nkb), 7, dtype=torch.uint8, device=dev)
     crit = torch.full((B, Hkv, G // tr, nkb), 12345.0, dtype=torch.float32, device=dev)
     cnt = torch.zeros(2, dtype=torch.int64, device=dev)
@@ -59,10 +60,11 @@ def _compare(d, res, *, splits, lam=None, a=None, tiles=None, tile_rows=0, out_b
     mh, ch = mask.cpu().numpy(), crit.cpu().numpy()
     oh = host64(o) if o is not None else None
     lh = lse.cpu().double().numpy()
-    B, Hq, _ = d.q.shape
+    B, Hq = d.q.shape[0], d.q.shape[-2]
     Hkv = d.k_cache.shape[1]
     G = Hq // Hkv
     tr = G if tile_rows == 0 else tile_rows
+    multi = d.q.dim() == 4
     rep = Report()
     if tiles is None:
         tiles = [(b, g, rt) for b in range(B) for g in range(Hkv) for rt in range(G // tr)]
@@ -80,7 +82,9 @@ def _compare(d, res, *, splits, lam=None, a=None, tiles=None, tile_rows=0, out_b
         assert np.all(mh[b, g, rt, nb:] == 2)
         check_tile(rep, ref, mh[b, g, rt], ch[b, g, rt], ln_lam,
                    lambda f: oracle.decode_tile(qh, kc, vc, bt, sl1, 0, g, rt, force=f, **kw),
-                   None if oh is None else oh[b, h0:h0 + tr], None if oh is None else lh[b, h0:h0 + tr],
+                   None if oh is None else (oh[b, :, h0:h0 + tr].reshape(-1, oh.shape[-1]) if multi
+                                            else oh[b, h0:h0 + tr]),
+                   None if oh is None else (lh[b, :, h0:h0 + tr].reshape(-1) if multi else lh[b, h0:h0 + tr]),
                    out_bf16=out_bf16)
     return rep
 
@@ -209,3 +213,47 @@ def test_latent_mla_late_large_logit_redo(splits):
     rep = _compare(d, res, splits=splits, a=0.0, tile_rows=128)
     print(f"S={splits}: {rep}")
     assert rep.skipped == 0
+
+
+@pytest.mark.parametrize("T,tile_rows,splits", [(2, 0, 1), (4, 4, 3), (8, 2, 16), (16, 1, 5), (3, 4, 1)])
+@pytest.mark.parametrize("a", [0.0, 4.0])
+def test_multi_token_decode(T, tile_rows, splits, a):
+    """T query tokens per sequence (the last T positions; token t sees keys <= seq_len - T + t) against
+    the paged cache: 16 q / 4 kv heads, ragged lengths including sequences no longer than T and a
+    one-token one, every (T, tile_rows) that fills up to the 16 query columns of a tile."""
+    m = _lib()
+    lens = [700, 64, 2 * T + 1, 1500, T, 130]
+    d = synth.decode_inputs(batch=len(lens), hq=16, hkv=4, ctx=None, d=128, seq_lens=lens, seed=50 + T,
+                            device="cuda", num_q_tokens=T)
+    res = _run(m, d, splits=splits, a=a, tile_rows=tile_rows)
+    rep = _compare(d, res, splits=splits, a=a, tile_rows=tile_rows)
+    print(f"T={T} tile_rows={tile_rows} S={splits} a={a}: {rep}")
+    if a == 0.0:
+        assert rep.skipped == 0
+
+
+def test_multi_token_decode_short_sequence_rows_without_keys():
+    """seq_lens below T: the first T - seq_len tokens see no key and get o = 0, lse = -inf; the others
+    match the oracle (the cache holds more keys than seq_lens admits, and they must stay unread)."""
+    m = _lib()
+    T = 6
+    d = synth.decode_inputs(batch=3, hq=8, hkv=2, ctx=None, d=128, seq_lens=[40, 200, 6], seed=71,
+                            device="cuda", num_q_tokens=T)
+    d.seq_lens[0] = 4    # tokens 0, 1 of sequence 0 see nothing
+    d.seq_lens[2] = 1    # only the last token of sequence 2 sees a key
+    res = _run(m, d, splits=2, lam=0.05, tile_rows=2)
+    o, lse = res[0].cpu(), res[1].cpu()
+    assert torch.all(o[0, :2] == 0) and torch.all(lse[0, :2] == float("-inf"))
+    assert torch.all(o[2, :5] == 0) and torch.all(lse[2, :5] == float("-inf"))
+    rep = _compare(d, res, splits=2, lam=0.05, tile_rows=2)
+    print(rep)
+
+
+def test_multi_token_one_token_equals_single_token_layout():
+    """T = 1 through the [B, 1, Hq, D] layout gives the bits of the [B, Hq, D] call."""
+    m = _lib()
+    d = synth.decode_inputs(batch=4, hq=32, hkv=8, ctx=3000, d=128, seed=72, device="cuda")
+    r1 = _run(m, d, splits=4, lam=0.01)
+    d.q = d.q[:, None].contiguous()
+    r4 = _run(m, d, splits=4, lam=0.01)
+    assert torch.equal(r1[0], r4[0][:, 0]) and torch.equal(r1[1], r4[1][:, 0]) and torch.equal(r1[2], r4[2])

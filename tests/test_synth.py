@@ -120,3 +120,23 @@ def test_head_strength_scales_each_heads_boosts():
         pass
     else:
         raise AssertionError("a wrong-length head_strength must be rejected")
+
+
+def test_decode_multi_token_queries_sit_at_the_last_positions():
+    """num_q_tokens = T: q [B, T, Hq, D]; token t's content correlates with the key at its own
+    position seq_len - T + t (window boost about 3 there, decaying away from it)."""
+    T, L, d = 8, 2048, 128
+    x = synth.decode_inputs(batch=2, hq=16, hkv=1, ctx=L, d=d, dtype=torch.float32, seed=12, num_q_tokens=T)
+    assert x.q.shape == (2, T, 16, d)
+    k = x.k_cache[x.block_table[0].long(), 0].reshape(-1, d)[:L, :d - 2].double()
+    q = x.q[0, :, :, :d - 2].double()
+    own = torch.stack([x.scale * q[t] @ k[L - T + t] for t in range(T)])     # [T, Hq]
+    assert abs(own.mean().item() - 3.0) < 0.5
+    far = torch.stack([x.scale * q[t] @ k[L - T + t - 1500] for t in range(T)])
+    assert abs(far.mean().item()) < 1.0 and own.mean().item() - far.mean().item() > 2.0
+    try:
+        synth.decode_inputs(batch=1, hq=4, hkv=1, ctx=5, d=64, seed=1, num_q_tokens=6)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("more query tokens than keys must be rejected")
