@@ -235,11 +235,12 @@ class Prefill:
 
 
 class Decode:
-    def __init__(self, m, torch, synth, ctx=D_CTX, latent=False, seed=None):
+    def __init__(self, m, torch, synth, ctx=D_CTX, latent=False, seed=None, num_q_tokens=None, tile_rows=None):
         self.m = m
         self.torch = torch
         self.latent = latent
         self.ctx = ctx
+        self.T = 1 if num_q_tokens is None else num_q_tokens
         dev = "cuda"
         if latent:
             self.B, self.Hq, self.Hkv, self.D, self.Dv, self.tile_rows = M_B, M_HQ, 1, M_D, M_DV, M_HQ
@@ -248,11 +249,13 @@ class Decode:
         seed = (synth.config_seed(5) if latent else synth.config_seed(3)) if seed is None else seed
         self.d = synth.decode_inputs(batch=self.B, hq=self.Hq, hkv=self.Hkv, ctx=ctx, d=self.D, dv=self.Dv,
                                      page_size=D_PAGE, block_k=D_BLK, window=True, seed=seed, device=dev,
-                                     latent=latent)
-        self.o = torch.empty(self.B, self.Hq, self.Dv, dtype=torch.bfloat16, device=dev)
-        self.lse = torch.empty(self.B, self.Hq, dtype=torch.float32, device=dev)
+                                     latent=latent, num_q_tokens=num_q_tokens)
+        if tile_rows is not None:
+            self.tile_rows = tile_rows
+        rows = tuple(self.d.q.shape[:-1])
+        self.o = torch.empty(rows + (self.Dv,), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(rows, dtype=torch.float32, device=dev)
         self.nkb = -(-(self.d.block_table.shape[1] * D_PAGE) // D_BLK)
-        self.n_rt = 1
         n = m.blasst_decode_workspace_size(self.d.q, self.d.k_cache, self.d.v_cache_t, self.d.block_table,
                                            self.d.seq_lens, self.o, **self._kw(0.0))
         self.ws = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -267,7 +270,8 @@ class Decode:
                              **self._kw(lam), **diag)
 
     def mask_shape(self):
-        return (self.B, self.Hkv, self.n_rt, self.nkb)
+        G = self.Hq // self.Hkv
+        return (self.B, self.Hkv, G // self.tile_rows if self.tile_rows else 1, self.nkb)
 
     def calibrate(self, target):
         """ln(lambda) at the target sparsity from the critical values of every tile of the batch
@@ -285,10 +289,11 @@ class Decode:
         kept = int((mask == 0).sum())
         k_bytes = self.B * self.Hkv * self.ctx * self.D * 2
         v_bytes = 0 if self.latent else kept * D_BLK * self.Dv * 2     # every block is full here
-        q_bytes = self.B * self.Hq * self.D * 2
+        rows = self.B * self.T * self.Hq          # query rows (tokens x heads)
+        q_bytes = rows * self.D * 2
         table = self.d.block_table.numel() * 4
-        parts = self.B * self.Hq * D_SPLITS * (self.Dv + 1) * 4 * 2
-        out = self.B * self.Hq * self.Dv * 2 + self.B * self.Hq * 4
+        parts = rows * D_SPLITS * (self.Dv + 1) * 4 * 2
+        out = rows * self.Dv * 2 + rows * 4
         dense_v = 0 if self.latent else self.B * self.Hkv * self.ctx * self.Dv * 2
         return (k_bytes + v_bytes + q_bytes + table + parts + out,
                 k_bytes + dense_v + q_bytes + table + parts + out)
@@ -558,6 +563,17 @@ def main():
         result["decode_131072"] = r
         del d128
         torch.cuda.empty_cache()
+        result["decode_multi_token"] = {}
+        for T in (2, 4):
+            mt = Decode(m, torch, synth, seed=synth.config_seed(3, 2), num_q_tokens=T, tile_rows=D_HQ // D_HKV)
+            lam = mt.calibrate(D_TARGET)
+            r = mt.measure(lam, args.steps)
+            r.update({"target_sparsity": D_TARGET, "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
+                      "workload": f"the decode workload with {T} query tokens per sequence (the last {T} "
+                                  f"positions), tiles of {T} tokens x 4 heads"})
+            result["decode_multi_token"][f"T{T}"] = r
+            del mt
+            torch.cuda.empty_cache()
         mla = Decode(m, torch, synth, ctx=M_CTX, latent=True)
         result["mla_decode"] = {"workload": MLA_WORKLOAD}
         for tgt in M_TARGETS:
