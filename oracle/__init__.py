@@ -17,6 +17,9 @@ Softmax Thresholding", arXiv 2512.12087):
   [fugu]  fugumt.com page with the English v1 abstract.
   [gist-ja] gist.science Japanese summary, sections 2.1 (skip condition) and 2.2 (calibration).
 
+``oracle.backward`` (torch fp64 autograd on the CPU) gives the gradients of the sparse prefill with
+the forward's decisions held fixed ([xllm] 训练流程: skipped blocks receive no gradient).
+
 Parity pins: every public function is pinned by a ``-m "not gpu"`` test against something other
 than itself (textbook dense softmax, hand-derived closed forms, invariants, reductions).  No
 function here is "parity unpinned".
@@ -44,3 +47,4 @@ from .calibration import (  # noqa: F401
     lambda_for,
     achieved_sparsity,
 )
+from . import backward  # noqa: F401,E402
