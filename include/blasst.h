@@ -174,8 +174,60 @@ typedef struct {
   int32_t num_q_tokens;      /* T, query tokens per sequence; 0 or 1: one */
 } blasst_decode_params;
 
+/*
+ * Prefill backward for sparsity-aware training: the gradients of the prefill forward with the
+ * forward's skip decisions held fixed.  The pages' training extension runs the BLASST forward and
+ * lets skipped blocks receive no gradient in the backward pass (xllm-io review, 训练流程 /
+ * 稀疏感知训练); the function differentiated is, for each query row, softmax attention over the
+ * visible keys of the key blocks its tile kept:
+ *   O_i = sum_{k in K_i} softmax_k(scale * q_i . k_k) v_k,
+ * so with P = exp(scale * Q K^T - LSE) on those pairs and D_i = sum_d dO_id O_id:
+ *   dV = P^T dO, dP = dO V^T, dS = scale * P * (dP - D), dQ = dS K, dK = dS^T Q,
+ * and a skipped or not-live tile-block adds nothing to dQ, dK or dV.
+ *
+ * Inputs (device memory, last dimension contiguous, element strides {batch, head, token}):
+ *   q, k, v   as for the forward (bf16)
+ *   o         the forward's output [batch][num_q_heads][seqlen_q][head_dim_v], dtype o_dtype (bf16 or
+ *             fp32; it enters only D, where an fp32 output avoids the bf16 rounding of O)
+ *   dout      dL/dO [batch][num_q_heads][seqlen_q][head_dim_v] (bf16)
+ *   lse       the forward's LSE [batch][num_q_heads][seqlen_q] fp32 contiguous
+ *   skip_mask the forward's skip mask [batch][num_q_heads][ceil(seqlen_q/block_q)]
+ *             [ceil(seqlen_k/block_k)] uint8, from a forward with the same causal flag and blocks;
+ *             NULL: every live block counts as kept (the backward of dense attention)
+ * Outputs (overwritten, dtype grad_dtype):
+ *   dq [batch][num_q_heads][seqlen_q][head_dim_qk], dk [batch][num_kv_heads][seqlen_k][head_dim_qk],
+ *   dv [batch][num_kv_heads][seqlen_k][head_dim_v]; dk and dv sum over the q heads of each kv head.
+ * workspace: device memory of at least blasst_prefill_backward_workspace_size() bytes (the row
+ * sums D), 256-byte aligned; the library allocates nothing.
+ * Rows without any kept key (LSE = -inf) get no gradient.
+ * Supported: bf16 inputs, bf16 or fp32 gradients, head_dim_qk == head_dim_v == 128,
+ * block_q == block_k == 128.
+ */
+typedef struct {
+  size_t struct_size;        /* sizeof(blasst_prefill_backward_params) */
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  const uint8_t *skip_mask;
+  void *dq, *dk, *dv;
+  void *workspace;
+  size_t workspace_bytes;
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3], dout_stride[3];
+  int64_t dq_stride[3], dk_stride[3], dv_stride[3];
+  int32_t in_dtype, grad_dtype, o_dtype; /* blasst_dtype */
+  int32_t batch, seqlen_q, seqlen_k, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v;
+  int32_t causal, block_q, block_k;
+  float softmax_scale;       /* <= 0 selects 1/sqrt(head_dim_qk); must match the forward */
+} blasst_prefill_backward_params;
+
 /* Prefill forward (see the struct comment).  stream: hipStream_t or NULL. */
 blasst_status blasst_prefill(const blasst_prefill_params *params, void *stream);
+
+/* Prefill backward (see the struct comment).  stream: hipStream_t or NULL. */
+blasst_status blasst_prefill_backward(const blasst_prefill_backward_params *params, void *stream);
+
+/* Workspace bytes that blasst_prefill_backward needs for these params.  Returns 0 and sets the last
+ * error when the params are invalid. */
+size_t blasst_prefill_backward_workspace_size(const blasst_prefill_backward_params *params);
 
 /* Paged split-KV decode forward (see the struct comment).  stream: hipStream_t or NULL. */
 blasst_status blasst_decode(const blasst_decode_params *params, void *stream);
@@ -211,6 +263,7 @@ const char *blasst_last_error(void);
 int32_t blasst_version(void);
 size_t blasst_prefill_params_size(void);
 size_t blasst_decode_params_size(void);
+size_t blasst_prefill_backward_params_size(void);
 
 #ifdef __cplusplus
 }

@@ -4,6 +4,9 @@
 from .blasst import (  # noqa: F401
     BlasstError,
     blasst_prefill,
+    blasst_prefill_backward,
+    blasst_prefill_backward_workspace_size,
+    backward_params,
     blasst_decode,
     blasst_decode_workspace_size,
     blasst_calib_quantile,

@@ -27,6 +27,7 @@ EXPORTED = [
     "blasst_prefill", "blasst_decode", "blasst_decode_workspace_size", "blasst_calib_quantile",
     "blasst_calibrate", "blasst_lambda_for", "blasst_status_string", "blasst_last_error",
     "blasst_version", "blasst_prefill_params_size", "blasst_decode_params_size",
+    "blasst_prefill_backward", "blasst_prefill_backward_workspace_size", "blasst_prefill_backward_params_size",
 ]
 
 
@@ -80,6 +81,27 @@ class DecodeParams(ctypes.Structure):
     ]
 
 
+class BackwardParams(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("dout", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p), ("skip_mask", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+        ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+        ("dout_stride", ctypes.c_int64 * 3), ("dq_stride", ctypes.c_int64 * 3),
+        ("dk_stride", ctypes.c_int64 * 3), ("dv_stride", ctypes.c_int64 * 3),
+        ("in_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32), ("o_dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32), ("seqlen_q", ctypes.c_int32), ("seqlen_k", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
 _lib = None
 
 
@@ -96,6 +118,10 @@ def lib():
         L.blasst_decode.restype = ctypes.c_int
         L.blasst_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeParams)]
         L.blasst_decode_workspace_size.restype = ctypes.c_size_t
+        L.blasst_prefill_backward.argtypes = [ctypes.POINTER(BackwardParams), ctypes.c_void_p]
+        L.blasst_prefill_backward.restype = ctypes.c_int
+        L.blasst_prefill_backward_workspace_size.argtypes = [ctypes.POINTER(BackwardParams)]
+        L.blasst_prefill_backward_workspace_size.restype = ctypes.c_size_t
         L.blasst_calib_quantile.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_int64, ctypes.c_double,
                                             ctypes.POINTER(ctypes.c_double)]
         L.blasst_calib_quantile.restype = ctypes.c_int
@@ -111,8 +137,10 @@ def lib():
         L.blasst_version.restype = ctypes.c_int32
         L.blasst_prefill_params_size.restype = ctypes.c_size_t
         L.blasst_decode_params_size.restype = ctypes.c_size_t
+        L.blasst_prefill_backward_params_size.restype = ctypes.c_size_t
         if L.blasst_prefill_params_size() != ctypes.sizeof(PrefillParams) or \
-                L.blasst_decode_params_size() != ctypes.sizeof(DecodeParams):
+                L.blasst_decode_params_size() != ctypes.sizeof(DecodeParams) or \
+                L.blasst_prefill_backward_params_size() != ctypes.sizeof(BackwardParams):
             raise ImportError("libblasst.so struct layout does not match this binding")
         _lib = L
     return _lib
@@ -193,6 +221,47 @@ def blasst_prefill(q, k, v, o, *, stream=None, **kw):
     stats_only)."""
     p = prefill_params(q, k, v, o, **kw)
     _check(lib().blasst_prefill(ctypes.byref(p), _stream(stream)))
+
+
+def backward_params(q, k, v, o, dout, lse, dq, dk, dv, *, causal, block_q=128, block_k=128, skip_mask=None,
+                    workspace=None, softmax_scale=0.0):
+    """Fills the C params struct for blasst_prefill_backward from tensors (no call)."""
+    p = BackwardParams()
+    p.struct_size = ctypes.sizeof(BackwardParams)
+    p.q, p.k, p.v, p.o, p.dout = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout)
+    p.lse, p.skip_mask = _ptr(lse), _ptr(skip_mask)
+    p.dq, p.dk, p.dv = _ptr(dq), _ptr(dk), _ptr(dv)
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    p.q_stride, p.k_stride, p.v_stride = _strides3(q), _strides3(k), _strides3(v)
+    p.o_stride, p.dout_stride = _strides3(o), _strides3(dout)
+    p.dq_stride, p.dk_stride, p.dv_stride = _strides3(dq), _strides3(dk), _strides3(dv)
+    p.in_dtype = _dtype_code(q)
+    p.grad_dtype = _dtype_code(dq)
+    p.o_dtype = _dtype_code(o)
+    p.batch, p.num_q_heads, p.seqlen_q, p.head_dim_qk = q.shape
+    p.num_kv_heads, p.seqlen_k = k.shape[1], k.shape[2]
+    p.head_dim_v = v.shape[3]
+    p.causal, p.block_q, p.block_k = int(bool(causal)), block_q, block_k
+    p.softmax_scale = float(softmax_scale)
+    return p
+
+
+def blasst_prefill_backward_workspace_size(*args, **kw) -> int:
+    p = backward_params(*args, **kw)
+    n = lib().blasst_prefill_backward_workspace_size(ctypes.byref(p))
+    if n == 0:
+        raise BlasstError(ERR_INVALID_ARG, lib().blasst_last_error().decode())
+    return int(n)
+
+
+def blasst_prefill_backward(q, k, v, o, dout, lse, dq, dk, dv, *, stream=None, **kw):
+    """Gradients of the sparse prefill with the forward's decisions fixed.  q [B, Hq, Lq, D], k/v
+    [B, Hkv, Lk, D], o/dout [B, Hq, Lq, D] (bf16), lse [B, Hq, Lq] fp32 from the forward; dq/dk/dv
+    shaped like q/k/v (bf16 or fp32).  Keyword args follow the C params (causal, skip_mask = the
+    forward's mask or None for dense, workspace, softmax_scale)."""
+    p = backward_params(q, k, v, o, dout, lse, dq, dk, dv, **kw)
+    _check(lib().blasst_prefill_backward(ctypes.byref(p), _stream(stream)))
 
 
 def decode_params(q, k_cache, v_cache, block_table, seq_lens, o, *, page_size, block_k, num_splits,

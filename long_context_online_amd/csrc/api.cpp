@@ -15,6 +15,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs &a, int D, int BC, bool out_f32
 hipError_t launch_prefill_f32(const PrefillArgs &a, int D, hipStream_t st);
 hipError_t launch_decode_gqa(const DecodeArgs &a, hipStream_t st);
 hipError_t launch_decode_latent(const DecodeArgs &a, hipStream_t st);
+hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t st);
 }  // namespace blasst
 
 namespace {
@@ -83,6 +84,7 @@ const char *blasst_last_error(void) { return g_err; }
 int32_t blasst_version(void) { return 10000; }
 size_t blasst_prefill_params_size(void) { return sizeof(blasst_prefill_params); }
 size_t blasst_decode_params_size(void) { return sizeof(blasst_decode_params); }
+size_t blasst_prefill_backward_params_size(void) { return sizeof(blasst_prefill_backward_params); }
 
 blasst_status blasst_prefill(const blasst_prefill_params *p, void *stream) {
   if (!p) return fail(BLASST_ERR_INVALID_ARG, "params is NULL");
@@ -214,6 +216,87 @@ static blasst_status validate_decode(const blasst_decode_params *p, bool need_pt
   }
   *ws_bytes = bytes;
   return BLASST_OK;
+}
+
+static blasst_status validate_backward(const blasst_prefill_backward_params *p, bool need_ptrs, size_t *ws) {
+  if (!p) return fail(BLASST_ERR_INVALID_ARG, "params is NULL");
+  if (p->struct_size != sizeof(blasst_prefill_backward_params))
+    return fail(BLASST_ERR_INVALID_ARG, "struct_size %zu != %zu", p->struct_size,
+                sizeof(blasst_prefill_backward_params));
+  if (p->batch < 1 || p->seqlen_q < 1 || p->seqlen_k < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 ||
+      p->head_dim_qk < 1 || p->head_dim_v < 1)
+    return fail(BLASST_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (p->num_q_heads % p->num_kv_heads)
+    return fail(BLASST_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (p->block_q < 1 || p->block_k < 1) return fail(BLASST_ERR_INVALID_ARG, "block sizes must be >= 1");
+  if (p->in_dtype != BLASST_BF16 && p->in_dtype != BLASST_FP32) return fail(BLASST_ERR_INVALID_ARG, "bad in_dtype");
+  if (p->grad_dtype != BLASST_BF16 && p->grad_dtype != BLASST_FP32)
+    return fail(BLASST_ERR_INVALID_ARG, "bad grad_dtype");
+  if (p->o_dtype != BLASST_BF16 && p->o_dtype != BLASST_FP32) return fail(BLASST_ERR_INVALID_ARG, "bad o_dtype");
+  if (p->causal != 0 && p->causal != 1) return fail(BLASST_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!std::isfinite(p->softmax_scale)) return fail(BLASST_ERR_INVALID_ARG, "softmax_scale must be finite");
+  for (int i = 0; i < 3; ++i)
+    if (p->q_stride[i] < 0 || p->k_stride[i] < 0 || p->v_stride[i] < 0 || p->o_stride[i] < 0 ||
+        p->dout_stride[i] < 0 || p->dq_stride[i] < 0 || p->dk_stride[i] < 0 || p->dv_stride[i] < 0)
+      return fail(BLASST_ERR_INVALID_ARG, "strides must be >= 0");
+  if (need_ptrs) {
+    if (!p->q || !p->k || !p->v || !p->o || !p->dout || !p->lse || !p->dq || !p->dk || !p->dv)
+      return fail(BLASST_ERR_INVALID_ARG, "q, k, v, o, dout, lse, dq, dk and dv must be non-NULL");
+  }
+  // ---- kernel coverage ----
+  if (p->in_dtype != BLASST_BF16) return fail(BLASST_ERR_UNSUPPORTED, "the backward supports bf16 inputs");
+  if (p->head_dim_qk != 128 || p->head_dim_v != 128 || p->block_q != 128 || p->block_k != 128)
+    return fail(BLASST_ERR_UNSUPPORTED, "the backward supports head dim 128 and 128 x 128 blocks");
+  for (int i = 0; i < 3; ++i)
+    if (p->q_stride[i] % 8 || p->k_stride[i] % 8 || p->v_stride[i] % 8 || p->o_stride[i] % 4 ||
+        p->dout_stride[i] % 8 || p->dq_stride[i] % 8 || p->dk_stride[i] % 8 || p->dv_stride[i] % 8)
+      return fail(BLASST_ERR_UNSUPPORTED, "strides must be multiples of 8 elements");
+  if (need_ptrs && (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->o) ||
+                    !aligned16(p->dout) || !aligned16(p->dq) || !aligned16(p->dk) || !aligned16(p->dv)))
+    return fail(BLASST_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
+  const double nqt = (p->seqlen_q + 127) / 128, nkb = (p->seqlen_k + 127) / 128;
+  if ((double)p->batch * p->num_q_heads * nqt * nkb > 2147483647.0 ||
+      (double)p->batch * p->num_q_heads * p->seqlen_q > 2147483647.0)
+    return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
+  *ws = ((size_t)p->batch * p->num_q_heads * p->seqlen_q * sizeof(float) + 255) / 256 * 256;
+  return BLASST_OK;
+}
+
+size_t blasst_prefill_backward_workspace_size(const blasst_prefill_backward_params *p) {
+  size_t ws = 0;
+  if (validate_backward(p, false, &ws) != BLASST_OK) return 0;
+  ok();
+  return ws;
+}
+
+blasst_status blasst_prefill_backward(const blasst_prefill_backward_params *p, void *stream) {
+  size_t ws = 0;
+  blasst_status st = validate_backward(p, true, &ws);
+  if (st != BLASST_OK) return st;
+  if (!p->workspace || p->workspace_bytes < ws)
+    return fail(BLASST_ERR_WORKSPACE, "workspace of %zu bytes required", ws);
+  if (reinterpret_cast<uintptr_t>(p->workspace) & 255u)
+    return fail(BLASST_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const double scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0 / std::sqrt((double)p->head_dim_qk);
+  blasst::BwdArgs a{};
+  a.q = p->q; a.k = p->k; a.v = p->v; a.o = p->o; a.dout = p->dout; a.lse = p->lse; a.mask = p->skip_mask;
+  a.dq = p->dq; a.dk = p->dk; a.dv = p->dv; a.dvec = (float *)p->workspace;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = p->q_stride[i]; a.ks[i] = p->k_stride[i]; a.vs[i] = p->v_stride[i]; a.os[i] = p->o_stride[i];
+    a.dos[i] = p->dout_stride[i]; a.dqs[i] = p->dq_stride[i]; a.dks[i] = p->dk_stride[i]; a.dvs[i] = p->dv_stride[i];
+  }
+  a.B = p->batch; a.Lq = p->seqlen_q; a.Lk = p->seqlen_k; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
+  a.G = p->num_q_heads / p->num_kv_heads;
+  a.nqt = (p->seqlen_q + 127) / 128;
+  a.nkb = (p->seqlen_k + 127) / 128;
+  a.causal = p->causal;
+  a.out_f32 = p->grad_dtype == BLASST_FP32;
+  a.o_f32 = p->o_dtype == BLASST_FP32;
+  a.scale = (float)scale;
+  a.scale_log2 = (float)(scale * 1.4426950408889634);
+  hipError_t e = blasst::launch_prefill_bwd(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BLASST_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 size_t blasst_decode_workspace_size(const blasst_decode_params *p) {

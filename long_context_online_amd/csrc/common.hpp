@@ -40,6 +40,18 @@ struct PrefillArgs {
   int decide;        // 0: no threshold at all (every live block kept, no vote)
 };
 
+// Arguments of the prefill backward kernels (bf16 inputs, head dim 128, 128 x 128 tile-blocks).
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dout;   // bf16 (o: bf16 or fp32, o_f32)
+  const float *lse;                   // forward LSE [B][Hq][Lq] (natural log, softmax scale included)
+  const uint8_t *mask;                // forward skip mask [B][Hq][nqt][nkb]; null: every live block kept
+  void *dq, *dk, *dv;                 // gradients, bf16 or fp32 (out_f32)
+  float *dvec;                        // [B][Hq][Lq] rowsum(dO * O), written by the dQ kernel
+  int64_t qs[3], ks[3], vs[3], os[3], dos[3], dqs[3], dks[3], dvs[3];  // element strides
+  int B, Lq, Lk, Hq, Hkv, G, nqt, nkb, causal, out_f32, o_f32;
+  float scale, scale_log2;
+};
+
 // Arguments of the paged decode kernels.
 struct DecodeArgs {
   const void *q, *kc, *vc;

@@ -1,0 +1,487 @@
+// BLASST prefill backward: gradients of the sparse prefill with the forward's decisions held fixed.
+//
+// Method: sparsity-aware training runs the BLASST forward and lets the skipped blocks receive no
+// gradient (pages: xllm-io review, 训练流程 / 稀疏感知训练).  The backward differentiates what the
+// forward evaluated: for each query row, softmax attention over the visible keys of the blocks its
+// tile kept.  With P = exp(scale * Q K^T - LSE) on those (row, key) pairs and D_i = sum_d dO_id O_id:
+//     dV = P^T dO,   dP = dO V^T,   dS = scale * P * (dP - D),   dQ = dS K,   dK = dS^T Q,
+// and a tile-block that the forward skipped (or that is not live) adds nothing to any of them.
+//
+// MI355X design (head dim 128, 128 x 128 tile-blocks, bf16 inputs, v_mfma_f32_32x32x16_bf16
+// throughout, with the operand arrangement of the forward kernel: products are taken in the
+// orientation that lets probabilities go from accumulator registers straight into the B operand of
+// the next product, and the one transposed operand of each product is read with the gfx950 transpose
+// read ds_read_b64_tr_b16 from a row-major LDS tile):
+//   * dQ kernel: one workgroup per (TPW q heads of a GQA group, query tile), 4 waves of 32 rows per
+//     tile; the rows' Q and dO stay in registers; K and V blocks go global -> LDS with direct loads
+//     into double-buffered tiles, one barrier per block, and only blocks that a tile of the workgroup
+//     kept are staged at all.  Per kept block: S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.  It
+//     also forms D from dO and O and stores it for the second kernel;
+//   * dK/dV kernel: one workgroup per (kv head, key block), 4 waves of 32 keys whose K and V rows stay
+//     in registers; it walks the (q head of the group, query tile) pairs whose forward decision for
+//     this block was "keep", staging their Q and dO tiles double-buffered; per pair and 32-row slice:
+//     S = Q K^T, dP = dO V^T, P, dS, then dV^T += dO^T P and dK^T += Q^T dS.  The q heads of the group
+//     accumulate in the same registers, so no atomics and no reduction pass are needed;
+//   * a skipped tile-block costs nothing at all (no staging, no product; the forward's QK^T is not
+//     repeated), so the backward's work follows the kept fraction;
+//   * which blocks (pairs) are kept is read 64 at a time: every lane reads one mask byte and a wave
+//     ballot gives a 64-bit word that the loop walks with count-trailing-zeros.
+#include "common.hpp"
+
+namespace blasst {
+
+namespace {
+typedef __attribute__((ext_vector_type(4))) short bv4i16;
+typedef __attribute__((address_space(3))) bv4i16 lds_bv4i16;
+
+constexpr int BD = 128;               // head dim of q, k and v
+constexpr int BB = 128;               // rows of a query tile = keys of a key block
+constexpr int ROWB = 272;             // LDS bytes per staged row: 256 + 16 (16 mod 256)
+constexpr int CPR = ROWB / 16;        // 16-byte positions per row (the 17th re-reads chunk 0)
+constexpr int TINS = BB * CPR / 64;   // wave-wide direct loads per tile (2176 positions = 34 x 64)
+constexpr int TILEB = TINS * 1024;    // bytes per staged tile
+
+// Direct global -> LDS loads of one 128-row x 128-element bf16 tile (rows row0 ... row0 + 127 of a
+// row-major matrix with `stride` elements per row) into an LDS tile of ROWB-byte rows.  Wave `wave`
+// of `nw` issues instructions wave, wave + nw, ...; rows at or past `nrows` re-read row nrows - 1,
+// so every lane reads valid memory.
+__device__ __forceinline__ void stage_tile(const __bf16 *base, int64_t stride, int row0, int nrows,
+                                           unsigned char *dst, int wave, int nw, int lane) {
+  for (int ins = wave; ins < TINS; ins += nw) {
+    const int p = ins * 64 + lane;
+    const int row = p / CPR;
+    int c = p - row * CPR;
+    if (c >= 16) c = 0;
+    const int src = min(row0 + row, nrows - 1);
+    direct_load16(base + (int64_t)src * stride + c * 8, lds_addr(dst + ins * 1024));
+  }
+}
+
+// Transpose read of one k-step (16 rows of the tile) for an A operand X^T, X row-major in LDS:
+// output lane l holds column 32 mv + l % 32 of X and the 8 rows of its lane half in the order of the
+// B operand taken from accumulator registers 8 (ks % 2) ... + 7 of m-tile ks / 2.
+__device__ __forceinline__ bf16x8 tr_operand(const unsigned char *t, int ks, int mv) {
+  const bv4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bv4i16 *)(t + ks * 16 * ROWB + mv * 64));
+  const bv4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bv4i16 *)(t + (ks * 16 + 8) * ROWB + mv * 64));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Byte offset of a lane's transpose reads inside a tile (16-lane group G, lane j of it: row
+// 4 (G / 2) + j / 4, columns 16 (G % 2) + 4 (j % 4) ... + 3).
+__device__ __forceinline__ int tr_lane_offset(int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  return ((g >> 1) * 4 + (j >> 2)) * ROWB + (16 * (g & 1) + 4 * (j & 3)) * 2;
+}
+
+template <bool OUT_F32>
+__device__ __forceinline__ void store4(void *base, int64_t idx, float x0, float x1, float x2, float x3) {
+  if (OUT_F32) {
+    f32x4 w = {x0, x1, x2, x3};
+    *(f32x4 *)((float *)base + idx) = w;
+  } else {
+    u32x2 w;
+    w[0] = pack_bf16x2(x0, x1);
+    w[1] = pack_bf16x2(x2, x3);
+    *(u32x2 *)((__bf16 *)base + idx) = w;
+  }
+}
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+// dQ (and D)
+// ---------------------------------------------------------------------------------------------
+template <int TPW, bool OUT_F32>
+__global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a) {
+  constexpr int NW = 4 * TPW;    // waves per workgroup
+  constexpr int KS = BD / 16;    // k-steps over the head dim
+  constexpr int MT = BB / 32;    // key m-tiles of a block
+  constexpr int MV = BD / 32;    // dim m-tiles of dQ^T
+  __shared__ __attribute__((aligned(16))) unsigned char sK[2][TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char sV[2][TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = wave >> 2;
+  const int wit = wave & 3;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // heavy causal tiles first; TPW heads of one kv head share the staged K/V blocks
+  const int groups = a.Hq / TPW;
+  const int per_level = a.B * groups;
+  const int level = blockIdx.x / per_level;
+  const int rem = blockIdx.x - level * per_level;
+  const int qt = a.causal ? (a.nqt - 1 - level) : level;
+  const int b = rem / groups;
+  const int hq0 = (rem - b * groups) * TPW;
+  const int hq = hq0 + tile;
+  const int g = hq0 / a.G;
+  const int r0 = qt * BB;
+  const int off = a.Lk - a.Lq;
+  const int last_row = min(r0 + BB, a.Lq) - 1;
+  int J = a.nkb;
+  if (a.causal) {
+    const int lim = last_row + off;
+    J = lim < 0 ? 0 : min(a.nkb, lim / BB + 1);
+  }
+
+  const __bf16 *qp = (const __bf16 *)a.q + b * a.qs[0] + hq * a.qs[1];
+  const __bf16 *dop = (const __bf16 *)a.dout + b * a.dos[0] + hq * a.dos[1];
+  const int64_t obase = b * a.os[0] + hq * a.os[1];
+  const __bf16 *kp = (const __bf16 *)a.k + b * a.ks[0] + g * a.ks[1];
+  const __bf16 *vp = (const __bf16 *)a.v + b * a.vs[0] + g * a.vs[1];
+
+  // ---- this lane's query row: Q and dO fragments (B operands), D = dO . O, LSE ----
+  const int my_row = r0 + wit * 32 + l32;
+  const bool row_ok = my_row < a.Lq;
+  bf16x8 qf[KS], df[KS];
+  float dsum = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const int c = kk * 16 + hi * 8;
+    qf[kk] = row_ok ? *(const bf16x8 *)(qp + (int64_t)my_row * a.qs[2] + c) : bf16x8{};
+    df[kk] = row_ok ? *(const bf16x8 *)(dop + (int64_t)my_row * a.dos[2] + c) : bf16x8{};
+    float of[8] = {};
+    if (row_ok) {
+      const int64_t oi = obase + (int64_t)my_row * a.os[2] + c;
+      if (a.o_f32) {
+        const f32x4 lo = *(const f32x4 *)((const float *)a.o + oi);
+        const f32x4 up = *(const f32x4 *)((const float *)a.o + oi + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          of[e] = lo[e];
+          of[e + 4] = up[e];
+        }
+      } else {
+        const bf16x8 ob = *(const bf16x8 *)((const __bf16 *)a.o + oi);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) of[e] = (float)ob[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf((float)df[kk][e], of[e], dsum);
+  }
+  dsum += __shfl_xor(dsum, 32);
+  const int64_t row_idx = ((int64_t)b * a.Hq + hq) * a.Lq + my_row;
+  const float lse = row_ok ? a.lse[row_idx] : kNegInf;
+  // a row without any kept key (LSE = -inf) and a row past the end get P = 0
+  const float lse_l2 = lse == kNegInf ? __builtin_huge_valf() : lse * kLog2e;
+  if (row_ok && hi == 0) a.dvec[row_idx] = dsum;
+
+  // ---- kept blocks, 64 per word: bit of block base + x = tile keeps block base + x ----
+  const uint8_t *mrow = a.mask ? a.mask + (((int64_t)b * a.Hq + hq0) * a.nqt + qt) * a.nkb : nullptr;
+  const int64_t mtile = (int64_t)a.nqt * a.nkb;   // distance between the mask rows of two heads
+  uint64_t w0 = 0, w1 = 0;
+  int wbase = -64;
+  auto fetch = [&](int base) {
+    wbase = base;
+    const int j = base + lane;
+    bool k0 = j < J, k1 = j < J;
+    if (mrow) {
+      k0 = k0 && mrow[j] == kKept;
+      if (TPW == 2) k1 = k1 && mrow[mtile + j] == kKept;
+    }
+    w0 = __ballot(k0);
+    w1 = TPW == 2 ? __ballot(k1) : 0ull;
+  };
+  auto next = [&](int from) -> int {   // first block >= from that some tile keeps, or J
+    while (from < J) {
+      if (from < wbase || from >= wbase + 64) fetch(from & ~63);
+      const uint64_t w = (w0 | w1) >> (from - wbase);
+      if (w) return from + (int)__builtin_ctzll(w);
+      from = wbase + 64;
+    }
+    return J;
+  };
+  auto mine = [&](int j) -> bool { return (((tile ? w1 : w0) >> (j - wbase)) & 1ull) != 0ull; };
+  auto stage = [&](int j, int buf) {
+    stage_tile(kp, a.ks[2], j * BB, a.Lk, sK[buf], wave, NW, lane);
+    stage_tile(vp, a.vs[2], j * BB, a.Lk, sV[buf], wave, NW, lane);
+  };
+
+  const int tr_off = tr_lane_offset(lane);
+  f32x16 dq_acc[MV];
+#pragma unroll
+  for (int i = 0; i < MV; ++i) dq_acc[i] = f32x16{};
+
+  int jc = next(0);
+  bool keep_c = jc < J && mine(jc);
+  if (jc < J) stage(jc, 0);
+  int buf = 0;
+  while (jc < J) {
+    const int jn = next(jc + 1);
+    const bool keep_n = jn < J && mine(jn);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block jc has landed in LDS
+    __syncthreads();                                   // ... for every wave; buffer buf ^ 1 is free
+    if (jn < J) stage(jn, buf ^ 1);
+    if (keep_c) {
+      const unsigned char *kb = sK[buf] + l32 * ROWB + hi * 16;
+      const unsigned char *vb = sV[buf] + l32 * ROWB + hi * 16;
+      const unsigned char *kt = sK[buf] + tr_off;
+      const int key0 = jc * BB;
+      const bool need_mask = (key0 + BB > a.Lk) || (a.causal && key0 + BB - 1 > r0 + off);
+      const int lim = a.causal ? min(my_row + off, a.Lk - 1) : a.Lk - 1;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const bf16x8 kf = *(const bf16x8 *)(kb + mt * 32 * ROWB + kk * 32);
+          const bf16x8 vf = *(const bf16x8 *)(vb + mt * 32 * ROWB + kk * 32);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[kk], dp, 0, 0, 0);
+        }
+        if (need_mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + mt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key > lim) s[r] = kNegInf;
+          }
+        }
+        // dS^T = scale * P^T (dP^T - D), packed as the B operand of the two k-steps over these keys
+        bf16x8 dsf[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -lse_l2));
+          dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dsum) * a.scale);
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int mv = 0; mv < MV; ++mv)
+            dq_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kt, 2 * mt + k2, mv), dsf[k2],
+                                                                 dq_acc[mv], 0, 0, 0);
+      }
+    }
+    buf ^= 1;
+    jc = jn;
+    keep_c = keep_n;
+  }
+
+  // ---- dQ: lane holds row my_row, dims 32 mv + 8 q + 4 hi ... + 3 in dq_acc[mv][4 q ... 4 q + 3] ----
+  if (row_ok) {
+    const int64_t base = b * a.dqs[0] + hq * a.dqs[1] + (int64_t)my_row * a.dqs[2];
+#pragma unroll
+    for (int mv = 0; mv < MV; ++mv)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        store4<OUT_F32>(a.dq, base + 32 * mv + 8 * q4 + 4 * hi, dq_acc[mv][4 * q4], dq_acc[mv][4 * q4 + 1],
+                        dq_acc[mv][4 * q4 + 2], dq_acc[mv][4 * q4 + 3]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dK and dV
+// ---------------------------------------------------------------------------------------------
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void prefill_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NW = 4;
+  constexpr int KS = BD / 16;
+  constexpr int MT = BB / 32;    // 32-row slices of a query tile
+  constexpr int MV = BD / 32;
+  __shared__ __attribute__((aligned(16))) unsigned char sQ[2][TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char sO[2][TILEB];   // dO tiles
+  __shared__ __attribute__((aligned(16))) float sL[2][BB];              // LSE * log2(e) of the tile's rows
+  __shared__ __attribute__((aligned(16))) float sD[2][BB];              // D of the tile's rows
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // key blocks with the most causal query tiles first
+  const int per_level = a.B * a.Hkv;
+  const int j = blockIdx.x / per_level;
+  const int rem = blockIdx.x - j * per_level;
+  const int b = rem / a.Hkv;
+  const int g = rem - b * a.Hkv;
+  const int key0 = j * BB;
+  const int off = a.Lk - a.Lq;
+  const int my_key = key0 + wave * 32 + l32;
+  const bool key_ok = my_key < a.Lk;
+
+  const __bf16 *kp = (const __bf16 *)a.k + b * a.ks[0] + g * a.ks[1];
+  const __bf16 *vp = (const __bf16 *)a.v + b * a.vs[0] + g * a.vs[1];
+
+  // ---- this lane's key: K and V fragments (B operands of S = Q K^T and dP = dO V^T) ----
+  bf16x8 kf[KS], vf[KS];
+  {
+    const int key = min(my_key, a.Lk - 1);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      kf[kk] = *(const bf16x8 *)(kp + (int64_t)key * a.ks[2] + kk * 16 + hi * 8);
+      vf[kk] = *(const bf16x8 *)(vp + (int64_t)key * a.vs[2] + kk * 16 + hi * 8);
+    }
+  }
+
+  // ---- (q head of the group, query tile) pairs p = h * nqt + t that kept this block ----
+  const int npairs = a.G * a.nqt;
+  auto live = [&](int t) -> bool {
+    if (!a.causal) return true;
+    const int lim = min(t * BB + BB, a.Lq) - 1 + off;
+    return lim >= key0;
+  };
+  uint64_t word = 0;
+  int wbase = -64;
+  auto fetch = [&](int base) {
+    wbase = base;
+    const int p = base + lane;
+    bool k = false;
+    if (p < npairs) {
+      const int h = p / a.nqt, t = p - (p / a.nqt) * a.nqt;
+      k = live(t);
+      if (a.mask && k) k = a.mask[(((int64_t)b * a.Hq + g * a.G + h) * a.nqt + t) * a.nkb + j] == kKept;
+    }
+    word = __ballot(k);
+  };
+  auto next = [&](int from) -> int {
+    while (from < npairs) {
+      if (from < wbase || from >= wbase + 64) fetch(from & ~63);
+      const uint64_t w = word >> (from - wbase);
+      if (w) return from + (int)__builtin_ctzll(w);
+      from = wbase + 64;
+    }
+    return npairs;
+  };
+  // LSE and D of a pair's rows travel through registers (thread t < 128: LSE of row t, else D of
+  // row t - 128), so rows past the end and rows without any kept key can be given P = 0 exactly
+  auto load_ld = [&](int p) -> float {
+    const int h = p / a.nqt, t = p - (p / a.nqt) * a.nqt;
+    const int row = t * BB + (tid & (BB - 1));
+    const int64_t idx = ((int64_t)b * a.Hq + g * a.G + h) * a.Lq + row;
+    if (tid < BB) {
+      const float l = row < a.Lq ? a.lse[idx] : kNegInf;
+      return l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+    }
+    return row < a.Lq ? a.dvec[idx] : 0.f;
+  };
+  auto store_ld = [&](int buf, float x) {
+    if (tid < BB) sL[buf][tid] = x;
+    else sD[buf][tid - BB] = x;
+  };
+  auto stage = [&](int p, int buf) {
+    const int h = p / a.nqt, t = p - (p / a.nqt) * a.nqt;
+    const int hq = g * a.G + h;
+    stage_tile((const __bf16 *)a.q + b * a.qs[0] + hq * a.qs[1], a.qs[2], t * BB, a.Lq, sQ[buf], wave, NW, lane);
+    stage_tile((const __bf16 *)a.dout + b * a.dos[0] + hq * a.dos[1], a.dos[2], t * BB, a.Lq, sO[buf], wave, NW,
+               lane);
+  };
+
+  const int tr_off = tr_lane_offset(lane);
+  f32x16 dv_acc[MV], dk_acc[MV];
+#pragma unroll
+  for (int i = 0; i < MV; ++i) {
+    dv_acc[i] = f32x16{};
+    dk_acc[i] = f32x16{};
+  }
+
+  int pc = next(0);
+  if (pc < npairs) {
+    stage(pc, 0);
+    store_ld(0, load_ld(pc));
+  }
+  int buf = 0;
+  while (pc < npairs) {
+    const int pn = next(pc + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // pair pc's tiles have landed in LDS
+    __syncthreads();                                   // ... for every wave; buffer buf ^ 1 is free
+    float ld_next = 0.f;
+    if (pn < npairs) {
+      stage(pn, buf ^ 1);
+      ld_next = load_ld(pn);
+    }
+    {
+      const int t = pc - (pc / a.nqt) * a.nqt;
+      const int row0 = t * BB;
+      const bool need_mask = a.causal && (key0 + BB - 1 > row0 + off);
+      const unsigned char *qb = sQ[buf] + l32 * ROWB + hi * 16;
+      const unsigned char *ob = sO[buf] + l32 * ROWB + hi * 16;
+      const unsigned char *qtr = sQ[buf] + tr_off;
+      const unsigned char *otr = sO[buf] + tr_off;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const bf16x8 qa = *(const bf16x8 *)(qb + mt * 32 * ROWB + kk * 32);
+          const bf16x8 oa = *(const bf16x8 *)(ob + mt * 32 * ROWB + kk * 32);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], dp, 0, 0, 0);
+        }
+        // lane holds key my_key and rows row0 + 32 mt + 8 (r / 4) + 4 hi + r % 4
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int rr = mt * 32 + 8 * q4 + 4 * hi;
+          const f32x4 l4 = *(const f32x4 *)&sL[buf][rr];
+          const f32x4 d4 = *(const f32x4 *)&sD[buf][rr];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q4 + e;
+            float p = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -l4[e]));
+            if (need_mask && my_key > row0 + rr + e + off) p = 0.f;
+            pf[r >> 3][r & 7] = (__bf16)p;
+            dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - d4[e]) * a.scale);
+          }
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int mv = 0; mv < MV; ++mv) {
+            dv_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(otr, 2 * mt + k2, mv), pf[k2],
+                                                                 dv_acc[mv], 0, 0, 0);
+            dk_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qtr, 2 * mt + k2, mv), dsf[k2],
+                                                                 dk_acc[mv], 0, 0, 0);
+          }
+      }
+    }
+    if (pn < npairs) store_ld(buf ^ 1, ld_next);
+    buf ^= 1;
+    pc = pn;
+  }
+
+  // ---- dK, dV: lane holds key my_key, dims 32 mv + 8 q + 4 hi ... + 3 in acc[mv][4 q ... 4 q + 3] ----
+  if (key_ok) {
+    const int64_t kb = b * a.dks[0] + g * a.dks[1] + (int64_t)my_key * a.dks[2];
+    const int64_t vb = b * a.dvs[0] + g * a.dvs[1] + (int64_t)my_key * a.dvs[2];
+#pragma unroll
+    for (int mv = 0; mv < MV; ++mv)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * mv + 8 * q4 + 4 * hi;
+        store4<OUT_F32>(a.dk, kb + d0, dk_acc[mv][4 * q4], dk_acc[mv][4 * q4 + 1], dk_acc[mv][4 * q4 + 2],
+                        dk_acc[mv][4 * q4 + 3]);
+        store4<OUT_F32>(a.dv, vb + d0, dv_acc[mv][4 * q4], dv_acc[mv][4 * q4 + 1], dv_acc[mv][4 * q4 + 2],
+                        dv_acc[mv][4 * q4 + 3]);
+      }
+  }
+}
+
+template <int TPW>
+static void launch_dq(const BwdArgs &a, hipStream_t st) {
+  const int grid = a.B * (a.Hq / TPW) * a.nqt;
+  if (a.out_f32)
+    hipLaunchKernelGGL((prefill_bwd_dq_kernel<TPW, true>), dim3(grid), dim3(256 * TPW), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_bwd_dq_kernel<TPW, false>), dim3(grid), dim3(256 * TPW), 0, st, a);
+}
+
+// The dQ kernel runs first: it writes D, which the dK/dV kernel reads (same stream).
+hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t st) {
+  if (a.G % 2 == 0)
+    launch_dq<2>(a, st);
+  else
+    launch_dq<1>(a, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int grid = a.B * a.Hkv * a.nkb;
+  if (a.out_f32)
+    hipLaunchKernelGGL((prefill_bwd_dkdv_kernel<true>), dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_bwd_dkdv_kernel<false>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace blasst

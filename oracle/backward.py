@@ -70,3 +70,27 @@ def prefill_backward(q, k, v, do, mask, *, causal: bool, block_q: int, block_k: 
     dq, dk, dv = torch.autograd.grad(o, (q, k, v), grad_outputs=do)
     return {"dq": dq.numpy(), "dk": dk.numpy(), "dv": dv.numpy(), "o": o.detach().numpy(),
             "lse": lse.detach().numpy()}
+
+
+def dq_rows(q, k, v, do, mask, b: int, h: int, rows, *, causal: bool, block_q: int, block_k: int, scale=None):
+    """dQ of the given query rows of (sequence b, q head h) only, by the same closed form and autograd
+    (each row's output depends on its own query only, so its dQ needs no other row): cheap at any L.
+    Returns [len(rows), D]."""
+    rows = np.asarray(rows)
+    q = np.asarray(q)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = np.asarray(k).shape[1], np.asarray(k).shape[2]
+    g = h // (Hq // Hkv)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    mask = np.asarray(mask)
+    kept = mask[b, h][rows // block_q][:, np.arange(Lk) // block_k] == KEPT          # [R, Lk]
+    if causal:
+        kept = kept & causal_visible(rows, Lk, Lq, Lk)
+    qr = torch.as_tensor(np.asarray(q[b, h, rows], dtype=np.float64))[None, None].clone().requires_grad_(True)
+    kk = torch.as_tensor(np.asarray(np.asarray(k)[b, g], dtype=np.float64))[None, None]
+    vv = torch.as_tensor(np.asarray(np.asarray(v)[b, g], dtype=np.float64))[None, None]
+    dd = torch.as_tensor(np.asarray(np.asarray(do)[b, h, rows], dtype=np.float64))[None, None]
+    o, _ = attention_on_kept(qr, kk, vv, torch.as_tensor(kept)[None, None], scale)
+    (dq,) = torch.autograd.grad(o, (qr,), grad_outputs=dd)
+    return dq[0, 0].numpy()

@@ -43,6 +43,7 @@ def test_struct_layout_matches_binding(m):
     lib = m.lib()
     assert lib.blasst_prefill_params_size() == ctypes.sizeof(m.blasst.PrefillParams)
     assert lib.blasst_decode_params_size() == ctypes.sizeof(m.blasst.DecodeParams)
+    assert lib.blasst_prefill_backward_params_size() == ctypes.sizeof(m.blasst.BackwardParams)
     assert lib.blasst_version() >= 10000
 
 
@@ -162,3 +163,46 @@ def test_calibration_matches_oracle(m):
     assert m.blasst_lambda_for(a1, b1, 0.5, 8192) == pytest.approx(oracle.lambda_for(a2, b2, 0.5, 8192), rel=1e-12)
     with pytest.raises(m.BlasstError):
         m.blasst_calibrate([1, 2], [0.5, 0.5], [0.1, 0.1])
+
+
+def _backward(**over):
+    from long_context_online_amd.blasst import BackwardParams
+    p = BackwardParams()
+    p.struct_size = ctypes.sizeof(BackwardParams)
+    p.q = p.k = p.v = p.o = p.dout = p.lse = p.dq = p.dk = p.dv = FAKE
+    st = [32 * 4096 * 128, 4096 * 128, 128]
+    for name in ("q_stride", "k_stride", "v_stride", "o_stride", "dout_stride", "dq_stride", "dk_stride",
+                 "dv_stride"):
+        getattr(p, name)[:] = st
+    p.in_dtype, p.grad_dtype, p.o_dtype = 0, 1, 0
+    p.batch, p.seqlen_q, p.seqlen_k, p.num_q_heads, p.num_kv_heads = 1, 4096, 4096, 32, 8
+    p.head_dim_qk = p.head_dim_v = 128
+    p.causal, p.block_q, p.block_k = 1, 128, 128
+    for k, v in over.items():
+        setattr(p, k, v)
+    return p
+
+
+BACKWARD_BAD = [
+    ({"q": None}, 1), ({"lse": None}, 1), ({"dv": None}, 1), ({"num_kv_heads": 5}, 1), ({"seqlen_q": 0}, 1),
+    ({"grad_dtype": 7}, 1), ({"o_dtype": 3}, 1), ({"causal": 2}, 1), ({"struct_size": 8}, 1), ({"softmax_scale": float("nan")}, 1),
+    ({"in_dtype": 1}, 2), ({"head_dim_qk": 64, "head_dim_v": 64}, 2), ({"block_q": 64, "block_k": 64}, 2),
+    ({"dq": FAKE + 8}, 2),
+    ({}, 4),   # no workspace
+]
+
+
+@pytest.mark.parametrize("over,status", BACKWARD_BAD, ids=[str(x[0]) for x in BACKWARD_BAD])
+def test_backward_rejects_invalid_arguments(m, over, status):
+    lib = m.lib()
+    p = _backward(**over)
+    assert lib.blasst_prefill_backward(ctypes.byref(p), None) == status
+    assert lib.blasst_last_error()
+
+
+def test_backward_workspace_size(m):
+    lib = m.lib()
+    assert lib.blasst_prefill_backward_workspace_size(ctypes.byref(_backward())) == 32 * 4096 * 4
+    odd = _backward(seqlen_q=1000, seqlen_k=1000)
+    assert lib.blasst_prefill_backward_workspace_size(ctypes.byref(odd)) == (32 * 1000 * 4 + 255) // 256 * 256
+    assert lib.blasst_prefill_backward_workspace_size(ctypes.byref(_backward(num_kv_heads=5))) == 0

@@ -127,3 +127,14 @@ def test_gqa_gradient_is_mha_with_repeated_kv_summed():
     assert np.max(np.abs(g["dq"] - m["dq"])) < 1e-13
     assert np.max(np.abs(g["dk"] - m["dk"].reshape(1, 2, 2, 12, 4).sum(axis=2))) < 1e-13
     assert np.max(np.abs(g["dv"] - m["dv"].reshape(1, 2, 2, 12, 3).sum(axis=2))) < 1e-13
+
+
+def test_dq_rows_is_the_full_backward_restricted_to_those_rows():
+    rng = np.random.default_rng(17)
+    q, k, v, do = _problem(rng, B=2, Hq=4, Hkv=2, Lq=20, Lk=24, D=4, Dv=3)
+    mask = oracle.prefill(q, k, v, causal=True, block_q=4, block_k=8, lam=0.4, scale=0.6)["mask"]
+    g = bw.prefill_backward(q, k, v, do, mask, causal=True, block_q=4, block_k=8, scale=0.6)
+    rows = np.array([0, 3, 7, 19, 12])
+    for b, h in ((0, 1), (1, 3)):
+        got = bw.dq_rows(q, k, v, do, mask, b, h, rows, causal=True, block_q=4, block_k=8, scale=0.6)
+        assert np.max(np.abs(got - g["dq"][b, h, rows])) < 1e-13
