@@ -320,6 +320,43 @@ class Decode:
         return r
 
 
+def backward_measure(m, torch, pre, lam, steps):
+    """The backward of the bench prefill (sparsity-aware training): gradients with the forward's
+    skip mask at the calibrated lambda against the dense backward (no mask), bf16 gradients, the
+    forward's output in bf16.  Dense-equivalent FLOPs follow the usual count for attention backward,
+    five products of the forward's size (QK^T recomputed, dP, dV, dQ, dK); the kernels issue seven
+    (the dQ kernel recomputes QK^T and dP) on the kept tile-blocks only."""
+    inp = pre.inp
+    B, Hq, L, D = inp.q.shape
+    mask = torch.empty(B, Hq, pre.nqt, pre.nkb, dtype=torch.uint8, device="cuda")
+    pre.run(lam, skip_mask=mask)
+    g = torch.Generator(device="cuda").manual_seed(4321)
+    dout = torch.randn(pre.o.shape, generator=g, device="cuda").to(torch.bfloat16)
+    dq, dk, dv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
+    args = (inp.q, inp.k, inp.v, pre.o, dout, pre.lse, dq, dk, dv)
+    n = m.blasst_prefill_backward_workspace_size(*args, causal=True)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+
+    def run(mk):
+        m.blasst_prefill_backward(*args, causal=True, skip_mask=mk, workspace=ws)
+
+    run(mask)
+    run(None)
+    sparse_ms = timed(torch, lambda: run(mask), steps)
+    dense_ms = timed(torch, lambda: run(None), steps)
+    torch.cuda.synchronize()
+    mh = mask.cpu().numpy()
+    live, kept = int((mh != 2).sum()), int((mh == 0).sum())
+    dense_flops = 2.5 * pre.dense_flops
+    issued = 7 * 2.0 * P_BLK * P_BLK * P_D * kept
+    return {"ms": round(sparse_ms, 4), "dense_ms": round(dense_ms, 4), "speedup_vs_dense": round(dense_ms / sparse_ms, 3),
+            "sparsity": round(1 - kept / live, 4), "lambda": lam,
+            "dense_equiv_tflops": round(dense_flops / (sparse_ms * 1e-3) / 1e12, 2),
+            "dense_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
+            "issued_tflops": round(issued / (sparse_ms * 1e-3) / 1e12, 2),
+            "workload": "the bench prefill's backward: dQ, dK, dV (bf16) from bf16 O and dO, forward skip mask"}
+
+
 def head_heterogeneity(m, torch, synth, pre, lam_p, steps):
     """Per-head sparsity under one threshold: the bench workload (heads alike) and the same shape
     with heads of different peakedness (head strengths spread geometrically over 0.25 ... 2, in a
@@ -536,6 +573,7 @@ def main():
             result["prefill_s050"]["target_sparsity"] = 0.5
             result["prefill_decision_overhead"] = pre.decision_overhead(max(3, args.steps // 2))
             result["prefill_heads"] = head_heterogeneity(m, torch, synth, pre, lam_p, max(3, args.steps // 2))
+            result["prefill_backward"] = backward_measure(m, torch, pre, lam_p, max(3, args.steps // 2))
     if dec:
         r = dec.measure(lam_d, args.steps, ms=dec_ms)
         r.update({"target_sparsity": M_TARGETS[-1] if dec.latent else D_TARGET,

@@ -400,16 +400,31 @@ __global__ __launch_bounds__(256, 1) void prefill_bwd_dkdv_kernel(BwdArgs a) {
       const unsigned char *ob = sO[buf] + l32 * ROWB + hi * 16;
       const unsigned char *qtr = sQ[buf] + tr_off;
       const unsigned char *otr = sO[buf] + tr_off;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+      // S and dP of a 32-row slice: A operands (Q and dO rows) read one k-step ahead of their MFMAs
+      auto sdp = [&](int mt, f32x16 &s, f32x16 &dp) {
+        bf16x8 qa[2], oa[2];
+        qa[0] = *(const bf16x8 *)(qb + mt * 32 * ROWB);
+        oa[0] = *(const bf16x8 *)(ob + mt * 32 * ROWB);
+        s = f32x16{};
+        dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-          const bf16x8 qa = *(const bf16x8 *)(qb + mt * 32 * ROWB + kk * 32);
-          const bf16x8 oa = *(const bf16x8 *)(ob + mt * 32 * ROWB + kk * 32);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], dp, 0, 0, 0);
+          if (kk + 1 < KS) {
+            qa[(kk + 1) & 1] = *(const bf16x8 *)(qb + mt * 32 * ROWB + (kk + 1) * 32);
+            oa[(kk + 1) & 1] = *(const bf16x8 *)(ob + mt * 32 * ROWB + (kk + 1) * 32);
+          }
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk & 1], kf[kk], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[kk & 1], vf[kk], dp, 0, 0, 0);
         }
+      };
+      // The slices are software-pipelined: the MFMAs of slice mt + 1's S and dP are issued before
+      // slice mt's exp / dS arithmetic, which then runs while they execute.
+      f32x16 s_cur, dp_cur;
+      sdp(0, s_cur, dp_cur);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x16 s_nxt = f32x16{}, dp_nxt = f32x16{};
+        if (mt + 1 < MT) sdp(mt + 1, s_nxt, dp_nxt);
         // lane holds key my_key and rows row0 + 32 mt + 8 (r / 4) + 4 hi + r % 4
         bf16x8 pf[2], dsf[2];
 #pragma unroll
@@ -420,27 +435,37 @@ __global__ __launch_bounds__(256, 1) void prefill_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * q4 + e;
-            float p = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -l4[e]));
+            float p = fast_exp2(__builtin_fmaf(s_cur[r], a.scale_log2, -l4[e]));
             if (need_mask && my_key > row0 + rr + e + off) p = 0.f;
             pf[r >> 3][r & 7] = (__bf16)p;
-            dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - d4[e]) * a.scale);
+            dsf[r >> 3][r & 7] = (__bf16)(p * (dp_cur[r] - d4[e]) * a.scale);
           }
         }
+        // dV^T += dO^T P and dK^T += Q^T dS over the slice's rows; transpose reads one MFMA pair ahead
+        bf16x8 ot = tr_operand(otr, 2 * mt, 0), qt = tr_operand(qtr, 2 * mt, 0);
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-          for (int mv = 0; mv < MV; ++mv) {
-            dv_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(otr, 2 * mt + k2, mv), pf[k2],
-                                                                 dv_acc[mv], 0, 0, 0);
-            dk_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qtr, 2 * mt + k2, mv), dsf[k2],
-                                                                 dk_acc[mv], 0, 0, 0);
+        for (int i = 0; i < 2 * MV; ++i) {
+          const int k2 = i / MV, mv = i % MV;
+          bf16x8 ot_n = ot, qt_n = qt;
+          if (i + 1 < 2 * MV) {
+            ot_n = tr_operand(otr, 2 * mt + (i + 1) / MV, (i + 1) % MV);
+            qt_n = tr_operand(qtr, 2 * mt + (i + 1) / MV, (i + 1) % MV);
           }
+          dv_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot, pf[k2], dv_acc[mv], 0, 0, 0);
+          dk_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsf[k2], dk_acc[mv], 0, 0, 0);
+          ot = ot_n;
+          qt = qt_n;
+        }
+        s_cur = s_nxt;
+        dp_cur = dp_nxt;
       }
     }
     if (pn < npairs) store_ld(buf ^ 1, ld_next);
     buf ^= 1;
     pc = pn;
   }
+
+
 
   // ---- dK, dV: lane holds key my_key, dims 32 mv + 8 q + 4 hi ... + 3 in acc[mv][4 q ... 4 q + 3] ----
   if (key_ok) {
