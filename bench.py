@@ -72,8 +72,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "mla"], default="all",
-                    help="restrict the timed step (for profiling runs)")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "mla", "backward"], default="all",
+                    help="restrict the timed step (for profiling runs; backward: the prefill's backward with "
+                         "the forward's skip mask at the calibrated lambda)")
     ap.add_argument("--quick", action="store_true",
                     help="only the timed step (no 128K decode, latent decode or calibration sweep)")
     ap.add_argument("--profile-only", action="store_true",
@@ -320,41 +321,46 @@ class Decode:
         return r
 
 
-def backward_measure(m, torch, pre, lam, steps):
+class Backward:
     """The backward of the bench prefill (sparsity-aware training): gradients with the forward's
-    skip mask at the calibrated lambda against the dense backward (no mask), bf16 gradients, the
-    forward's output in bf16.  Dense-equivalent FLOPs follow the usual count for attention backward,
-    five products of the forward's size (QK^T recomputed, dP, dV, dQ, dK); the kernels issue seven
-    (the dQ kernel recomputes QK^T and dP) on the kept tile-blocks only."""
-    inp = pre.inp
-    B, Hq, L, D = inp.q.shape
-    mask = torch.empty(B, Hq, pre.nqt, pre.nkb, dtype=torch.uint8, device="cuda")
-    pre.run(lam, skip_mask=mask)
-    g = torch.Generator(device="cuda").manual_seed(4321)
-    dout = torch.randn(pre.o.shape, generator=g, device="cuda").to(torch.bfloat16)
-    dq, dk, dv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
-    args = (inp.q, inp.k, inp.v, pre.o, dout, pre.lse, dq, dk, dv)
-    n = m.blasst_prefill_backward_workspace_size(*args, causal=True)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    skip mask at the given lambda, bf16 gradients, the forward's output in bf16.  Dense-equivalent
+    FLOPs follow the usual count for attention backward, five products of the forward's size (QK^T
+    recomputed, dP, dV, dQ, dK); the kernels issue seven (the dQ kernel recomputes QK^T and dP), on
+    the kept tile-blocks only."""
 
-    def run(mk):
-        m.blasst_prefill_backward(*args, causal=True, skip_mask=mk, workspace=ws)
+    def __init__(self, m, torch, pre, lam):
+        self.m, self.torch, self.pre, self.lam = m, torch, pre, lam
+        inp = pre.inp
+        B, Hq, L, D = inp.q.shape
+        self.mask = torch.empty(B, Hq, pre.nqt, pre.nkb, dtype=torch.uint8, device="cuda")
+        pre.run(lam, skip_mask=self.mask)
+        g = torch.Generator(device="cuda").manual_seed(4321)
+        self.dout = torch.randn(pre.o.shape, generator=g, device="cuda").to(torch.bfloat16)
+        self.grads = (torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v))
+        self.args = (inp.q, inp.k, inp.v, pre.o, self.dout, pre.lse) + self.grads
+        n = m.blasst_prefill_backward_workspace_size(*self.args, causal=True)
+        self.ws = torch.empty(n, dtype=torch.uint8, device="cuda")
 
-    run(mask)
-    run(None)
-    sparse_ms = timed(torch, lambda: run(mask), steps)
-    dense_ms = timed(torch, lambda: run(None), steps)
-    torch.cuda.synchronize()
-    mh = mask.cpu().numpy()
-    live, kept = int((mh != 2).sum()), int((mh == 0).sum())
-    dense_flops = 2.5 * pre.dense_flops
-    issued = 7 * 2.0 * P_BLK * P_BLK * P_D * kept
-    return {"ms": round(sparse_ms, 4), "dense_ms": round(dense_ms, 4), "speedup_vs_dense": round(dense_ms / sparse_ms, 3),
-            "sparsity": round(1 - kept / live, 4), "lambda": lam,
-            "dense_equiv_tflops": round(dense_flops / (sparse_ms * 1e-3) / 1e12, 2),
-            "dense_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
-            "issued_tflops": round(issued / (sparse_ms * 1e-3) / 1e12, 2),
-            "workload": "the bench prefill's backward: dQ, dK, dV (bf16) from bf16 O and dO, forward skip mask"}
+    def run(self, sparse=True):
+        self.m.blasst_prefill_backward(*self.args, causal=True, skip_mask=self.mask if sparse else None,
+                                       workspace=self.ws)
+
+    def measure(self, steps, ms=None):
+        torch = self.torch
+        self.run()
+        self.run(False)
+        sparse_ms = timed(torch, self.run, steps) if ms is None else ms
+        dense_ms = timed(torch, lambda: self.run(False), steps)
+        mh = self.mask.cpu().numpy()
+        live, kept = int((mh != 2).sum()), int((mh == 0).sum())
+        dense_flops = 2.5 * self.pre.dense_flops
+        issued = 7 * 2.0 * P_BLK * P_BLK * P_D * kept
+        return {"ms": round(sparse_ms, 4), "dense_ms": round(dense_ms, 4),
+                "speedup_vs_dense": round(dense_ms / sparse_ms, 3), "sparsity": round(1 - kept / live, 4),
+                "lambda": self.lam, "dense_equiv_tflops": round(dense_flops / (sparse_ms * 1e-3) / 1e12, 2),
+                "dense_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2),
+                "issued_tflops": round(issued / (sparse_ms * 1e-3) / 1e12, 2),
+                "workload": "the bench prefill's backward: dQ, dK, dV (bf16) from bf16 O and dO, forward skip mask"}
 
 
 def head_heterogeneity(m, torch, synth, pre, lam_p, steps):
@@ -490,6 +496,10 @@ def main():
         dec = Decode(m, torch, synth, ctx=M_CTX, latent=True)
     else:
         dec = Decode(m, torch, synth) if args.only in ("all", "decode") else None
+    bwd = None
+    if args.only == "backward":  # the prefill's backward as the timed step
+        base = Prefill(m, torch, synth)
+        bwd = Backward(m, torch, base, base.calibrate(P_TARGET))
     torch.cuda.synchronize()
 
     lam_p = pre.calibrate(P_TARGET) if pre else None
@@ -500,6 +510,8 @@ def main():
             pre.run(lam_p)
         if dec:
             dec.run(lam_d)
+        if bwd:
+            bwd.run()
 
     for _ in range(args.warmup):
         step()
@@ -518,6 +530,8 @@ def main():
         e[1].record()
         if dec:
             dec.run(lam_d)
+        if bwd:
+            bwd.run()
         e[2].record()
         ev.append(e)
     torch.cuda.synchronize()
@@ -531,7 +545,9 @@ def main():
             ref_dst.copy_(ref_src)
         torch.cuda.synchronize()
         print(json.dumps({"profile_only": True, "steps": args.steps, "warmup": args.warmup,
-                          "prefill_ms": round(pre_ms, 4) if pre else None, "decode_ms": round(dec_ms, 4) if dec else None,
+                          "prefill_ms": round(pre_ms, 4) if pre else None,
+                          "decode_ms": round(dec_ms, 4) if dec else None,
+                          "backward_ms": round(dec_ms, 4) if bwd else None,
                           "prefill_lambda": lam_p, "decode_lambda": lam_d,
                           "reference_copy_bytes": 2 * ref_src.numel() * ref_src.element_size()}))
         return
@@ -573,7 +589,9 @@ def main():
             result["prefill_s050"]["target_sparsity"] = 0.5
             result["prefill_decision_overhead"] = pre.decision_overhead(max(3, args.steps // 2))
             result["prefill_heads"] = head_heterogeneity(m, torch, synth, pre, lam_p, max(3, args.steps // 2))
-            result["prefill_backward"] = backward_measure(m, torch, pre, lam_p, max(3, args.steps // 2))
+            bw = Backward(m, torch, pre, lam_p)
+            result["prefill_backward"] = bw.measure(max(3, args.steps // 2))
+            del bw
     if dec:
         r = dec.measure(lam_d, args.steps, ms=dec_ms)
         r.update({"target_sparsity": M_TARGETS[-1] if dec.latent else D_TARGET,
@@ -591,7 +609,13 @@ def main():
         if not pre:
             result.update({"value": r["hbm_gbps"], "unit": "GB/s"})
             config["workload"] = r["workload"]
-    del pre, dec
+    if bwd:
+        r = bwd.measure(args.steps, ms=dec_ms)
+        r["timed_step_ms_p10_p50_p90"] = percentiles(dec_all)
+        result["prefill_backward"] = r
+        result.update({"value": r["dense_equiv_tflops"], "unit": "TFLOP/s (dense-equivalent, backward)"})
+        config["workload"] = r["workload"]
+    del pre, dec, bwd
     torch.cuda.empty_cache()
     if not args.quick and args.only == "all":
         d128 = Decode(m, torch, synth, ctx=131072, seed=synth.config_seed(3, 1))

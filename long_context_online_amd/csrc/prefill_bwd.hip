@@ -274,12 +274,22 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
 // ---------------------------------------------------------------------------------------------
 // dK and dV
 // ---------------------------------------------------------------------------------------------
+// Transpose read for the A operand of v_mfma_f32_16x16x32_bf16 over 32 tile rows (k-step ks) and 16
+// columns (tile mv) of a row-major LDS tile X: lane l (16-lane group q = l / 16) gets column
+// 16 mv + l % 16 and rows 32 ks + 4 q ... + 3 and 32 ks + 16 + 4 q ... + 3, the order in which the
+// C layout of two consecutive 16-row S slices holds them (so P and dS feed the B operand as they are).
+__device__ __forceinline__ bf16x8 tr_operand16(const unsigned char *t, int ks, int mv) {
+  const bv4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bv4i16 *)(t + ks * 32 * ROWB + mv * 32));
+  const bv4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bv4i16 *)(t + (ks * 32 + 16) * ROWB + mv * 32));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 template <bool OUT_F32>
-__global__ __launch_bounds__(256, 1) void prefill_bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int NW = 4;
-  constexpr int KS = BD / 16;
-  constexpr int MT = BB / 32;    // 32-row slices of a query tile
-  constexpr int MV = BD / 32;
+__global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NW = 8;          // 8 waves of 16 keys: two waves per SIMD
+  constexpr int KS = BD / 32;    // k-steps of 32 over the head dim
+  constexpr int NSL = BB / 16;   // 16-row slices of a query tile
+  constexpr int MV = BD / 16;    // 16-wide dim tiles of dK^T, dV^T
   __shared__ __attribute__((aligned(16))) unsigned char sQ[2][TILEB];
   __shared__ __attribute__((aligned(16))) unsigned char sO[2][TILEB];   // dO tiles
   __shared__ __attribute__((aligned(16))) float sL[2][BB];              // LSE * log2(e) of the tile's rows
@@ -288,8 +298,8 @@ __global__ __launch_bounds__(256, 1) void prefill_bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;      // 16-lane group
 
   // key blocks with the most causal query tiles first
   const int per_level = a.B * a.Hkv;
@@ -299,7 +309,7 @@ __global__ __launch_bounds__(256, 1) void prefill_bwd_dkdv_kernel(BwdArgs a) {
   const int g = rem - b * a.Hkv;
   const int key0 = j * BB;
   const int off = a.Lk - a.Lq;
-  const int my_key = key0 + wave * 32 + l32;
+  const int my_key = key0 + wave * 16 + l16;
   const bool key_ok = my_key < a.Lk;
 
   const __bf16 *kp = (const __bf16 *)a.k + b * a.ks[0] + g * a.ks[1];
@@ -311,8 +321,8 @@ __global__ __launch_bounds__(256, 1) void prefill_bwd_dkdv_kernel(BwdArgs a) {
     const int key = min(my_key, a.Lk - 1);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      kf[kk] = *(const bf16x8 *)(kp + (int64_t)key * a.ks[2] + kk * 16 + hi * 8);
-      vf[kk] = *(const bf16x8 *)(vp + (int64_t)key * a.vs[2] + kk * 16 + hi * 8);
+      kf[kk] = *(const bf16x8 *)(kp + (int64_t)key * a.ks[2] + kk * 32 + q4 * 8);
+      vf[kk] = *(const bf16x8 *)(vp + (int64_t)key * a.vs[2] + kk * 32 + q4 * 8);
     }
   }
 
@@ -345,8 +355,8 @@ __global__ __launch_bounds__(256, 1) void prefill_bwd_dkdv_kernel(BwdArgs a) {
     }
     return npairs;
   };
-  // LSE and D of a pair's rows travel through registers (thread t < 128: LSE of row t, else D of
-  // row t - 128), so rows past the end and rows without any kept key can be given P = 0 exactly
+  // LSE and D of a pair's rows travel through registers (thread t < 128: LSE of row t, 128 <= t < 256:
+  // D of row t - 128), so rows past the end and rows without any kept key get P = 0 exactly
   auto load_ld = [&](int p) -> float {
     const int h = p / a.nqt, t = p - (p / a.nqt) * a.nqt;
     const int row = t * BB + (tid & (BB - 1));
@@ -355,11 +365,11 @@ __global__ __launch_bounds__(256, 1) void prefill_bwd_dkdv_kernel(BwdArgs a) {
       const float l = row < a.Lq ? a.lse[idx] : kNegInf;
       return l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
     }
-    return row < a.Lq ? a.dvec[idx] : 0.f;
+    return (tid < 2 * BB && row < a.Lq) ? a.dvec[idx] : 0.f;
   };
   auto store_ld = [&](int buf, float x) {
     if (tid < BB) sL[buf][tid] = x;
-    else sD[buf][tid - BB] = x;
+    else if (tid < 2 * BB) sD[buf][tid - BB] = x;
   };
   auto stage = [&](int p, int buf) {
     const int h = p / a.nqt, t = p - (p / a.nqt) * a.nqt;
@@ -369,12 +379,13 @@ __global__ __launch_bounds__(256, 1) void prefill_bwd_dkdv_kernel(BwdArgs a) {
                lane);
   };
 
-  const int tr_off = tr_lane_offset(lane);
-  f32x16 dv_acc[MV], dk_acc[MV];
+  // transpose reads: 16-lane group q reads rows 4 q + (l16 / 4), columns 4 (l16 % 4) ... + 3
+  const int tr_off = (4 * q4 + (l16 >> 2)) * ROWB + 4 * (l16 & 3) * 2;
+  f32x4 dv_acc[MV], dk_acc[MV];
 #pragma unroll
   for (int i = 0; i < MV; ++i) {
-    dv_acc[i] = f32x16{};
-    dk_acc[i] = f32x16{};
+    dv_acc[i] = f32x4{};
+    dk_acc[i] = f32x4{};
   }
 
   int pc = next(0);
@@ -396,68 +407,44 @@ __global__ __launch_bounds__(256, 1) void prefill_bwd_dkdv_kernel(BwdArgs a) {
       const int t = pc - (pc / a.nqt) * a.nqt;
       const int row0 = t * BB;
       const bool need_mask = a.causal && (key0 + BB - 1 > row0 + off);
-      const unsigned char *qb = sQ[buf] + l32 * ROWB + hi * 16;
-      const unsigned char *ob = sO[buf] + l32 * ROWB + hi * 16;
+      const unsigned char *qb = sQ[buf] + l16 * ROWB + q4 * 16;
+      const unsigned char *ob = sO[buf] + l16 * ROWB + q4 * 16;
       const unsigned char *qtr = sQ[buf] + tr_off;
       const unsigned char *otr = sO[buf] + tr_off;
-      // S and dP of a 32-row slice: A operands (Q and dO rows) read one k-step ahead of their MFMAs
-      auto sdp = [&](int mt, f32x16 &s, f32x16 &dp) {
-        bf16x8 qa[2], oa[2];
-        qa[0] = *(const bf16x8 *)(qb + mt * 32 * ROWB);
-        oa[0] = *(const bf16x8 *)(ob + mt * 32 * ROWB);
-        s = f32x16{};
-        dp = f32x16{};
+      // one k-step of 32 rows = two 16-row slices: S and dP (C layout: lane holds key my_key and
+      // rows 16 sl + 4 q4 ... + 3), then P and dS as B operands, then dV^T and dK^T
+#pragma unroll 2
+      for (int ks = 0; ks < NSL / 2; ++ks) {
+        f32x4 s[2] = {f32x4{}, f32x4{}}, dp[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          if (kk + 1 < KS) {
-            qa[(kk + 1) & 1] = *(const bf16x8 *)(qb + mt * 32 * ROWB + (kk + 1) * 32);
-            oa[(kk + 1) & 1] = *(const bf16x8 *)(ob + mt * 32 * ROWB + (kk + 1) * 32);
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int sl = 2 * ks + h2;
+            const bf16x8 qa = *(const bf16x8 *)(qb + sl * 16 * ROWB + kk * 64);
+            const bf16x8 oa = *(const bf16x8 *)(ob + sl * 16 * ROWB + kk * 64);
+            s[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[kk], s[h2], 0, 0, 0);
+            dp[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[kk], dp[h2], 0, 0, 0);
           }
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk & 1], kf[kk], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[kk & 1], vf[kk], dp, 0, 0, 0);
-        }
-      };
-      // The slices are software-pipelined: the MFMAs of slice mt + 1's S and dP are issued before
-      // slice mt's exp / dS arithmetic, which then runs while they execute.
-      f32x16 s_cur, dp_cur;
-      sdp(0, s_cur, dp_cur);
+        bf16x8 pf, dsf;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x16 s_nxt = f32x16{}, dp_nxt = f32x16{};
-        if (mt + 1 < MT) sdp(mt + 1, s_nxt, dp_nxt);
-        // lane holds key my_key and rows row0 + 32 mt + 8 (r / 4) + 4 hi + r % 4
-        bf16x8 pf[2], dsf[2];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int rr = mt * 32 + 8 * q4 + 4 * hi;
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int rr = (2 * ks + h2) * 16 + 4 * q4;
           const f32x4 l4 = *(const f32x4 *)&sL[buf][rr];
           const f32x4 d4 = *(const f32x4 *)&sD[buf][rr];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int r = 4 * q4 + e;
-            float p = fast_exp2(__builtin_fmaf(s_cur[r], a.scale_log2, -l4[e]));
+            float p = fast_exp2(__builtin_fmaf(s[h2][e], a.scale_log2, -l4[e]));
             if (need_mask && my_key > row0 + rr + e + off) p = 0.f;
-            pf[r >> 3][r & 7] = (__bf16)p;
-            dsf[r >> 3][r & 7] = (__bf16)(p * (dp_cur[r] - d4[e]) * a.scale);
+            pf[4 * h2 + e] = (__bf16)p;
+            dsf[4 * h2 + e] = (__bf16)(p * (dp[h2][e] - d4[e]) * a.scale);
           }
         }
-        // dV^T += dO^T P and dK^T += Q^T dS over the slice's rows; transpose reads one MFMA pair ahead
-        bf16x8 ot = tr_operand(otr, 2 * mt, 0), qt = tr_operand(qtr, 2 * mt, 0);
 #pragma unroll
-        for (int i = 0; i < 2 * MV; ++i) {
-          const int k2 = i / MV, mv = i % MV;
-          bf16x8 ot_n = ot, qt_n = qt;
-          if (i + 1 < 2 * MV) {
-            ot_n = tr_operand(otr, 2 * mt + (i + 1) / MV, (i + 1) % MV);
-            qt_n = tr_operand(qtr, 2 * mt + (i + 1) / MV, (i + 1) % MV);
-          }
-          dv_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot, pf[k2], dv_acc[mv], 0, 0, 0);
-          dk_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsf[k2], dk_acc[mv], 0, 0, 0);
-          ot = ot_n;
-          qt = qt_n;
+        for (int mv = 0; mv < MV; ++mv) {
+          dv_acc[mv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_operand16(otr, ks, mv), pf, dv_acc[mv], 0, 0, 0);
+          dk_acc[mv] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_operand16(qtr, ks, mv), dsf, dk_acc[mv], 0, 0, 0);
         }
-        s_cur = s_nxt;
-        dp_cur = dp_nxt;
       }
     }
     if (pn < npairs) store_ld(buf ^ 1, ld_next);
@@ -465,22 +452,16 @@ __global__ __launch_bounds__(256, 1) void prefill_bwd_dkdv_kernel(BwdArgs a) {
     pc = pn;
   }
 
-
-
-  // ---- dK, dV: lane holds key my_key, dims 32 mv + 8 q + 4 hi ... + 3 in acc[mv][4 q ... 4 q + 3] ----
+  // ---- dK, dV: lane holds key my_key, dims 16 mv + 4 q4 ... + 3 in acc[mv] ----
   if (key_ok) {
     const int64_t kb = b * a.dks[0] + g * a.dks[1] + (int64_t)my_key * a.dks[2];
     const int64_t vb = b * a.dvs[0] + g * a.dvs[1] + (int64_t)my_key * a.dvs[2];
 #pragma unroll
-    for (int mv = 0; mv < MV; ++mv)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * mv + 8 * q4 + 4 * hi;
-        store4<OUT_F32>(a.dk, kb + d0, dk_acc[mv][4 * q4], dk_acc[mv][4 * q4 + 1], dk_acc[mv][4 * q4 + 2],
-                        dk_acc[mv][4 * q4 + 3]);
-        store4<OUT_F32>(a.dv, vb + d0, dv_acc[mv][4 * q4], dv_acc[mv][4 * q4 + 1], dv_acc[mv][4 * q4 + 2],
-                        dv_acc[mv][4 * q4 + 3]);
-      }
+    for (int mv = 0; mv < MV; ++mv) {
+      const int d0 = 16 * mv + 4 * q4;
+      store4<OUT_F32>(a.dk, kb + d0, dk_acc[mv][0], dk_acc[mv][1], dk_acc[mv][2], dk_acc[mv][3]);
+      store4<OUT_F32>(a.dv, vb + d0, dv_acc[mv][0], dv_acc[mv][1], dv_acc[mv][2], dv_acc[mv][3]);
+    }
   }
 }
 
@@ -503,9 +484,9 @@ hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int grid = a.B * a.Hkv * a.nkb;
   if (a.out_f32)
-    hipLaunchKernelGGL((prefill_bwd_dkdv_kernel<true>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_bwd_dkdv_kernel<true>), dim3(grid), dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL((prefill_bwd_dkdv_kernel<false>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_bwd_dkdv_kernel<false>), dim3(grid), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
