@@ -123,6 +123,40 @@ typedef struct {
 } blasst_prefill_params;
 
 /*
+ * Chunked prefill against a paged KV cache: the seqlen_q query tokens of each sequence are its last
+ * seqlen_q positions (their keys already written to the cache), and they attend to the sequence's
+ * seq_lens[b] cached keys with the prefill's tiles, skip rule, splits and bottom-right causal mask:
+ * query row i of sequence b sees keys k <= seq_lens[b] - seqlen_q + i.  The method serves prefill
+ * and decode alike (xllm-io review, 核心思想 item 2); this is the prefill computation for a chunk
+ * of a long prompt whose earlier keys sit in the same cache that decode reads.
+ *
+ * Layouts: q, o, lse, skip_mask, crit, counters as for blasst_prefill (seqlen_q rows, the mask's
+ * key-block count is ceil(max_pages_per_seq * page_size / block_k)); k_cache, v_cache,
+ * block_table and seq_lens as for blasst_decode (v_cache transposed inside each page).  A row that
+ * sees no key (seq_lens[b] < seqlen_q) gets o = 0 and lse = -inf.  The threshold's L is seq_lens[b]
+ * (per sequence, resolved on the device).
+ * Supported: bf16 in, bf16 or fp32 out, head_dim_qk == head_dim_v == 128, block_q == block_k == 128,
+ * page_size 16, causal only, seq_lens[b] >= 1.
+ */
+typedef struct {
+  size_t struct_size;        /* sizeof(blasst_prefill_paged_params) */
+  const void *q, *k_cache, *v_cache;
+  const int32_t *block_table, *seq_lens;
+  void *o;
+  float *lse;
+  uint8_t *skip_mask;
+  float *crit;
+  unsigned long long *counters;
+  int64_t q_stride[3], o_stride[3];
+  blasst_threshold thr;
+  int32_t in_dtype, out_dtype;
+  int32_t batch, seqlen_q, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v;
+  int32_t page_size, max_pages_per_seq, num_pages;
+  int32_t block_q, block_k, num_splits, stats_only;
+  float softmax_scale;
+} blasst_prefill_paged_params;
+
+/*
  * Decode: the query tokens of each sequence attend to the keys of a paged KV cache, split along
  * the keys into num_splits chunks that run in parallel and are merged by a log-sum-exp combine.
  * With T = num_q_tokens (0 means 1) query tokens per sequence, they are the last T positions of
@@ -222,6 +256,9 @@ typedef struct {
 /* Prefill forward (see the struct comment).  stream: hipStream_t or NULL. */
 blasst_status blasst_prefill(const blasst_prefill_params *params, void *stream);
 
+/* Chunked prefill against a paged cache (see the struct comment).  stream: hipStream_t or NULL. */
+blasst_status blasst_prefill_paged(const blasst_prefill_paged_params *params, void *stream);
+
 /* Prefill backward (see the struct comment).  stream: hipStream_t or NULL. */
 blasst_status blasst_prefill_backward(const blasst_prefill_backward_params *params, void *stream);
 
@@ -264,6 +301,7 @@ int32_t blasst_version(void);
 size_t blasst_prefill_params_size(void);
 size_t blasst_decode_params_size(void);
 size_t blasst_prefill_backward_params_size(void);
+size_t blasst_prefill_paged_params_size(void);
 
 #ifdef __cplusplus
 }

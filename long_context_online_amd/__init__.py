@@ -5,6 +5,8 @@ from .blasst import (  # noqa: F401
     BlasstError,
     blasst_prefill,
     blasst_prefill_backward,
+    blasst_prefill_paged,
+    paged_prefill_params,
     blasst_prefill_backward_workspace_size,
     backward_params,
     blasst_decode,

@@ -28,6 +28,7 @@ EXPORTED = [
     "blasst_calibrate", "blasst_lambda_for", "blasst_status_string", "blasst_last_error",
     "blasst_version", "blasst_prefill_params_size", "blasst_decode_params_size",
     "blasst_prefill_backward", "blasst_prefill_backward_workspace_size", "blasst_prefill_backward_params_size",
+    "blasst_prefill_paged", "blasst_prefill_paged_params_size",
 ]
 
 
@@ -81,6 +82,25 @@ class DecodeParams(ctypes.Structure):
     ]
 
 
+class PagedPrefillParams(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("skip_mask", ctypes.c_void_p), ("crit", ctypes.c_void_p), ("counters", ctypes.c_void_p),
+        ("q_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+        ("thr", Threshold),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32), ("seqlen_q", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+        ("stats_only", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
 class BackwardParams(ctypes.Structure):
     _fields_ = [
         ("struct_size", ctypes.c_size_t),
@@ -118,6 +138,9 @@ def lib():
         L.blasst_decode.restype = ctypes.c_int
         L.blasst_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeParams)]
         L.blasst_decode_workspace_size.restype = ctypes.c_size_t
+        L.blasst_prefill_paged.argtypes = [ctypes.POINTER(PagedPrefillParams), ctypes.c_void_p]
+        L.blasst_prefill_paged.restype = ctypes.c_int
+        L.blasst_prefill_paged_params_size.restype = ctypes.c_size_t
         L.blasst_prefill_backward.argtypes = [ctypes.POINTER(BackwardParams), ctypes.c_void_p]
         L.blasst_prefill_backward.restype = ctypes.c_int
         L.blasst_prefill_backward_workspace_size.argtypes = [ctypes.POINTER(BackwardParams)]
@@ -140,7 +163,8 @@ def lib():
         L.blasst_prefill_backward_params_size.restype = ctypes.c_size_t
         if L.blasst_prefill_params_size() != ctypes.sizeof(PrefillParams) or \
                 L.blasst_decode_params_size() != ctypes.sizeof(DecodeParams) or \
-                L.blasst_prefill_backward_params_size() != ctypes.sizeof(BackwardParams):
+                L.blasst_prefill_backward_params_size() != ctypes.sizeof(BackwardParams) or \
+                L.blasst_prefill_paged_params_size() != ctypes.sizeof(PagedPrefillParams):
             raise ImportError("libblasst.so struct layout does not match this binding")
         _lib = L
     return _lib
@@ -221,6 +245,39 @@ def blasst_prefill(q, k, v, o, *, stream=None, **kw):
     stats_only)."""
     p = prefill_params(q, k, v, o, **kw)
     _check(lib().blasst_prefill(ctypes.byref(p), _stream(stream)))
+
+
+def paged_prefill_params(q, k_cache, v_cache, block_table, seq_lens, o, *, num_splits=1, lam=None, a=None,
+                         softmax_scale=0.0, lse=None, skip_mask=None, crit=None, counters=None, stats_only=False,
+                         out_dtype=None, block_q=128, block_k=128):
+    """Fills the C params struct for blasst_prefill_paged from tensors (no call).  q [B, Hq, Lq, D]
+    (any strides with a contiguous last dim, e.g. a [B, Lq, Hq, D] tensor viewed with permute)."""
+    p = PagedPrefillParams()
+    p.struct_size = ctypes.sizeof(PagedPrefillParams)
+    p.q, p.k_cache, p.v_cache = _ptr(q), _ptr(k_cache), _ptr(v_cache)
+    p.block_table, p.seq_lens = _ptr(block_table), _ptr(seq_lens)
+    p.o, p.lse = _ptr(o), _ptr(lse)
+    p.skip_mask, p.crit, p.counters = _ptr(skip_mask), _ptr(crit), _ptr(counters)
+    p.q_stride = _strides3(q)
+    p.o_stride = _strides3(o) if o is not None else (ctypes.c_int64 * 3)(0, 0, 0)
+    p.thr = _threshold(lam, a)
+    p.in_dtype = _dtype_code(q)
+    p.out_dtype = _dtype_code(o) if o is not None else (p.in_dtype if out_dtype is None else out_dtype)
+    p.batch, p.num_q_heads, p.seqlen_q, p.head_dim_qk = q.shape
+    p.num_pages, p.num_kv_heads, p.page_size, _ = k_cache.shape
+    p.head_dim_v = v_cache.shape[2]
+    p.max_pages_per_seq = block_table.shape[1]
+    p.block_q, p.block_k, p.num_splits, p.stats_only = block_q, block_k, num_splits, int(bool(stats_only))
+    p.softmax_scale = float(softmax_scale)
+    return p
+
+
+def blasst_prefill_paged(q, k_cache, v_cache, block_table, seq_lens, o, *, stream=None, **kw):
+    """Chunked prefill against a paged cache: q [B, Hq, Lq, D] are the last Lq positions of each
+    sequence; k_cache [P, Hkv, 16, D], v_cache [P, Hkv, D, 16] (V transposed per page), block_table
+    [B, max_pages] int32, seq_lens [B] int32; o [B, Hq, Lq, D].  Keyword args follow the C params."""
+    p = paged_prefill_params(q, k_cache, v_cache, block_table, seq_lens, o, **kw)
+    _check(lib().blasst_prefill_paged(ctypes.byref(p), _stream(stream)))
 
 
 def backward_params(q, k, v, o, dout, lse, dq, dk, dv, *, causal, block_q=128, block_k=128, skip_mask=None,

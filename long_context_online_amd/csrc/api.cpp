@@ -16,6 +16,7 @@ hipError_t launch_prefill_f32(const PrefillArgs &a, int D, hipStream_t st);
 hipError_t launch_decode_gqa(const DecodeArgs &a, hipStream_t st);
 hipError_t launch_decode_latent(const DecodeArgs &a, hipStream_t st);
 hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t st);
+hipError_t launch_prefill_paged(const PrefillArgs &a, bool out_f32, hipStream_t st);
 }  // namespace blasst
 
 namespace {
@@ -85,6 +86,71 @@ int32_t blasst_version(void) { return 10000; }
 size_t blasst_prefill_params_size(void) { return sizeof(blasst_prefill_params); }
 size_t blasst_decode_params_size(void) { return sizeof(blasst_decode_params); }
 size_t blasst_prefill_backward_params_size(void) { return sizeof(blasst_prefill_backward_params); }
+size_t blasst_prefill_paged_params_size(void) { return sizeof(blasst_prefill_paged_params); }
+
+blasst_status blasst_prefill_paged(const blasst_prefill_paged_params *p, void *stream) {
+  if (!p) return fail(BLASST_ERR_INVALID_ARG, "params is NULL");
+  if (p->struct_size != sizeof(blasst_prefill_paged_params))
+    return fail(BLASST_ERR_INVALID_ARG, "struct_size %zu != %zu", p->struct_size, sizeof(blasst_prefill_paged_params));
+  if (!p->q || !p->k_cache || !p->v_cache || !p->block_table || !p->seq_lens)
+    return fail(BLASST_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table and seq_lens must be non-NULL");
+  if (!p->stats_only && !p->o) return fail(BLASST_ERR_INVALID_ARG, "o must be non-NULL unless stats_only");
+  if (p->batch < 1 || p->seqlen_q < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 || p->head_dim_qk < 1 ||
+      p->head_dim_v < 1)
+    return fail(BLASST_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (p->num_q_heads % p->num_kv_heads)
+    return fail(BLASST_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (p->page_size < 1 || p->max_pages_per_seq < 1 || p->num_pages < 1)
+    return fail(BLASST_ERR_INVALID_ARG, "page_size, max_pages_per_seq and num_pages must be >= 1");
+  if (p->block_q < 1 || p->block_k < 1) return fail(BLASST_ERR_INVALID_ARG, "block sizes must be >= 1");
+  if (p->num_splits < 1) return fail(BLASST_ERR_INVALID_ARG, "num_splits must be >= 1");
+  if (p->in_dtype != BLASST_BF16 && p->in_dtype != BLASST_FP32) return fail(BLASST_ERR_INVALID_ARG, "bad in_dtype");
+  if (p->out_dtype != BLASST_BF16 && p->out_dtype != BLASST_FP32) return fail(BLASST_ERR_INVALID_ARG, "bad out_dtype");
+  if (!std::isfinite(p->softmax_scale)) return fail(BLASST_ERR_INVALID_ARG, "softmax_scale must be finite");
+  for (int i = 0; i < 3; ++i)
+    if (p->q_stride[i] < 0 || p->o_stride[i] < 0) return fail(BLASST_ERR_INVALID_ARG, "strides must be >= 0");
+  double ln_lam;
+  const char *why = "";
+  if (!resolve_threshold(p->thr, 1.0, &ln_lam, &why)) return fail(BLASST_ERR_INVALID_ARG, "%s", why);
+  // ---- kernel coverage ----
+  if (p->in_dtype != BLASST_BF16) return fail(BLASST_ERR_UNSUPPORTED, "paged prefill supports bf16 inputs");
+  if (p->head_dim_qk != 128 || p->head_dim_v != 128 || p->block_q != 128 || p->block_k != 128 || p->page_size != 16)
+    return fail(BLASST_ERR_UNSUPPORTED, "paged prefill supports head dim 128, 128 x 128 blocks and 16-token pages");
+  const int oelem = p->out_dtype == BLASST_BF16 ? 2 : 4;
+  for (int i = 0; i < 3; ++i)
+    if (p->q_stride[i] % 8 || p->o_stride[i] % (16 / oelem))
+      return fail(BLASST_ERR_UNSUPPORTED, "strides must be multiples of 16 bytes");
+  if (!aligned16(p->q) || !aligned16(p->k_cache) || !aligned16(p->v_cache) || (p->o && !aligned16(p->o)))
+    return fail(BLASST_ERR_UNSUPPORTED, "q, caches and o must be 16-byte aligned");
+  const double scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0 / std::sqrt((double)p->head_dim_qk);
+  blasst::PrefillArgs a{};
+  a.q = p->q; a.k = p->k_cache; a.v = p->v_cache; a.o = p->o; a.lse = p->lse;
+  a.mask = p->skip_mask; a.crit = p->crit; a.counters = p->counters;
+  for (int i = 0; i < 3; ++i) { a.qs[i] = p->q_stride[i]; a.os[i] = p->o_stride[i]; }
+  a.B = p->batch; a.Lq = p->seqlen_q; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
+  a.G = p->num_q_heads / p->num_kv_heads;
+  a.Lk = p->max_pages_per_seq * p->page_size;
+  a.nqt = (p->seqlen_q + 127) / 128;
+  a.nkb = (int)(((int64_t)p->max_pages_per_seq * p->page_size + 127) / 128);
+  a.causal = 1; a.num_splits = p->num_splits; a.stats_only = p->stats_only ? 1 : 0;
+  a.scale = (float)scale;
+  a.scale_log2 = (float)(scale * 1.4426950408889634);
+  a.decide = 1;
+  a.table = p->block_table; a.seq_lens = p->seq_lens; a.max_pages = p->max_pages_per_seq;
+  if (p->thr.mode == BLASST_THR_A_OVER_L) {
+    a.thr_mode = 1;
+    a.a_thr = (float)p->thr.a;
+  } else {
+    a.thr_mode = 0;
+    a.thr_raw = thr_raw_from(p->thr.mode == BLASST_THR_NONE || p->thr.lambda == 0.0 ? -INFINITY
+                                                                                      : std::log(p->thr.lambda), scale);
+  }
+  if ((double)a.B * a.Hq * a.nqt > 2147483647.0 || (double)a.B * a.Hq * a.nqt * a.nkb > 2147483647.0)
+    return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
+  hipError_t e = blasst::launch_prefill_paged(a, p->out_dtype == BLASST_FP32, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BLASST_ERR_HIP, "paged prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
 
 blasst_status blasst_prefill(const blasst_prefill_params *p, void *stream) {
   if (!p) return fail(BLASST_ERR_INVALID_ARG, "params is NULL");

@@ -38,6 +38,14 @@ struct PrefillArgs {
   float scale_log2;  // scale * log2(e): exp(scale*(s - m)) = exp2(scale_log2*(s - m))
   float thr_raw;     // ln(lambda) / scale: skip iff (m~ - m) < thr_raw on raw logits
   int decide;        // 0: no threshold at all (every live block kept, no vote)
+  // Paged K/V (chunked prefill against a paged cache; the kernel's PAGED variant): k is the key
+  // cache [pages][Hkv][16][D], v the value cache [pages][Hkv][D][16] (V transposed inside each
+  // page), table [B][max_pages] page ids, seq_lens [B] the context length of each sequence, whose
+  // last Lq positions are the queries (Lk above is unused then).
+  const int32_t *table, *seq_lens;
+  int max_pages;
+  int thr_mode;      // 0: thr_raw; 1: lambda_b = min(1, a_thr / seq_lens[b]) per sequence
+  float a_thr;
 };
 
 // Arguments of the prefill backward kernels (bf16 inputs, head dim 128, 128 x 128 tile-blocks).

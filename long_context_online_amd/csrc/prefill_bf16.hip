@@ -44,8 +44,11 @@ typedef __attribute__((ext_vector_type(4))) short v4i16;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // DEC = false: no threshold at all (every live block kept, no vote); used to measure what the
-// decisions cost.
-template <int D, int BC, int TPW, bool OUT_F32, bool STATS, bool DEC = true>
+// decisions cost.  PAGED = true: K and V come from a paged cache (chunked prefill; head dim 128,
+// 128-key blocks of eight 16-token pages): K rows are gathered page by page, and V, which the cache
+// stores transposed inside each page, is staged as a V^T tile ([dv][key]), so the A operand of
+// O^T += V^T P^T is two plain 8-byte LDS reads instead of transpose reads.
+template <int D, int BC, int TPW, bool OUT_F32, bool STATS, bool DEC = true, bool PAGED = false>
 __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int WPT = BC / 32;       // waves per tile (32 rows each)
   constexpr int BR = BC;             // rows per tile
@@ -103,11 +106,21 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   const int hq = hq0 + tile;
   const int g = hq0 / a.G;                     // TPW divides G, so the group shares kv head g
   const int r0 = qt * BR;
-  const int off = a.Lk - a.Lq;                 // bottom-right causal alignment
+  int Lk = a.Lk;                               // keys of this sequence
+  float thr_raw = a.thr_raw;
+  if constexpr (PAGED) {
+    Lk = min(a.seq_lens[b], a.max_pages * 16);
+    if (a.thr_mode == 1) {
+      const float lam = fminf(1.f, a.a_thr / (float)Lk);
+      thr_raw = lam > 0.f ? __logf(lam) / a.scale : kNegInf;
+    }
+  }
+  const int off = Lk - a.Lq;                   // bottom-right causal alignment
 
   const __bf16 *qp = (const __bf16 *)a.q + b * a.qs[0] + hq * a.qs[1];
-  const __bf16 *kp = (const __bf16 *)a.k + b * a.ks[0] + g * a.ks[1];
-  const __bf16 *vp = (const __bf16 *)a.v + b * a.vs[0] + g * a.vs[1];
+  const __bf16 *kp = (const __bf16 *)a.k + (PAGED ? 0 : b * a.ks[0] + g * a.ks[1]);
+  const __bf16 *vp = (const __bf16 *)a.v + (PAGED ? 0 : b * a.vs[0] + g * a.vs[1]);
+  const int32_t *tab = PAGED ? a.table + (int64_t)b * a.max_pages : nullptr;
 
   const int last_row = min(r0 + BR, a.Lq) - 1;
   int J;  // live blocks (the same for every tile of the workgroup)
@@ -143,9 +156,13 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
         int row = p / CP, c = p - (p / CP) * CP;
         if (c >= CH) c = 0;
         if (row >= BC) row = 0;
-        const int key = min(key0 + row, a.Lk - 1);
-        __builtin_amdgcn_global_load_lds((const void *)(base + (int64_t)key * stride + c * 8),
-                                         (lds_void *)(dst + ins * 1024), 16, 0, 0);
+        const int key = min(key0 + row, Lk - 1);
+        const __bf16 *src;
+        if constexpr (PAGED)   // K row of the key's page (16 tokens per page)
+          src = base + ((int64_t)tab[key >> 4] * a.Hkv + g) * (16 * D) + (key & 15) * D + c * 8;
+        else
+          src = base + (int64_t)key * stride + c * 8;
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + ins * 1024), 16, 0, 0);
       }
     }
   };
@@ -153,9 +170,32 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     load_tile(kp, a.ks[2], j, sK[buf], std::integral_constant<int, KCP>{}, std::integral_constant<int, KCH>{},
               std::integral_constant<int, KINS>{});
   };
+  // Paged V^T tile: row dv holds the block's 128 keys, 16 bytes (8 keys, half a page) per position;
+  // row stride VTROW = 272 bytes (16 positions + 1 pad).  Keys past the sequence's last page read
+  // that page (their values are zeroed before use).
+  constexpr int VTCP = 17, VTROW = VTCP * 16, VTINS = D * VTCP / 64;
+  static_assert(!PAGED || (D == 128 && BC == 128 && VTINS * 1024 <= VBUF), "paged tiles are 128 x 128");
   auto load_v = [&](int j, int buf) {
-    load_tile(vp, a.vs[2], j, sV[buf], std::integral_constant<int, VCP>{}, std::integral_constant<int, VCH>{},
-              std::integral_constant<int, VINS>{});
+    if constexpr (PAGED) {
+      const int key0 = j * BC;
+      const int last_page = (Lk - 1) >> 4;
+#pragma unroll
+      for (int i = 0; i < (VTINS + NW - 1) / NW; ++i) {
+        const int ins = i * NW + wave;
+        if (ins < VTINS) {
+          const int p = ins * 64 + lane;
+          const int dv = p / VTCP;
+          int c = p - dv * VTCP;
+          if (c >= 16) c = 0;
+          const int page = min((key0 >> 4) + (c >> 1), last_page);
+          const __bf16 *src = vp + (((int64_t)tab[page] * a.Hkv + g) * D + dv) * 16 + (c & 1) * 8;
+          __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(sV[buf] + ins * 1024), 16, 0, 0);
+        }
+      }
+    } else {
+      load_tile(vp, a.vs[2], j, sV[buf], std::integral_constant<int, VCP>{}, std::integral_constant<int, VCH>{},
+                std::integral_constant<int, VINS>{});
+    }
   };
   // Transpose-read addressing for the V^T operand of k-step kk, dv m-tile mv: source lane
   // j = 4k + q of 16-lane group G points at V[16 kk + 4 (G / 2) + k][32 mv + 16 (G % 2) + 4 q ...+3];
@@ -215,6 +255,10 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       }
       const float base = (m_acc == kNegInf) ? 0.f : m_acc * a.scale_log2;
       const unsigned char *vb = sV[buf ^ 1] + tr_off;
+      // paged: V^T row reads; keys past the sequence end hold arbitrary bytes and get V = 0
+      const unsigned char *vtb = sV[buf ^ 1] + l32 * VTROW + hi * 8;
+      const int vkey0 = (t - 1) * BC;
+      const bool vtail = PAGED && vkey0 + BC > Lk;
       // P^T for k-step kk (16 keys) is formed right before its MFMAs: keys of score registers
       // s[kk/2][8*(kk%2) .. +7], i.e. key 16*kk + 8*(e/4) + 4*hi + e%4 for element e.
 #pragma unroll
@@ -231,10 +275,22 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
         l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, l_part2, false);
 #pragma unroll
         for (int mv = 0; mv < MTV; ++mv) {
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16 *)(vb + kk * 16 * VROW + mv * 64));
-          const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16 *)(vb + (kk * 16 + 8) * VROW + mv * 64));
+          v4i16 lo, up;
+          if constexpr (PAGED) {
+            // keys 16 kk + 4 hi ... + 3 and 16 kk + 8 + 4 hi ... + 3 of dv row 32 mv + l32
+            lo = *(const v4i16 *)(vtb + mv * 32 * VTROW + kk * 32);
+            up = *(const v4i16 *)(vtb + mv * 32 * VTROW + kk * 32 + 16);
+            if (vtail) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (vkey0 + 16 * kk + 4 * hi + e >= Lk) lo[e] = 0;
+                if (vkey0 + 16 * kk + 8 + 4 * hi + e >= Lk) up[e] = 0;
+              }
+            }
+          } else {
+            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + kk * 16 * VROW + mv * 64));
+            up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + (kk * 16 + 8) * VROW + mv * 64));
+          }
           const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
           o_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o_acc[mv], 0, 0, 0);
         }
@@ -266,9 +322,9 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
 
     // ---- causal / tail mask (only blocks that need it) ----
     const int key0 = t * BC;
-    const bool need_mask = (key0 + BC > a.Lk) || (a.causal && key0 + BC - 1 > r0 + off);
+    const bool need_mask = (key0 + BC > Lk) || (a.causal && key0 + BC - 1 > r0 + off);
     if (need_mask) {
-      const int lim = a.causal ? min(my_row + off, a.Lk - 1) : a.Lk - 1;
+      const int lim = a.causal ? min(my_row + off, Lk - 1) : Lk - 1;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -287,7 +343,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     mx = max_xor32(mx);
     if (!row_ok) mx = kNegInf;
     if (DEC) {
-      const bool skip_row = row_votes_skip(mx, m_dec, a.thr_raw);
+      const bool skip_row = row_votes_skip(mx, m_dec, thr_raw);
       const bool wave_keep = __ballot(!skip_row) != 0ull;
       float wcrit = 0.f;
       if (a.crit) wcrit = max_lanes32(row_crit(mx, m_dec));
@@ -402,6 +458,29 @@ static hipError_t launch_one(const PrefillArgs &a, bool out_f32, hipStream_t st)
   // two q heads of one GQA group share each staged K/V block when the group has an even size
   if (a.G % 2 == 0) return launch_tpw<D, BC, 2>(a, out_f32, st);
   return launch_tpw<D, BC, 1>(a, out_f32, st);
+}
+
+// Chunked prefill against a paged cache (head dim 128, 128 x 128 blocks, 16-token pages).
+hipError_t launch_prefill_paged(const PrefillArgs &a, bool out_f32, hipStream_t st) {
+  const int tpw = a.G % 2 == 0 ? 2 : 1;
+  const int grid = a.B * (a.Hq / tpw) * a.nqt;
+  const int nt = 256 * tpw;
+  if (tpw == 2) {
+    if (a.stats_only)
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, 128, 2, false, true, true, true>), dim3(grid), dim3(nt), 0, st, a);
+    else if (out_f32)
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, 128, 2, true, false, true, true>), dim3(grid), dim3(nt), 0, st, a);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, 128, 2, false, false, true, true>), dim3(grid), dim3(nt), 0, st, a);
+  } else {
+    if (a.stats_only)
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, 128, 1, false, true, true, true>), dim3(grid), dim3(nt), 0, st, a);
+    else if (out_f32)
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, 128, 1, true, false, true, true>), dim3(grid), dim3(nt), 0, st, a);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, 128, 1, false, false, true, true>), dim3(grid), dim3(nt), 0, st, a);
+  }
+  return hipGetLastError();
 }
 
 // Returns hipErrorNotSupported when no instantiation matches.

@@ -44,6 +44,7 @@ def test_struct_layout_matches_binding(m):
     assert lib.blasst_prefill_params_size() == ctypes.sizeof(m.blasst.PrefillParams)
     assert lib.blasst_decode_params_size() == ctypes.sizeof(m.blasst.DecodeParams)
     assert lib.blasst_prefill_backward_params_size() == ctypes.sizeof(m.blasst.BackwardParams)
+    assert lib.blasst_prefill_paged_params_size() == ctypes.sizeof(m.blasst.PagedPrefillParams)
     assert lib.blasst_version() >= 10000
 
 
@@ -206,3 +207,41 @@ def test_backward_workspace_size(m):
     odd = _backward(seqlen_q=1000, seqlen_k=1000)
     assert lib.blasst_prefill_backward_workspace_size(ctypes.byref(odd)) == (32 * 1000 * 4 + 255) // 256 * 256
     assert lib.blasst_prefill_backward_workspace_size(ctypes.byref(_backward(num_kv_heads=5))) == 0
+
+
+def _paged(**over):
+    from long_context_online_amd.blasst import PagedPrefillParams, Threshold
+    p = PagedPrefillParams()
+    p.struct_size = ctypes.sizeof(PagedPrefillParams)
+    p.q = p.k_cache = p.v_cache = p.block_table = p.seq_lens = p.o = FAKE
+    p.q_stride[:] = [32 * 512 * 128, 512 * 128, 128]
+    p.o_stride[:] = p.q_stride[:]
+    p.thr = Threshold(1, 0, 0.0, 4.0)
+    p.in_dtype, p.out_dtype = 0, 0
+    p.batch, p.seqlen_q, p.num_q_heads, p.num_kv_heads = 2, 512, 32, 8
+    p.head_dim_qk = p.head_dim_v = 128
+    p.page_size, p.max_pages_per_seq, p.num_pages = 16, 256, 600
+    p.block_q = p.block_k = 128
+    p.num_splits = 1
+    for k, v in over.items():
+        if k == "thr":
+            p.thr = Threshold(*v)
+        else:
+            setattr(p, k, v)
+    return p
+
+
+PAGED_BAD = [
+    ({"q": None}, 1), ({"seq_lens": None}, 1), ({"v_cache": None}, 1), ({"o": None}, 1), ({"num_kv_heads": 5}, 1),
+    ({"num_splits": 0}, 1), ({"thr": (0, 0, 1.5, 0.0)}, 1), ({"struct_size": 16}, 1), ({"page_size": 0}, 1),
+    ({"in_dtype": 1}, 2), ({"page_size": 32}, 2), ({"block_q": 64, "block_k": 64}, 2),
+    ({"head_dim_qk": 64, "head_dim_v": 64}, 2), ({"q": FAKE + 4}, 2),
+]
+
+
+@pytest.mark.parametrize("over,status", PAGED_BAD, ids=[str(x[0]) for x in PAGED_BAD])
+def test_paged_prefill_rejects_invalid_arguments(m, over, status):
+    lib = m.lib()
+    p = _paged(**over)
+    assert lib.blasst_prefill_paged(ctypes.byref(p), None) == status
+    assert lib.blasst_last_error()
