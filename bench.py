@@ -35,6 +35,7 @@ PEAK_HBM_GBPS = 8000.0
 # prefill workload
 P_B, P_HQ, P_HKV, P_L, P_D, P_BLK = 1, 32, 8, 32768, 128, 128
 P_TARGET = 0.75
+C_B, C_L, C_T = 4, 32768, 2048      # chunked prefill: sequences, context length, chunk length
 # decode workload
 D_B, D_HQ, D_HKV, D_CTX, D_D, D_PAGE, D_BLK, D_SPLITS = 32, 32, 8, 32768, 128, 16, 64, 16
 D_TARGET = 0.73
@@ -319,6 +320,58 @@ class Decode:
             flops = blocks * D_BLK * self.Hq * (self.D * 2) + kept * D_BLK * self.Hq * (self.Dv * 2)
             r["mfma_tflops"] = round(flops / (sparse_ms * 1e-3) / 1e12, 2)
         return r
+
+
+class PagedPrefill:
+    """Chunked prefill against the paged cache: C_B sequences whose C_L-token contexts end with a
+    C_T-token chunk (the queries), 32 q / 8 kv heads, d 128, 16-token pages in a permuted pool."""
+
+    def __init__(self, m, torch, synth, seed=None):
+        self.m, self.torch = m, torch
+        seed = synth.config_seed(6) if seed is None else seed
+        self.d = synth.decode_inputs(batch=C_B, hq=P_HQ, hkv=P_HKV, ctx=C_L, d=P_D, page_size=D_PAGE,
+                                     block_k=P_BLK, window=True, seed=seed, device="cuda", num_q_tokens=C_T)
+        self.q = self.d.q.permute(0, 2, 1, 3)
+        self.o = torch.empty(C_B, P_HQ, C_T, P_D, dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty(C_B, P_HQ, C_T, dtype=torch.float32, device="cuda")
+        self.nqt = C_T // P_BLK
+        self.nkb = -(-(self.d.block_table.shape[1] * D_PAGE) // P_BLK)
+        pairs = C_T * (C_L - C_T) + C_T * (C_T + 1) // 2
+        self.dense_flops = 4.0 * C_B * P_HQ * P_D * pairs
+
+    def run(self, lam, **diag):
+        d = self.d
+        self.m.blasst_prefill_paged(self.q, d.k_cache, d.v_cache_t, d.block_table, d.seq_lens, self.o, lam=lam,
+                                    lse=self.lse, **diag)
+
+    def calibrate(self, target):
+        torch = self.torch
+        crit = torch.empty(C_B, P_HQ, self.nqt, self.nkb, dtype=torch.float32, device="cuda")
+        d = self.d
+        self.m.blasst_prefill_paged(self.q, d.k_cache, d.v_cache_t, d.block_table, d.seq_lens, None, lam=0.0,
+                                    crit=crit, stats_only=True)
+        torch.cuda.synchronize()
+        g = torch.Generator().manual_seed(4343)
+        picks = [(int(torch.randint(0, C_B, (1,), generator=g)), int(torch.randint(0, P_HQ, (1,), generator=g)),
+                  int((i + 0.5) * self.nqt / CALIB_TILES)) for i in range(CALIB_TILES)]
+        sample = torch.stack([crit[b, h, t] for b, h, t in picks])
+        return math.exp(self.m.blasst_calib_quantile(sample.cpu().numpy(), target))
+
+    def measure(self, lam, steps):
+        torch = self.torch
+        cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+        self.run(lam, counters=cnt)
+        torch.cuda.synchronize()
+        live, skipped = int(cnt[0]), int(cnt[1])
+        sparse_ms = timed(torch, lambda: self.run(lam), steps)
+        dense_ms = timed(torch, lambda: self.run(0.0), steps)
+        return {"ms": round(sparse_ms, 4), "dense_ms": round(dense_ms, 4),
+                "speedup_vs_dense": round(dense_ms / sparse_ms, 3),
+                "dense_equiv_tflops": round(self.dense_flops / (sparse_ms * 1e-3) / 1e12, 2),
+                "dense_tflops": round(self.dense_flops / (dense_ms * 1e-3) / 1e12, 2),
+                "lambda": lam, "sparsity": round(skipped / live, 4),
+                "workload": f"chunked prefill against the paged cache: {C_B} sequences, {C_L}-token contexts "
+                            f"ending with a {C_T}-token chunk, 32 q / 8 kv heads, d 128, 16-token pages"}
 
 
 class Backward:
@@ -624,6 +677,13 @@ def main():
         r.update({"target_sparsity": D_TARGET, "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4)})
         result["decode_131072"] = r
         del d128
+        torch.cuda.empty_cache()
+        cp = PagedPrefill(m, torch, synth)
+        lam = cp.calibrate(P_TARGET)
+        r = cp.measure(lam, args.steps)
+        r["target_sparsity"] = P_TARGET
+        result["chunked_prefill"] = r
+        del cp
         torch.cuda.empty_cache()
         result["decode_multi_token"] = {}
         for T in (2, 4):

@@ -120,7 +120,11 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   const __bf16 *qp = (const __bf16 *)a.q + b * a.qs[0] + hq * a.qs[1];
   const __bf16 *kp = (const __bf16 *)a.k + (PAGED ? 0 : b * a.ks[0] + g * a.ks[1]);
   const __bf16 *vp = (const __bf16 *)a.v + (PAGED ? 0 : b * a.vs[0] + g * a.vs[1]);
-  const int32_t *tab = PAGED ? a.table + (int64_t)b * a.max_pages : nullptr;
+  // the sequence's page ids, read through the scalar cache (the addresses are wave-uniform), so page
+  // lookups wait on lgkmcnt and never on the direct loads in flight (vmcnt)
+  typedef const __attribute__((address_space(4))) int32_t *const_i32p;
+  const const_i32p tab = PAGED ? (const_i32p)(uintptr_t)(a.table + (int64_t)b * a.max_pages) : nullptr;
+  const int last_page = PAGED ? (Lk - 1) >> 4 : 0;
 
   const int last_row = min(r0 + BR, a.Lq) - 1;
   int J;  // live blocks (the same for every tile of the workgroup)
@@ -158,10 +162,17 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
         if (row >= BC) row = 0;
         const int key = min(key0 + row, Lk - 1);
         const __bf16 *src;
-        if constexpr (PAGED)   // K row of the key's page (16 tokens per page)
-          src = base + ((int64_t)tab[key >> 4] * a.Hkv + g) * (16 * D) + (key & 15) * D + c * 8;
-        else
+        if constexpr (PAGED) {
+          // K row of the key's page (16 tokens per page); the instruction's rows lie on at most two
+          // pages, whose ids are read once per instruction (uniform) and picked per lane
+          const int r_lo = (ins * 64) / CP, r_hi = min((ins * 64 + 63) / CP, BC - 1);
+          const int pa = min((key0 + r_lo) >> 4, last_page), pb = min((key0 + r_hi) >> 4, last_page);
+          const int pid_a = tab[pa], pid_b = tab[pb];
+          const int pid = (key >> 4) == pa ? pid_a : pid_b;
+          src = base + ((int64_t)pid * a.Hkv + g) * (16 * D) + (key & 15) * D + c * 8;
+        } else {
           src = base + (int64_t)key * stride + c * 8;
+        }
         __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + ins * 1024), 16, 0, 0);
       }
     }
@@ -177,8 +188,10 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   static_assert(!PAGED || (D == 128 && BC == 128 && VTINS * 1024 <= VBUF), "paged tiles are 128 x 128");
   auto load_v = [&](int j, int buf) {
     if constexpr (PAGED) {
-      const int key0 = j * BC;
-      const int last_page = (Lk - 1) >> 4;
+      const int kp0 = j * (BC / 16);
+      int pids[BC / 16];   // ids of the block's 8 pages (uniform), picked per lane below
+#pragma unroll
+      for (int i = 0; i < BC / 16; ++i) pids[i] = tab[min(kp0 + i, last_page)];
 #pragma unroll
       for (int i = 0; i < (VTINS + NW - 1) / NW; ++i) {
         const int ins = i * NW + wave;
@@ -187,8 +200,11 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
           const int dv = p / VTCP;
           int c = p - dv * VTCP;
           if (c >= 16) c = 0;
-          const int page = min((key0 >> 4) + (c >> 1), last_page);
-          const __bf16 *src = vp + (((int64_t)tab[page] * a.Hkv + g) * D + dv) * 16 + (c & 1) * 8;
+          int pid = pids[0];
+#pragma unroll
+          for (int q = 1; q < BC / 16; ++q)
+            if ((c >> 1) == q) pid = pids[q];
+          const __bf16 *src = vp + (((int64_t)pid * a.Hkv + g) * D + dv) * 16 + (c & 1) * 8;
           __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(sV[buf] + ins * 1024), 16, 0, 0);
         }
       }
