@@ -146,12 +146,32 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
 
   // ---- staging: direct global -> LDS ---------------------------------------------------------
   // One wave instruction fills 1 KB = 64 consecutive 16-byte positions of a buffer; position p is
-  // (row p / CP, chunk p % CP).  Pad chunks and rows past the tile load a valid chunk of row 0 and
-  // keys past the end load the last key, so every lane reads valid memory (those keys are masked).
+  // (row p / CP, chunk p % CP); pad chunks load chunk 0 of their row.  Contiguous K/V go through a
+  // buffer resource per block whose extent ends at the last key, so keys past the end read as zero
+  // (and are masked) without any clamping, and a load costs a few 24-bit integer ops for its offset.
   auto load_tile = [&](const __bf16 *base, int64_t stride, int j, unsigned char *dst, auto CPc, auto CHc,
                        auto INSc) {
     constexpr int CP = decltype(CPc)::value, CH = decltype(CHc)::value, INS = decltype(INSc)::value;
     const int key0 = j * BC;
+    if constexpr (!PAGED) {
+      static_assert(INS * 64 == BC * CP, "every position of a tile is one row chunk");
+      const uint32_t row_b = (uint32_t)stride * 2u;
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(base + (int64_t)key0 * stride), (short)0, (int)((uint32_t)min(Lk - key0, BC) * row_b), 0x00020000);
+#pragma unroll
+      for (int i = 0; i < (INS + NW - 1) / NW; ++i) {
+        const int ins = i * NW + wave;
+        if (ins < INS) {
+          const int p = ins * 64 + lane;
+          const int row = p / CP;
+          int c = p - row * CP;
+          if (c >= CH) c = 0;
+          const int voff = (int)(__mul24(row, row_b) + c * 16);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(dst + ins * 1024), 16, voff, 0, 0, 0);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < (INS + NW - 1) / NW; ++i) {
       const int ins = i * NW + wave;
