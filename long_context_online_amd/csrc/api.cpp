@@ -190,6 +190,9 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *stream) {
   if (p->in_dtype == BLASST_BF16) {
     if (!((D == 64 || D == 128) && (p->block_k == 64 || p->block_k == 128)))
       return fail(BLASST_ERR_UNSUPPORTED, "bf16 prefill supports head dim 64/128 and blocks 64/128");
+    // K and V rows are addressed with 24-bit byte offsets inside a block
+    if (p->k_stride[2] >= (1 << 22) || p->v_stride[2] >= (1 << 22))
+      return fail(BLASST_ERR_UNSUPPORTED, "k and v token strides must be below 2^22 elements");
   } else {
     if (!((D == 64 || D == 128) && p->block_k == 64 && p->out_dtype == BLASST_FP32))
       return fail(BLASST_ERR_UNSUPPORTED, "fp32 prefill supports head dim 64/128, blocks 64, fp32 out");

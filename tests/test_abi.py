@@ -72,6 +72,7 @@ def _prefill(**over):
 
 
 PREFILL_BAD = [
+    ({"k_stride": (1 << 40, 1 << 30, 1 << 22)}, 2),
     ({"q": None}, 1), ({"o": None}, 1), ({"batch": 0}, 1), ({"num_kv_heads": 3}, 1),
     ({"num_splits": 0}, 1), ({"in_dtype": 7}, 1), ({"causal": 2}, 1), ({"block_k": 0}, 1),
     ({"thr": (0, 0, 1.5, 0.0)}, 1), ({"thr": (0, 0, -0.1, 0.0)}, 1), ({"thr": (1, 0, 0.0, -2.0)}, 1),
