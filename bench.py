@@ -627,7 +627,7 @@ def main():
         result["prefill"] = r
         result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                              "traffic": profiled_traffic("prefill_bf16_kernel<128, 128, 2, false, false, true>"),
+                              "traffic": profiled_traffic("prefill_bf16_kernel<128, 128, 2, false, false, true, false>"),
                               "traffic_unit": "HBM bytes per launch",
                               "min_bytes": pre.min_bytes,
                               "kernel": "prefill_bf16_kernel<128, 128, 2, bf16 out>",
