@@ -210,3 +210,24 @@ def test_llama8b_gqa_32k_backward_sampled_and_invariants():
     print(f"sparsity {(mh == SKIPPED).sum() / (mh != 2).sum():.3f}; key blocks no tile kept: {len(dead)}")
     for g, j in dead[:20]:
         assert torch.all(dk[0, g, j * 128:(j + 1) * 128] == 0) and torch.all(dv[0, g, j * 128:(j + 1) * 128] == 0)
+
+
+def test_backward_more_queries_than_keys():
+    """Lq = 500 over Lk = 300 (bottom-right causal): rows without keys get no gradient and add nothing."""
+    m = _lib()
+    inp = synth.prefill_inputs(batch=1, hq=4, hkv=2, L=500, d=128, block_k=128, window=True, seed=62,
+                               device="cuda")
+
+    class Cut:
+        q = inp.q
+        k = inp.k[:, :, :300].contiguous()
+        v = inp.v[:, :, :300].contiguous()
+
+    o, lse, mask = _forward(m, Cut, causal=True, lam=0.02)
+    dout = _dout(o.shape, 10)
+    dq, dk, dv = _backward(m, Cut, o, lse, dout, mask, causal=True)
+    assert torch.all(dq[:, :, :200] == 0)
+    ref = bw.prefill_backward(host64(Cut.q), host64(Cut.k), host64(Cut.v), host64(dout), mask.cpu().numpy(),
+                              causal=True, block_q=128, block_k=128)
+    errs = [_check(dq, ref["dq"], "dq"), _check(dk, ref["dk"], "dk"), _check(dv, ref["dv"], "dv")]
+    print(f"rel errs {errs}")

@@ -219,3 +219,20 @@ def test_heterogeneous_heads_per_head_sparsity(dtype, blk):
           ", ".join(f"{c}:{s:.3f}" for c, s in sorted(zip(strength, sp))))
     order = np.argsort(strength)
     assert sp[order[-1]] > sp[order[0]] + 0.2
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_more_queries_than_keys(splits):
+    """Lq = 500 queries over Lk = 300 keys, bottom-right causal: the first 200 rows see no key (O = 0,
+    LSE = -inf), the rest match the oracle; the tile that straddles the boundary votes with rows
+    that see nothing."""
+    m = _lib()
+    inp = synth.prefill_inputs(batch=1, hq=4, hkv=2, L=500, d=128, block_k=128, window=True, seed=61,
+                               device="cuda")
+    k = inp.k[:, :, :300].contiguous()
+    v = inp.v[:, :, :300].contiguous()
+    res = _run(m, inp.q, k, v, causal=True, bq=128, bk=128, splits=splits, lam=0.01)
+    o, lse = res[0], res[1]
+    assert torch.all(o[:, :, :200] == 0) and torch.all(lse[:, :, :200] == float("-inf"))
+    rep = _compare_all(inp.q, k, v, res, causal=True, bq=128, bk=128, splits=splits, ln_lam=math.log(0.01))
+    print(rep)
