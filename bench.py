@@ -416,6 +416,22 @@ class Backward:
                 "workload": "the bench prefill's backward: dQ, dK, dV (bf16) from bf16 O and dO, forward skip mask"}
 
 
+SWEEP_TARGETS = (0.4, 0.5, 0.6, 0.7, 0.8, 0.9)
+
+
+def sparsity_sweep(obj, steps):
+    """Speedup over lambda = 0 at calibrated target sparsities 40 ... 90 % (the layout of the pages'
+    speedup-versus-sparsity table); lambda is capped at 1, so high targets may not be reachable and
+    the achieved sparsity is what the line reports."""
+    out = []
+    for t in SWEEP_TARGETS:
+        lam = obj.calibrate(t)
+        r = obj.measure(lam, steps)
+        out.append({"target": t, "sparsity": r["sparsity"], "speedup_vs_dense": r["speedup_vs_dense"],
+                    "ms": r["ms"], "dense_ms": r["dense_ms"], "lambda": lam})
+    return out
+
+
 def head_heterogeneity(m, torch, synth, pre, lam_p, steps):
     """Per-head sparsity under one threshold: the bench workload (heads alike) and the same shape
     with heads of different peakedness (head strengths spread geometrically over 0.25 ... 2, in a
@@ -645,6 +661,7 @@ def main():
             bw = Backward(m, torch, pre, lam_p)
             result["prefill_backward"] = bw.measure(max(3, args.steps // 2))
             del bw
+            result["prefill_speedup_vs_sparsity"] = sparsity_sweep(pre, max(3, args.steps // 2))
     if dec:
         r = dec.measure(lam_d, args.steps, ms=dec_ms)
         r.update({"target_sparsity": M_TARGETS[-1] if dec.latent else D_TARGET,
@@ -654,6 +671,8 @@ def main():
                                "pages, 64-token blocks, 16 splits, bf16")})
         r["timed_step_ms_p10_p50_p90"] = percentiles(dec_all)
         result["decode"] = r
+        if not args.quick and not dec.latent:
+            result["decode_speedup_vs_sparsity"] = sparsity_sweep(dec, args.steps)
         result["roofline_decode"] = {"bound": "hbm", "achieved": r["hbm_gbps"], "peak": PEAK_HBM_GBPS,
                                      "unit": "GB/s", "frac": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
                                      "traffic": profiled_traffic(DEC_KERNEL[dec.latent]),
