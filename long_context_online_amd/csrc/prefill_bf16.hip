@@ -253,13 +253,14 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   const int mask_row = ((b * a.Hq + hq) * a.nqt + qt) * a.nkb;
   const bool tile_leader = wit == 0 && lane == 0;
 
-  // ---- block loop, software-pipelined by one block: iteration t does the P.V product of block
-  // t - 1 (its scores are still in registers) and then QK^T, row max and vote of block t.  One
-  // barrier per iteration both publishes block t's votes and makes K_{t+1} and V_t (prefetched at
-  // the top of the iteration into the buffers that iteration t - 1 finished with) visible. ----
-  f32x16 s[MT];            // scores of the block whose P.V is pending
-  float mx_pend = kNegInf; // its row max
-  bool keep_pend = false;  // its decision
+  // ---- block loop, software-pipelined by one block.  Iteration t computes QK^T, row max and vote
+  // of block t, then one barrier publishes the votes and makes K_{t+1} (prefetched at the top of
+  // the iteration) and V_{t-1} visible; then the P.V product of block t - 1 (its probabilities
+  // packed in registers), and for a kept block t its probabilities and the direct loads of V_t.
+  // So V is staged only for blocks that a tile of the workgroup kept. ----
+  f32x16 s[MT];            // scores of block t
+  bf16x8 pf_pend[KSV];     // bf16 probabilities of the kept block whose P.V is pending
+  bool keep_pend = false;  // block t - 1 was kept by this tile
   if (J > 0) {
     load_k(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -267,48 +268,76 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   }
   for (int t = 0; t <= J; ++t) {
     const int buf = t & 1;
+    if (t + 1 < J) load_k(t + 1, buf ^ 1);
+    float mx = kNegInf;
     if (t < J) {
-      if (t + 1 < J) load_k(t + 1, buf ^ 1);
-      if (!STATS) load_v(t, buf);
+      if ((t % chunk) == 0) m_dec = kNegInf;
+
+      // ---- S^T = K_t Q^T ----
+      const unsigned char *kb = sK[buf] + l32 * KROW + hi * 16;
+      // K fragments are read one k-step ahead of the MFMAs that consume them, so LDS latency
+      // overlaps the previous k-step's MFMAs instead of stalling every MFMA
+      bf16x8 kf[2][MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) kf[0][mt] = *(const bf16x8 *)(kb + mt * 32 * KROW);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        if (kk + 1 < KS) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            kf[(kk + 1) & 1][mt] = *(const bf16x8 *)(kb + mt * 32 * KROW + (kk + 1) * 32);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk & 1][mt], qf[kk], kk == 0 ? f32x16{} : s[mt], 0,
+                                                          0, 0);
+        __builtin_amdgcn_sched_barrier(0);  // keep the next k-step's reads ahead of these MFMAs
+      }
+
+      // ---- causal / tail mask (only blocks that need it) ----
+      const int key0 = t * BC;
+      const bool need_mask = (key0 + BC > Lk) || (a.causal && key0 + BC - 1 > r0 + off);
+      if (need_mask) {
+        const int lim = a.causal ? min(my_row + off, Lk - 1) : Lk - 1;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + mt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key > lim) s[mt][r] = kNegInf;
+          }
+      }
+
+      // ---- block row max, vote, critical value ----
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+      mx = max_xor32(mx);
+      if (!row_ok) mx = kNegInf;
+      if (DEC) {
+        const bool skip_row = row_votes_skip(mx, m_dec, thr_raw);
+        const bool wave_keep = __ballot(!skip_row) != 0ull;
+        float wcrit = 0.f;
+        if (a.crit) wcrit = max_lanes32(row_crit(mx, m_dec));
+        if (lane == 0) {
+          sVote[buf][wave] = wave_keep ? 1 : 0;
+          sCrit[buf][wave] = wcrit;
+        }
+      }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K_{t+1} and V_{t-1} have landed in LDS
+    __syncthreads();
 
     if (!STATS && keep_pend) {
-      // ---- kept block t - 1: online-softmax update and O^T += V^T P^T ----
-      // Lazy rescaling: the accumulation reference m_acc is raised only when a row's block max
-      // exceeds it by more than 2^8 in probability (a row's first finite max just sets it: O and l
-      // are still zero); below that, probabilities relative to the stale reference are at most 256,
-      // which bf16 P and the fp32 sums hold with the same relative precision, and O / l and the
-      // LSE are unchanged.  So the accumulators are rescaled only when the max jumps.
-      if (m_acc == kNegInf) m_acc = mx_pend;
-      if (__ballot((mx_pend - m_acc) * a.scale_log2 > 8.f) != 0ull) {
-        const float m_new = fmaxf(m_acc, mx_pend);
-        const float alpha = fast_exp2((m_acc - m_new) * a.scale_log2);
-        l_part *= alpha;
-        l_part2 *= alpha;
-#pragma unroll
-        for (int i = 0; i < MTV; ++i) o_acc[i] *= alpha;
-        m_acc = m_new;
-      }
-      const float base = (m_acc == kNegInf) ? 0.f : m_acc * a.scale_log2;
+      // ---- kept block t - 1: O^T += V^T P^T ----
       const unsigned char *vb = sV[buf ^ 1] + tr_off;
       // paged: V^T row reads; keys past the sequence end hold arbitrary bytes and get V = 0
       const unsigned char *vtb = sV[buf ^ 1] + l32 * VTROW + hi * 8;
       const int vkey0 = (t - 1) * BC;
       const bool vtail = PAGED && vkey0 + BC > Lk;
-      // P^T for k-step kk (16 keys) is formed right before its MFMAs: keys of score registers
-      // s[kk/2][8*(kk%2) .. +7], i.e. key 16*kk + 8*(e/4) + 4*hi + e%4 for element e.
 #pragma unroll
       for (int kk = 0; kk < KSV; ++kk) {
-        bf16x8 pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pf[e] = (__bf16)fast_exp2(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + e], a.scale_log2, -base));
-        // row sum: one bf16 dot2 with (1, 1) per pair of probabilities
-        const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), one2, l_part, false);
-        l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), one2, l_part2, false);
-        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), one2, l_part, false);
-        l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, l_part2, false);
 #pragma unroll
         for (int mv = 0; mv < MTV; ++mv) {
           v4i16 lo, up;
@@ -328,73 +357,21 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
             up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + (kk * 16 + 8) * VROW + mv * 64));
           }
           const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
-          o_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o_acc[mv], 0, 0, 0);
+          o_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf_pend[kk], o_acc[mv], 0, 0, 0);
         }
       }
     }
     if (t == J) break;
-    if ((t % chunk) == 0) m_dec = kNegInf;
 
-    // ---- S^T = K_t Q^T ----
-    const unsigned char *kb = sK[buf] + l32 * KROW + hi * 16;
-    // K fragments are read one k-step ahead of the MFMAs that consume them, so LDS latency overlaps
-    // the previous k-step's MFMAs instead of stalling every MFMA
-    bf16x8 kf[2][MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) kf[0][mt] = *(const bf16x8 *)(kb + mt * 32 * KROW);
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      if (kk + 1 < KS) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          kf[(kk + 1) & 1][mt] = *(const bf16x8 *)(kb + mt * 32 * KROW + (kk + 1) * 32);
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk & 1][mt], qf[kk], kk == 0 ? f32x16{} : s[mt], 0, 0,
-                                                        0);
-      __builtin_amdgcn_sched_barrier(0);  // keep the next k-step's reads ahead of these MFMAs
-    }
-
-    // ---- causal / tail mask (only blocks that need it) ----
-    const int key0 = t * BC;
-    const bool need_mask = (key0 + BC > Lk) || (a.causal && key0 + BC - 1 > r0 + off);
-    if (need_mask) {
-      const int lim = a.causal ? min(my_row + off, Lk - 1) : Lk - 1;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + mt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key > lim) s[mt][r] = kNegInf;
-        }
-    }
-
-    // ---- block row max, vote, critical value ----
-    float mx = kNegInf;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-    mx = max_xor32(mx);
-    if (!row_ok) mx = kNegInf;
-    if (DEC) {
-      const bool skip_row = row_votes_skip(mx, m_dec, thr_raw);
-      const bool wave_keep = __ballot(!skip_row) != 0ull;
-      float wcrit = 0.f;
-      if (a.crit) wcrit = max_lanes32(row_crit(mx, m_dec));
-      if (lane == 0) {
-        sVote[buf][wave] = wave_keep ? 1 : 0;
-        sCrit[buf][wave] = wcrit;
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K_{t+1} and V_t have landed in LDS
-    __syncthreads();
-    int keep = 1;
+    int keep = 1, keep_any = 1;
     if (DEC) {
       keep = 0;
+      keep_any = 0;
 #pragma unroll
-      for (int w = 0; w < WPT; ++w) keep |= sVote[buf][tile * WPT + w];
+      for (int w = 0; w < NW; ++w) {
+        keep_any |= sVote[buf][w];
+        if (w / WPT == tile) keep |= sVote[buf][w];
+      }
     }
     m_dec = fmaxf(m_dec, mx);
     ++live_cnt;
@@ -408,7 +385,44 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
         a.crit[mask_row + t] = c * a.scale;
       }
     }
-    mx_pend = mx;
+    if (!STATS && keep) {
+      // ---- kept block t: online-softmax update and its probabilities ----
+      // Lazy rescaling: the accumulation reference m_acc is raised only when a row's block max
+      // exceeds it by more than 2^8 in probability (a row's first finite max just sets it: O and l
+      // are still zero); below that, probabilities relative to the stale reference are at most 256,
+      // which bf16 P and the fp32 sums hold with the same relative precision, and O / l and the
+      // LSE are unchanged.  So the accumulators are rescaled only when the max jumps.  (O already
+      // holds block t - 1: its P.V ran above.)
+      if (m_acc == kNegInf) m_acc = mx;
+      if (__ballot((mx - m_acc) * a.scale_log2 > 8.f) != 0ull) {
+        const float m_new = fmaxf(m_acc, mx);
+        const float alpha = fast_exp2((m_acc - m_new) * a.scale_log2);
+        l_part *= alpha;
+        l_part2 *= alpha;
+#pragma unroll
+        for (int i = 0; i < MTV; ++i) o_acc[i] *= alpha;
+        m_acc = m_new;
+      }
+      const float base = (m_acc == kNegInf) ? 0.f : m_acc * a.scale_log2;
+      // P^T for k-step kk (16 keys): keys of score registers s[kk/2][8*(kk%2) .. +7], i.e. key
+      // 16*kk + 8*(e/4) + 4*hi + e%4 for element e.
+      const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+      for (int kk = 0; kk < KSV; ++kk) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pf_pend[kk][e] = (__bf16)fast_exp2(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + e], a.scale_log2, -base));
+        // row sum: one bf16 dot2 with (1, 1) per pair of probabilities
+        const bf16x8 pf = pf_pend[kk];
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), one2, l_part, false);
+        l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), one2, l_part2, false);
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), one2, l_part, false);
+        l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, l_part2, false);
+      }
+    }
+    // V_t only for a block that a tile of the workgroup kept (the buffer held V_{t-2}, whose P.V
+    // every wave finished before this iteration's barrier)
+    if (!STATS && keep_any) load_v(t, buf);
     keep_pend = keep != 0;
   }
 
