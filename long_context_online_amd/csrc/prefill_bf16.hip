@@ -2,9 +2,10 @@
 //
 // Method: FlashAttention-style tiled online softmax over the KV blocks of a query tile, visited
 // left to right; block j is skipped when every row of the tile has m~ - m < ln(lambda), and a
-// skipped block gets no exp and no P.V product, while QK^T is still computed for every block and
-// the V block is still staged (pages: xllm-io review, 核心公式 and 预填充内核优化; gist.science (de),
-// 2. Methodik / Kernidee and 3. Kernel-Design).
+// skipped block gets no exp and no P.V product, while QK^T is still computed for every block
+// (pages: xllm-io review, 核心公式 and 预填充内核优化; gist.science (de), 2. Methodik / Kernidee and
+// 3. Kernel-Design).  The pages keep staging the V block of a skipped block; here a skipped block's
+// V is not loaded either.
 //
 // MI355X design:
 //   * a workgroup owns TPW query tiles that read the same K/V stream (two q heads of one GQA group
@@ -18,11 +19,13 @@
 //     O^T = V^T P^T; the V^T operand is read from a row-major V tile with the gfx950 transpose
 //     read ds_read_b64_tr_b16 (within a 16-lane group, output lane i, element k is element i%4 of
 //     source lane 4k + i/4's 8-byte read), so no transpose pass is needed anywhere;
-//   * K and V both go global -> LDS directly (global_load_lds_dwordx4, no registers, no VALU) into
-//     double-buffered LDS; the block loop is software-pipelined by one block (the P.V product of
-//     block t - 1 runs in the same iteration as QK^T of block t), so ONE barrier per block both
-//     publishes the votes and makes the next K block and this V block visible, and staging a
-//     skipped block's V costs only the load instructions;
+//   * K and V go global -> LDS directly (buffer_load ... lds, no registers) into double-buffered
+//     LDS; the block loop is software-pipelined by one block: iteration t computes QK^T and the
+//     vote of block t, then ONE barrier publishes the votes and makes K_{t+1} (prefetched at the
+//     top of the iteration) and V_{t-1} visible; then the P.V product of block t - 1 runs from its
+//     probabilities packed in registers, and only if block t was kept by a tile of the workgroup
+//     are its probabilities formed and V_t loaded, so a skipped block costs QK^T, the row max and
+//     the vote and nothing else;
 //   * the skip vote: per-row predicate -> wave ballot -> one LDS flag per wave -> OR over the
 //     tile's waves after the vote barrier; the skip is a uniform branch, so a skipped block issues
 //     no v_exp and no P.V MFMA;
@@ -31,8 +34,8 @@
 //     banks), V rows 64 mod 256 bytes apart (the two 16-lane groups of a transpose-read pass read
 //     4 rows x 32 bytes each at column offsets 0 and 32); every read address is one per-lane base
 //     plus an immediate;
-//   * heavy (late, long causal) tiles launch first, and workgroups of one kv head are mapped to the
-//     same XCD (workgroups are dispatched round-robin over the 8 XCDs) for L2 reuse.
+//   * heavy (late, long causal) tiles launch first, and the q heads of one kv head share an XCD's L2
+//     for a stripe of levels (the mapping is described at the tile coordinates below).
 #include <type_traits>
 
 #include "common.hpp"
