@@ -39,7 +39,7 @@ constexpr int D = 128, PAGE = 16, BK = 64, NWAVE = 4, NB = 4;
 
 template <bool OUT_F32>
 __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
-  __shared__ float sPmax[NB][NWAVE][16];
+  __shared__ float sPmax[2][NB][NWAVE][16];  // double-buffered by batch parity
   __shared__ float sRed[NWAVE][16][D + 4];
   __shared__ float sL[NWAVE][16];
 
@@ -124,7 +124,8 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
     load_k(pid_cur);
     tab_next = load_table(j0 + NB);
   }
-  for (int jb = j0; jb < j1; jb += NB) {
+  int pbuf = 0;
+  for (int jb = j0; jb < j1; jb += NB, pbuf ^= 1) {
     const int nb = min(NB, j1 - jb);
     // ---- scores of this wave's page of each block in the batch ----
     f32x4 s[NB];
@@ -141,17 +142,25 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
         if (i >= nb || keyb + r > lim) s[i][r] = kNegInf;
       float pm = fmaxf(fmaxf(s[i][0], s[i][1]), fmaxf(s[i][2], s[i][3]));
       pm = max_xor16_32(pm);
-      if (grp == 0) sPmax[i][wave][n] = pm;
+      if (grp == 0) sPmax[pbuf][i][wave][n] = pm;
     }
+    // ---- the next batch's K loads go out now (the scores above have consumed the K registers),
+    // so they are in flight across the barrier and the decisions ----
     int pid_next[NB];
     pick(tab_next, pid_next);
+    const bool more = jb + NB < j1;
+    if (more) {
+      load_k(pid_next);
+      tab_next = load_table(jb + 2 * NB);
+    }
     __syncthreads();
     // ---- in-batch sequential decisions (identical in every wave) ----
     int keep_bits = 0;
     float mblk[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      float mb = fmaxf(fmaxf(sPmax[i][0][n], sPmax[i][1][n]), fmaxf(sPmax[i][2][n], sPmax[i][3][n]));
+      const float(&pm)[NWAVE][16] = sPmax[pbuf][i];
+      float mb = fmaxf(fmaxf(pm[0][n], pm[1][n]), fmaxf(pm[2][n], pm[3][n]));
       if (!col_ok) mb = kNegInf;
       mblk[i] = mb;
       if (i < nb) {
@@ -174,14 +183,7 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
       }
     }
     if (a.stats_only) keep_bits = 0;
-    // ---- next batch's K loads and the page ids of the batch after it, then the V loads of the
-    // surviving blocks only; all are in flight together and the PV products wait for all of them
-    // (vector loads return in order) ----
-    const bool more = jb + NB < j1;
-    if (more) {
-      load_k(pid_next);
-      tab_next = load_table(jb + 2 * NB);
-    }
+    // ---- the V loads of the surviving blocks only ----
     u32x2 vreg[NB][D / 16];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -228,7 +230,8 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) pid_cur[i] = pid_next[i];
-    __syncthreads();  // sPmax is rewritten by the next batch
+    // no barrier here: the next batch writes the other sPmax buffer, and this one is rewritten only
+    // after the next batch's barrier, which every wave reaches after its reads above
   }
 
   if (tid == 0 && a.counters) {
