@@ -95,6 +95,12 @@ __device__ __forceinline__ float row_crit(float m_blk, float m_run) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8) that
+// waits for vmcnt(0) only.  Passed to __builtin_amdgcn_s_waitcnt, the wait is visible to the
+// compiler's own wait insertion, which then takes every earlier vector load as complete (a wait
+// written as inline assembly is not).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // Workgroup barrier that waits only for this wave's LDS operations.  __syncthreads() also waits for
 // every outstanding global load (vmcnt(0)), which would stall on the next block's direct-to-LDS
 // prefetch; here those loads stay in flight and are waited for explicitly before the buffer swap.
@@ -115,6 +121,19 @@ __device__ __forceinline__ void direct_load16(const void *addr, uint32_t lds_bas
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
                : "=&s"(saved)
                : "v"(addr), "s"(lds_base));
+}
+
+// Buffer-resource form of the same direct load: 16 bytes per lane from the resource's base plus
+// voff (a 32-bit byte offset per lane; reads past the resource's num_records return zero) into LDS
+// bytes [lds_base + 16 i, lds_base + 16 i + 16).  rsrc = {base low 32 bits, base high 16 bits
+// (stride 0), num_records in bytes, 0x00020000}; every operand but voff must be wave-uniform.
+// Assembly for the same reason as direct_load16: written with the compiler builtin, a later LDS
+// read of the other half of a double buffer waits for this load (vmcnt(0)).
+__device__ __forceinline__ void buffer_load16_lds(u32x4 rsrc, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(voff), "s"(rsrc), "s"(lds_base));
 }
 
 // LDS byte address of a pointer into __shared__ memory

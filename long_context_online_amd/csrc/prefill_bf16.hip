@@ -159,8 +159,13 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     if constexpr (!PAGED) {
       static_assert(INS * 64 == BC * CP, "every position of a tile is one row chunk");
       const uint32_t row_b = (uint32_t)stride * 2u;
-      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)(base + (int64_t)key0 * stride), (short)0, (int)((uint32_t)min(Lk - key0, BC) * row_b), 0x00020000);
+      const uint64_t addr = (uint64_t)(uintptr_t)(base + (int64_t)key0 * stride);
+      u32x4 rsrc;
+      rsrc[0] = (uint32_t)addr;
+      rsrc[1] = (uint32_t)(addr >> 32) & 0xffffu;  // stride 0
+      rsrc[2] = (uint32_t)min(Lk - key0, BC) * row_b;
+      rsrc[3] = 0x00020000u;
+      const uint32_t lds0 = lds_addr(dst);
 #pragma unroll
       for (int i = 0; i < (INS + NW - 1) / NW; ++i) {
         const int ins = i * NW + wave;
@@ -169,8 +174,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
           const int row = p / CP;
           int c = p - row * CP;
           if (c >= CH) c = 0;
-          const int voff = (int)(__mul24(row, row_b) + c * 16);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(dst + ins * 1024), 16, voff, 0, 0, 0);
+          buffer_load16_lds(rsrc, __mul24(row, row_b) + c * 16, lds0 + ins * 1024);
         }
       }
       return;
@@ -264,9 +268,18 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   f32x16 s[MT];            // scores of block t
   bf16x8 pf_pend[KSV];     // bf16 probabilities of the kept block whose P.V is pending
   bool keep_pend = false;  // block t - 1 was kept by this tile
-  if (J > 0) {
-    load_k(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (PAGED) {
+    if (J > 0) {
+      load_k(0, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+  } else {
+    if (J > 0) load_k(0, 0);
+    // a wait the compiler sees (not inline asm), on every path into the loop: without it the
+    // compiler takes the Q fragments as possibly in flight at the loop head and waits for
+    // vmcnt(0), i.e. for the K prefetch just issued, before the first QK^T product of every block
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
   for (int t = 0; t <= J; ++t) {
