@@ -123,6 +123,15 @@ __device__ __forceinline__ void direct_load16(const void *addr, uint32_t lds_bas
                : "v"(addr), "s"(lds_base));
 }
 
+// 4-byte form of direct_load16 (global_load_lds_dword: lane i writes LDS bytes [lds_base + 4 i,
+// lds_base + 4 i + 4)); the same rules apply.
+__device__ __forceinline__ void direct_load4(const void *addr, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(addr), "s"(lds_base));
+}
+
 // Buffer-resource form of the same direct load: 16 bytes per lane from the resource's base plus
 // voff (a 32-bit byte offset per lane; reads past the resource's num_records return zero) into LDS
 // bytes [lds_base + 16 i, lds_base + 16 i + 16).  rsrc = {base low 32 bits, base high 16 bits

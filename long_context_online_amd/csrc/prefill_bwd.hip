@@ -324,6 +324,9 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
       kf[kk] = *(const bf16x8 *)(kp + (int64_t)key * a.ks[2] + kk * 32 + q4 * 8);
       vf[kk] = *(const bf16x8 *)(vp + (int64_t)key * a.vs[2] + kk * 32 + q4 * 8);
     }
+    // a wait the compiler sees: otherwise it takes these fragments as possibly in flight inside the
+    // pair loop and waits there for vector loads, i.e. for the next pair's staging as well
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
 
   // ---- (q head of the group, query tile) pairs p = h * nqt + t that kept this block ----
@@ -355,28 +358,40 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
     }
     return npairs;
   };
-  // LSE and D of a pair's rows travel through registers (thread t < 128: LSE of row t, 128 <= t < 256:
-  // D of row t - 128), so rows past the end and rows without any kept key get P = 0 exactly
-  auto load_ld = [&](int p) -> float {
-    const int h = p / a.nqt, t = p - (p / a.nqt) * a.nqt;
-    const int row = t * BB + (tid & (BB - 1));
-    const int64_t idx = ((int64_t)b * a.Hq + g * a.G + h) * a.Lq + row;
-    if (tid < BB) {
-      const float l = row < a.Lq ? a.lse[idx] : kNegInf;
-      return l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
-    }
-    return (tid < 2 * BB && row < a.Lq) ? a.dvec[idx] : 0.f;
-  };
-  auto store_ld = [&](int buf, float x) {
-    if (tid < BB) sL[buf][tid] = x;
-    else if (tid < 2 * BB) sD[buf][tid - BB] = x;
-  };
+  // A pair's Q and dO tiles and the LSE and D of its rows are staged by direct loads (waves 0-1: LSE,
+  // 2-3: D, 64 rows each; rows past the end read the last row), all in flight while the previous
+  // pair is processed.
+  static_assert(BB == 128, "four 64-row instructions cover LSE and D of a tile");
   auto stage = [&](int p, int buf) {
     const int h = p / a.nqt, t = p - (p / a.nqt) * a.nqt;
     const int hq = g * a.G + h;
     stage_tile((const __bf16 *)a.q + b * a.qs[0] + hq * a.qs[1], a.qs[2], t * BB, a.Lq, sQ[buf], wave, NW, lane);
     stage_tile((const __bf16 *)a.dout + b * a.dos[0] + hq * a.dos[1], a.dos[2], t * BB, a.Lq, sO[buf], wave, NW,
                lane);
+    if (wave < 4) {
+      const int row = min(t * BB + (wave & 1) * 64 + lane, a.Lq - 1);
+      const int64_t idx = ((int64_t)b * a.Hq + hq) * a.Lq + row;
+      const float *src = (wave < 2 ? (const float *)a.lse : (const float *)a.dvec) + idx;
+      direct_load4(src, lds_addr((wave < 2 ? sL[buf] : sD[buf]) + (wave & 1) * 64));
+    }
+  };
+  // After a wave's staging loads have landed (its own vmcnt(0)), each lane of waves 0-3 rewrites the
+  // value its own load wrote: LSE becomes the exponent offset LSE log2(e), +inf (P = 0 exactly) for
+  // rows without any kept key (LSE = -inf) and rows past the end, whose D becomes 0.  The next
+  // barrier publishes them.
+  auto fix_ld = [&](int p, int buf) {
+    if (wave < 4) {
+      const int t = p - (p / a.nqt) * a.nqt;
+      const int i = (wave & 1) * 64 + lane;
+      const bool ok = t * BB + i < a.Lq;
+      if (wave < 2) {
+        const float l = sL[buf][i];
+        sL[buf][i] = (!ok || l == kNegInf) ? __builtin_huge_valf() : l * kLog2e;
+      } else {
+        const float d = sD[buf][i];
+        sD[buf][i] = ok ? d : 0.f;
+      }
+    }
   };
 
   // transpose reads: 16-lane group q reads rows 4 q + (l16 / 4), columns 4 (l16 % 4) ... + 3
@@ -391,18 +406,15 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
   int pc = next(0);
   if (pc < npairs) {
     stage(pc, 0);
-    store_ld(0, load_ld(pc));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    fix_ld(pc, 0);
   }
   int buf = 0;
   while (pc < npairs) {
     const int pn = next(pc + 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // pair pc's tiles have landed in LDS
     __syncthreads();                                   // ... for every wave; buffer buf ^ 1 is free
-    float ld_next = 0.f;
-    if (pn < npairs) {
-      stage(pn, buf ^ 1);
-      ld_next = load_ld(pn);
-    }
+    if (pn < npairs) stage(pn, buf ^ 1);
     {
       const int t = pc - (pc / a.nqt) * a.nqt;
       const int row0 = t * BB;
@@ -447,7 +459,10 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
         }
       }
     }
-    if (pn < npairs) store_ld(buf ^ 1, ld_next);
+    if (pn < npairs) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // pair pn's staging has landed
+      fix_ld(pn, buf ^ 1);
+    }
     buf ^= 1;
     pc = pn;
   }
