@@ -74,6 +74,9 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   __shared__ __attribute__((aligned(16))) unsigned char sK[2][KBUF];
   __shared__ __attribute__((aligned(16))) unsigned char sV[2][VBUF];
   __shared__ int sVote[2][NW];
+  // paged: ids of the 8 pages of blocks t .. t + 3 (a ring indexed by block & 3), staged two blocks
+  // ahead by wave 0
+  __shared__ int sIds[PAGED ? 4 : 1][BC / 16];
   __shared__ float sCrit[2][NW];
 
   const int tid = threadIdx.x;
@@ -123,10 +126,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   const __bf16 *qp = (const __bf16 *)a.q + b * a.qs[0] + hq * a.qs[1];
   const __bf16 *kp = (const __bf16 *)a.k + (PAGED ? 0 : b * a.ks[0] + g * a.ks[1]);
   const __bf16 *vp = (const __bf16 *)a.v + (PAGED ? 0 : b * a.vs[0] + g * a.vs[1]);
-  // the sequence's page ids, read through the scalar cache (the addresses are wave-uniform), so page
-  // lookups wait on lgkmcnt and never on the direct loads in flight (vmcnt)
-  typedef const __attribute__((address_space(4))) int32_t *const_i32p;
-  const const_i32p tab = PAGED ? (const_i32p)(uintptr_t)(a.table + (int64_t)b * a.max_pages) : nullptr;
+  const int32_t *tab = PAGED ? a.table + (int64_t)b * a.max_pages : nullptr;  // the sequence's page ids
   const int last_page = PAGED ? (Lk - 1) >> 4 : 0;
 
   const int last_row = min(r0 + BR, a.Lq) - 1;
@@ -179,28 +179,23 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       }
       return;
     }
+    // the lane index through an empty asm: the per-lane offsets below are then recomputed at every
+    // load instead of being kept in registers across the block loop (where they spilled)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < (INS + NW - 1) / NW; ++i) {
       const int ins = i * NW + wave;
       if (ins < INS) {
-        const int p = ins * 64 + lane;
+        const int p = ins * 64 + ln;
         int row = p / CP, c = p - (p / CP) * CP;
         if (c >= CH) c = 0;
         if (row >= BC) row = 0;
         const int key = min(key0 + row, Lk - 1);
-        const __bf16 *src;
-        if constexpr (PAGED) {
-          // K row of the key's page (16 tokens per page); the instruction's rows lie on at most two
-          // pages, whose ids are read once per instruction (uniform) and picked per lane
-          const int r_lo = (ins * 64) / CP, r_hi = min((ins * 64 + 63) / CP, BC - 1);
-          const int pa = min((key0 + r_lo) >> 4, last_page), pb = min((key0 + r_hi) >> 4, last_page);
-          const int pid_a = tab[pa], pid_b = tab[pb];
-          const int pid = (key >> 4) == pa ? pid_a : pid_b;
-          src = base + ((int64_t)pid * a.Hkv + g) * (16 * D) + (key & 15) * D + c * 8;
-        } else {
-          src = base + (int64_t)key * stride + c * 8;
-        }
-        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst + ins * 1024), 16, 0, 0);
+        // K row of the key's page (16 tokens per page), the page id from the block's staged ids
+        const int pid = sIds[j & 3][(key >> 4) - (key0 >> 4)];
+        const __bf16 *src = base + ((int64_t)pid * a.Hkv + g) * (16 * D) + (key & 15) * D + c * 8;
+        direct_load16(src, lds_addr(dst + ins * 1024));
       }
     }
   };
@@ -215,24 +210,19 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   static_assert(!PAGED || (D == 128 && BC == 128 && VTINS * 1024 <= VBUF), "paged tiles are 128 x 128");
   auto load_v = [&](int j, int buf) {
     if constexpr (PAGED) {
-      const int kp0 = j * (BC / 16);
-      int pids[BC / 16];   // ids of the block's 8 pages (uniform), picked per lane below
-#pragma unroll
-      for (int i = 0; i < BC / 16; ++i) pids[i] = tab[min(kp0 + i, last_page)];
+      int ln = lane;   // recomputed offsets, as for K
+      asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int i = 0; i < (VTINS + NW - 1) / NW; ++i) {
         const int ins = i * NW + wave;
         if (ins < VTINS) {
-          const int p = ins * 64 + lane;
+          const int p = ins * 64 + ln;
           const int dv = p / VTCP;
           int c = p - dv * VTCP;
           if (c >= 16) c = 0;
-          int pid = pids[0];
-#pragma unroll
-          for (int q = 1; q < BC / 16; ++q)
-            if ((c >> 1) == q) pid = pids[q];
+          const int pid = sIds[j & 3][c >> 1];
           const __bf16 *src = vp + (((int64_t)pid * a.Hkv + g) * D + dv) * 16 + (c & 1) * 8;
-          __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(sV[buf] + ins * 1024), 16, 0, 0);
+          direct_load16(src, lds_addr(sV[buf] + ins * 1024));
         }
       }
     } else {
@@ -240,6 +230,17 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
                 std::integral_constant<int, VINS>{});
     }
   };
+  // Paged: wave 0 stages the ids of block j's 8 pages (clamped to the sequence's last page) into ring
+  // slot j & 3, 4 bytes per lane.  Slot j & 3 is refilled (for block j + 4, at the top of iteration
+  // j + 2) only after the barrier of iteration j + 1, which every wave reaches after its last read of
+  // the slot (the V_j loads at the end of iteration j); the ids are read after the barrier that
+  // follows the loads' wait.
+  auto stage_ids = [&](int j) {
+    if constexpr (PAGED) {
+      if (wave == 0 && lane < BC / 16) direct_load4(tab + min(j * (BC / 16) + lane, last_page), lds_addr(sIds[j & 3]));
+    }
+  };
+
   // Transpose-read addressing for the V^T operand of k-step kk, dv m-tile mv: source lane
   // j = 4k + q of 16-lane group G points at V[16 kk + 4 (G / 2) + k][32 mv + 16 (G % 2) + 4 q ...+3];
   // the second read covers keys + 8.  Output lane l then holds dv 32 mv + l % 32 and the keys of
@@ -268,22 +269,21 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   f32x16 s[MT];            // scores of block t
   bf16x8 pf_pend[KSV];     // bf16 probabilities of the kept block whose P.V is pending
   bool keep_pend = false;  // block t - 1 was kept by this tile
-  if constexpr (PAGED) {
-    if (J > 0) {
-      load_k(0, 0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-    }
-  } else {
-    if (J > 0) load_k(0, 0);
-    // a wait the compiler sees (not inline asm), on every path into the loop: without it the
-    // compiler takes the Q fragments as possibly in flight at the loop head and waits for
-    // vmcnt(0), i.e. for the K prefetch just issued, before the first QK^T product of every block
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if (PAGED && J > 0) {
+    stage_ids(0);
+    if (J > 1) stage_ids(1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
+  if (J > 0) load_k(0, 0);
+  // a wait the compiler sees (not inline asm), on every path into the loop: without it the compiler
+  // takes the Q fragments as possibly in flight at the loop head and waits for vmcnt(0), i.e. for the
+  // K prefetch just issued, before the first QK^T product of every block
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
   for (int t = 0; t <= J; ++t) {
     const int buf = t & 1;
+    if (t + 2 < J) stage_ids(t + 2);
     if (t + 1 < J) load_k(t + 1, buf ^ 1);
     float mx = kNegInf;
     if (t < J) {
