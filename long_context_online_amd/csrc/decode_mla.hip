@@ -113,8 +113,11 @@ __global__ __launch_bounds__(NT, 1) void decode_mla_kernel(DecodeArgs a) {
   const char *kc = (const char *)a.kc;
   const int32_t *table = a.table + (int64_t)b * a.max_pages;
   constexpr int64_t kPageBytes = (int64_t)PAGE * DQK * 2;  // one kv head
-  auto load_block = [&](int j, int buf) {
-    const int pid = __builtin_amdgcn_readfirstlane(table[min(j * (BK / PAGE) + wave, npg - 1)]);
+  // this wave's page of block j; read one block ahead of its use, so that taking it into a scalar
+  // register never waits on memory (the loop drains all loads at its end)
+  auto page_id = [&](int j) -> int { return table[min(j * (BK / PAGE) + wave, npg - 1)]; };
+  auto load_block = [&](int pid_raw, int buf) {
+    const int pid = __builtin_amdgcn_readfirstlane(pid_raw);
     const char *base = kc + (int64_t)pid * kPageBytes;  // wave-uniform
     const uint32_t lbase = lds_addr(sK[buf] + wave * PGB);
 #pragma unroll
@@ -155,15 +158,20 @@ __global__ __launch_bounds__(NT, 1) void decode_mla_kernel(DecodeArgs a) {
     skip_cnt = 0;
     bool redo = false;
 
+    int pid_next = 0;  // page id of block j + 1 (this wave's page)
     if (j0 < j1) {
-      load_block(j0, 0);
+      load_block(page_id(j0), 0);
+      pid_next = page_id(j0 + 1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
     for (int j = j0; j < j1; ++j) {
       const int buf = (j - j0) & 1;
       const bool has_next = j + 1 < j1;
-      if (has_next) load_block(j + 1, buf ^ 1);
+      if (has_next) {
+        load_block(pid_next, buf ^ 1);
+        pid_next = page_id(j + 2);
+      }
       const int key0 = j * BK;
       if (key0 + BK > L) {
         // slots past the sequence end hold arbitrary bytes: zero them so that P = 0 meets V = 0
