@@ -299,9 +299,10 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
 }
 
 // Log-sum-exp merge of the per-split partials: one wave per (sequence, q head), four per
-// workgroup.  Lane s < S reads lse_s to form the global max and sum; each lane then owns CPL output
-// channels (pairs 2 * lane + 128 k), and the partial rows of SC splits are loaded together before
-// any is used, so the loads of a chunk overlap instead of paying one memory latency per split.
+// workgroup.  Each lane owns CPL output channels (pairs 2 * lane + 128 k).  The splits are merged in
+// chunks of SC with a running max: every load of a chunk (the SC lse values, the same in every lane,
+// and the lane's channels of the SC partial rows) is issued before any is used, so a chunk costs one
+// memory latency; with S <= SC (the usual case) the whole merge is one round trip.
 template <bool OUT_F32, int CPL>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float *ws_o, const float *ws_lse, void *o,
                                                               float *lse_out, int BH, int S) {
@@ -310,20 +311,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *ws_o, 
   const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (bh >= BH) return;
   const float *pl = ws_lse + (int64_t)bh * S;
-  float my = kNegInf;
-  for (int s = lane; s < S; s += 64) my = fmaxf(my, pl[s]);
-  float mx = my;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  float tot = 0.f;
-  for (int s = lane; s < S; s += 64) tot += (pl[s] == kNegInf) ? 0.f : __expf(pl[s] - mx);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const float *po = ws_o + (int64_t)bh * S * Dv + lane * 2;
+  float mx = kNegInf, tot = 0.f;  // running max and sum of exp(lse_s - mx) over the merged splits
   float2 acc[NP];
 #pragma unroll
   for (int k = 0; k < NP; ++k) acc[k] = make_float2(0.f, 0.f);
-  const float *po = ws_o + (int64_t)bh * S * Dv + lane * 2;
   for (int s0 = 0; s0 < S; s0 += SC) {
     float ls[SC];
     float2 v[SC][NP];
@@ -335,16 +327,30 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float *ws_o, 
       for (int k = 0; k < NP; ++k)
         v[u][k] = ok ? *(const float2 *)(po + (int64_t)(s0 + u) * Dv + 128 * k) : make_float2(0.f, 0.f);
     }
+    float cm = mx;
+#pragma unroll
+    for (int u = 0; u < SC; ++u) cm = fmaxf(cm, ls[u]);
+    if (cm == kNegInf) continue;  // no split so far saw a key
+    const float r = mx == kNegInf ? 0.f : __expf(mx - cm);  // rescale of what was merged before
+    tot *= r;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      acc[k].x *= r;
+      acc[k].y *= r;
+    }
 #pragma unroll
     for (int u = 0; u < SC; ++u) {
-      const float w = ls[u] == kNegInf ? 0.f : __expf(ls[u] - mx);
+      const float w = ls[u] == kNegInf ? 0.f : __expf(ls[u] - cm);
+      tot += w;
 #pragma unroll
       for (int k = 0; k < NP; ++k) {
         acc[k].x += w * v[u][k].x;
         acc[k].y += w * v[u][k].y;
       }
     }
+    mx = cm;
   }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
   for (int k = 0; k < NP; ++k) {
     const int c = lane * 2 + 128 * k;
