@@ -36,18 +36,28 @@ typedef __attribute__((address_space(3))) bv4i16 lds_bv4i16;
 
 constexpr int BD = 128;               // head dim of q, k and v
 constexpr int BB = 128;               // rows of a query tile = keys of a key block
-constexpr int ROWB = 272;             // LDS bytes per staged row: 256 + 16 (16 mod 256)
-constexpr int CPR = ROWB / 16;        // 16-byte positions per row (the 17th re-reads chunk 0)
-constexpr int TINS = BB * CPR / 64;   // wave-wide direct loads per tile (2176 positions = 34 x 64)
-constexpr int TILEB = TINS * 1024;    // bytes per staged tile
+// LDS row strides of the staged 128 x 128 bf16 tiles (256 data bytes + pad), chosen per tile from
+// the LDS bank conflicts measured for each read pattern (a probe of the exact patterns, stride by
+// stride): rows read as the A operand of 32x32x16 products are conflict-free at 16 mod 64 bytes;
+// transpose reads for 32x32x16 operands only at 64 mod 256; rows and transpose reads for
+// 16x16x32 operands only at 32 mod 256.
+constexpr int ROW_DQ_K = 304;   // dQ kernel K tile: rows for S^T, transpose reads for dQ^T (2-way there)
+constexpr int ROW_DQ_V = 272;   // dQ kernel V tile: rows only
+constexpr int ROW_DKV = 288;    // dK/dV kernel Q and dO tiles: 16x16x32 rows and transpose reads
+template <int ROWB>
+constexpr int tile_ins() { return BB * (ROWB / 16) / 64; }   // wave-wide direct loads per tile
+template <int ROWB>
+constexpr int tile_bytes() { return tile_ins<ROWB>() * 1024; }
 
 // Direct global -> LDS loads of one 128-row x 128-element bf16 tile (rows row0 ... row0 + 127 of a
-// row-major matrix with `stride` elements per row) into an LDS tile of ROWB-byte rows.  Wave `wave`
-// of `nw` issues instructions wave, wave + nw, ...; rows at or past `nrows` re-read row nrows - 1,
-// so every lane reads valid memory.
+// row-major matrix with `stride` elements per row) into an LDS tile of ROWB-byte rows (pad positions
+// re-read chunk 0 of their row).  Wave `wave` of `nw` issues instructions wave, wave + nw, ...; rows
+// at or past `nrows` re-read row nrows - 1, so every lane reads valid memory.
+template <int ROWB>
 __device__ __forceinline__ void stage_tile(const __bf16 *base, int64_t stride, int row0, int nrows,
                                            unsigned char *dst, int wave, int nw, int lane) {
-  for (int ins = wave; ins < TINS; ins += nw) {
+  constexpr int CPR = ROWB / 16;
+  for (int ins = wave; ins < tile_ins<ROWB>(); ins += nw) {
     const int p = ins * 64 + lane;
     const int row = p / CPR;
     int c = p - row * CPR;
@@ -60,6 +70,7 @@ __device__ __forceinline__ void stage_tile(const __bf16 *base, int64_t stride, i
 // Transpose read of one k-step (16 rows of the tile) for an A operand X^T, X row-major in LDS:
 // output lane l holds column 32 mv + l % 32 of X and the 8 rows of its lane half in the order of the
 // B operand taken from accumulator registers 8 (ks % 2) ... + 7 of m-tile ks / 2.
+template <int ROWB>
 __device__ __forceinline__ bf16x8 tr_operand(const unsigned char *t, int ks, int mv) {
   const bv4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bv4i16 *)(t + ks * 16 * ROWB + mv * 64));
   const bv4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bv4i16 *)(t + (ks * 16 + 8) * ROWB + mv * 64));
@@ -68,6 +79,7 @@ __device__ __forceinline__ bf16x8 tr_operand(const unsigned char *t, int ks, int
 
 // Byte offset of a lane's transpose reads inside a tile (16-lane group G, lane j of it: row
 // 4 (G / 2) + j / 4, columns 16 (G % 2) + 4 (j % 4) ... + 3).
+template <int ROWB>
 __device__ __forceinline__ int tr_lane_offset(int lane) {
   const int g = lane >> 4, j = lane & 15;
   return ((g >> 1) * 4 + (j >> 2)) * ROWB + (16 * (g & 1) + 4 * (j & 3)) * 2;
@@ -96,8 +108,8 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
   constexpr int KS = BD / 16;    // k-steps over the head dim
   constexpr int MT = BB / 32;    // key m-tiles of a block
   constexpr int MV = BD / 32;    // dim m-tiles of dQ^T
-  __shared__ __attribute__((aligned(16))) unsigned char sK[2][TILEB];
-  __shared__ __attribute__((aligned(16))) unsigned char sV[2][TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char sK[2][tile_bytes<ROW_DQ_K>()];
+  __shared__ __attribute__((aligned(16))) unsigned char sV[2][tile_bytes<ROW_DQ_V>()];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -196,11 +208,11 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
   };
   auto mine = [&](int j) -> bool { return (((tile ? w1 : w0) >> (j - wbase)) & 1ull) != 0ull; };
   auto stage = [&](int j, int buf) {
-    stage_tile(kp, a.ks[2], j * BB, a.Lk, sK[buf], wave, NW, lane);
-    stage_tile(vp, a.vs[2], j * BB, a.Lk, sV[buf], wave, NW, lane);
+    stage_tile<ROW_DQ_K>(kp, a.ks[2], j * BB, a.Lk, sK[buf], wave, NW, lane);
+    stage_tile<ROW_DQ_V>(vp, a.vs[2], j * BB, a.Lk, sV[buf], wave, NW, lane);
   };
 
-  const int tr_off = tr_lane_offset(lane);
+  const int tr_off = tr_lane_offset<ROW_DQ_K>(lane);
   f32x16 dq_acc[MV];
 #pragma unroll
   for (int i = 0; i < MV; ++i) dq_acc[i] = f32x16{};
@@ -216,8 +228,8 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
     __syncthreads();                                   // ... for every wave; buffer buf ^ 1 is free
     if (jn < J) stage(jn, buf ^ 1);
     if (keep_c) {
-      const unsigned char *kb = sK[buf] + l32 * ROWB + hi * 16;
-      const unsigned char *vb = sV[buf] + l32 * ROWB + hi * 16;
+      const unsigned char *kb = sK[buf] + l32 * ROW_DQ_K + hi * 16;
+      const unsigned char *vb = sV[buf] + l32 * ROW_DQ_V + hi * 16;
       const unsigned char *kt = sK[buf] + tr_off;
       const int key0 = jc * BB;
       const bool need_mask = (key0 + BB > a.Lk) || (a.causal && key0 + BB - 1 > r0 + off);
@@ -227,8 +239,8 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-          const bf16x8 kf = *(const bf16x8 *)(kb + mt * 32 * ROWB + kk * 32);
-          const bf16x8 vf = *(const bf16x8 *)(vb + mt * 32 * ROWB + kk * 32);
+          const bf16x8 kf = *(const bf16x8 *)(kb + mt * 32 * ROW_DQ_K + kk * 32);
+          const bf16x8 vf = *(const bf16x8 *)(vb + mt * 32 * ROW_DQ_V + kk * 32);
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[kk], dp, 0, 0, 0);
         }
@@ -250,7 +262,7 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
           for (int mv = 0; mv < MV; ++mv)
-            dq_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kt, 2 * mt + k2, mv), dsf[k2],
+            dq_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<ROW_DQ_K>(kt, 2 * mt + k2, mv), dsf[k2],
                                                                  dq_acc[mv], 0, 0, 0);
       }
     }
@@ -279,6 +291,7 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
 // 16 mv + l % 16 and rows 32 ks + 4 q ... + 3 and 32 ks + 16 + 4 q ... + 3, the order in which the
 // C layout of two consecutive 16-row S slices holds them (so P and dS feed the B operand as they are).
 __device__ __forceinline__ bf16x8 tr_operand16(const unsigned char *t, int ks, int mv) {
+  constexpr int ROWB = ROW_DKV;
   const bv4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bv4i16 *)(t + ks * 32 * ROWB + mv * 32));
   const bv4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bv4i16 *)(t + (ks * 32 + 16) * ROWB + mv * 32));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -290,8 +303,9 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int KS = BD / 32;    // k-steps of 32 over the head dim
   constexpr int NSL = BB / 16;   // 16-row slices of a query tile
   constexpr int MV = BD / 16;    // 16-wide dim tiles of dK^T, dV^T
-  __shared__ __attribute__((aligned(16))) unsigned char sQ[2][TILEB];
-  __shared__ __attribute__((aligned(16))) unsigned char sO[2][TILEB];   // dO tiles
+  constexpr int ROWB = ROW_DKV;
+  __shared__ __attribute__((aligned(16))) unsigned char sQ[2][tile_bytes<ROWB>()];
+  __shared__ __attribute__((aligned(16))) unsigned char sO[2][tile_bytes<ROWB>()];   // dO tiles
   __shared__ __attribute__((aligned(16))) float sL[2][BB];              // LSE * log2(e) of the tile's rows
   __shared__ __attribute__((aligned(16))) float sD[2][BB];              // D of the tile's rows
 
@@ -365,9 +379,10 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
   auto stage = [&](int p, int buf) {
     const int h = p / a.nqt, t = p - (p / a.nqt) * a.nqt;
     const int hq = g * a.G + h;
-    stage_tile((const __bf16 *)a.q + b * a.qs[0] + hq * a.qs[1], a.qs[2], t * BB, a.Lq, sQ[buf], wave, NW, lane);
-    stage_tile((const __bf16 *)a.dout + b * a.dos[0] + hq * a.dos[1], a.dos[2], t * BB, a.Lq, sO[buf], wave, NW,
-               lane);
+    stage_tile<ROWB>((const __bf16 *)a.q + b * a.qs[0] + hq * a.qs[1], a.qs[2], t * BB, a.Lq, sQ[buf], wave, NW,
+                     lane);
+    stage_tile<ROWB>((const __bf16 *)a.dout + b * a.dos[0] + hq * a.dos[1], a.dos[2], t * BB, a.Lq, sO[buf], wave,
+                     NW, lane);
     if (wave < 4) {
       const int row = min(t * BB + (wave & 1) * 64 + lane, a.Lq - 1);
       const int64_t idx = ((int64_t)b * a.Hq + hq) * a.Lq + row;
