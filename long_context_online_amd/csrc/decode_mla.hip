@@ -183,18 +183,25 @@ __global__ __launch_bounds__(NT, 1) void decode_mla_kernel(DecodeArgs a) {
       // ---- S^T = K_j q^T (keys 32 mt + 8 (r / 4) + 4 hi + r % 4 of register r) ----
       f32x16 s[MT];
       const unsigned char *kb = sK[buf] + l32 * ROW + hi * 16;
-      bf16x8 kf[2][MT];
+      // K fragments are read KPF k-steps ahead into a ring (one wave per SIMD: nothing else hides the
+      // LDS latency behind the two MFMAs of a k-step)
+      constexpr int KPF = 2;
+      bf16x8 kf[KPF + 1][MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) kf[0][mt] = *(const bf16x8 *)(kb + mt * 32 * ROW);
+      for (int p = 0; p < KPF; ++p)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) kf[p][mt] = *(const bf16x8 *)(kb + mt * 32 * ROW + p * 32);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        if (kk + 1 < KS) {
+        if (kk + KPF < KS) {
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) kf[(kk + 1) & 1][mt] = *(const bf16x8 *)(kb + mt * 32 * ROW + (kk + 1) * 32);
+          for (int mt = 0; mt < MT; ++mt)
+            kf[(kk + KPF) % (KPF + 1)][mt] = *(const bf16x8 *)(kb + mt * 32 * ROW + (kk + KPF) * 32);
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk & 1][mt], qf[kk], kk == 0 ? f32x16{} : s[mt], 0, 0, 0);
+          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % (KPF + 1)][mt], qf[kk], kk == 0 ? f32x16{} : s[mt], 0,
+                                                          0, 0);
         if ((kk & 1) == 1) __builtin_amdgcn_sched_barrier(0);
       }
       if (key0 + BK > L) {
