@@ -89,11 +89,12 @@ def _compare(d, res, *, splits, lam=None, a=None, tiles=None, tile_rows=0, out_b
     return rep
 
 
-@pytest.mark.parametrize("splits", [1, 3, 16])
+@pytest.mark.parametrize("splits", [1, 3, 16, 24])
 @pytest.mark.parametrize("a", [0.0, 2.0, 20.0])
 def test_gqa_paged_ragged(splits, a):
     """32 q / 8 kv heads, d = 128, ragged sequence lengths (including a one-page and a one-token
-    sequence), 16-token pages in a permuted pool with NaN spare pages."""
+    sequence), 16-token pages in a permuted pool with NaN spare pages.  24 splits: the combine merges
+    two chunks of splits, and splits past a sequence's blocks hold empty partials."""
     m = _lib()
     lens = [1000, 64, 17, 2048, 1, 333]
     d = synth.decode_inputs(batch=len(lens), hq=32, hkv=8, ctx=None, d=128, seq_lens=lens, seed=3,
@@ -157,7 +158,7 @@ def test_gqa_decode_full_size_sampled(ctx):
 
 
 @pytest.mark.parametrize("tile_rows", [128, 64])
-@pytest.mark.parametrize("splits", [1, 4])
+@pytest.mark.parametrize("splits", [1, 4, 12])
 @pytest.mark.parametrize("a", [0.0, 2.0, 20.0])
 def test_latent_mla_ragged(tile_rows, splits, a):
     """Latent attention: 128 q heads on one 576-channel latent head, V = first 512 channels, ragged

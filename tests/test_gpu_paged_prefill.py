@@ -159,3 +159,16 @@ def test_chunk_of_32k_contexts_sampled_tiles():
     rep = _compare(d, res, splits=1, a=float(L) * 0.02, tiles=tiles)
     mh = res[2].cpu().numpy()
     print(f"sparsity {(mh == 1).sum() / (mh != 2).sum():.3f}; {rep}")
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_paged_prefill_one_to_three_blocks(splits):
+    """Contexts of 100, 128, 129, 256 and 257 keys (one, one, two, two and three 128-key blocks, the
+    last page partly filled or full) with a 64-token chunk: the first blocks' page ids, which the
+    kernel stages before its block loop, and sequences that end inside or at the end of a page."""
+    m = _lib()
+    d = synth.decode_inputs(batch=5, hq=8, hkv=2, ctx=None, d=128, seq_lens=[100, 128, 129, 256, 257], seed=105,
+                            device="cuda", num_q_tokens=64)
+    res = _run(m, d, splits=splits, lam=0.02)
+    rep = _compare(d, res, splits=splits, lam=0.02)
+    print(f"S={splits}: {rep}")
