@@ -46,6 +46,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((ext_vector_type(4))) short v4i16;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
+// Paged key order inside each 32-key group of a K tile: LDS row m = 8 a + 4 h + b holds key
+// 16 (a / 2) + 8 h + 4 (a % 2) + b.  The 32x32 score layout gives register r of lane half h the row
+// 8 (r / 4) + 4 h + r % 4, so with this order the 8 probabilities a lane packs for one k-step of the
+// P.V product (registers 8 s ... 8 s + 7) are the consecutive keys 16 s + 8 h ... + 7, and their V^T
+// operand is one 16-byte read of a V^T row (the natural order needs two 8-byte reads, which conflict
+// on LDS banks at every row stride).
+__device__ __forceinline__ int paged_key_of_row(int m) {
+  const int a = m >> 3, h = (m >> 2) & 1, b = m & 3;
+  return (m & ~31) + 16 * ((a & 3) >> 1) + 8 * h + 4 * (a & 1) + b;
+}
+
 // DEC = false: no threshold at all (every live block kept, no vote); used to measure what the
 // decisions cost.  PAGED = true: K and V come from a paged cache (chunked prefill; head dim 128,
 // 128-key blocks of eight 16-token pages): K rows are gathered page by page, and V, which the cache
@@ -191,7 +202,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
         int row = p / CP, c = p - (p / CP) * CP;
         if (c >= CH) c = 0;
         if (row >= BC) row = 0;
-        const int key = min(key0 + row, Lk - 1);
+        const int key = min(key0 + paged_key_of_row(row), Lk - 1);
         // K row of the key's page (16 tokens per page), the page id from the block's staged ids
         const int pid = sIds[j & 3][(key >> 4) - (key0 >> 4)];
         const __bf16 *src = base + ((int64_t)pid * a.Hkv + g) * (16 * D) + (key & 15) * D + c * 8;
@@ -319,7 +330,8 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = key0 + mt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const int kr = mt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);   // K tile row
+            const int key = key0 + (PAGED ? paged_key_of_row(kr) : kr);
             if (key > lim) s[mt][r] = kNegInf;
           }
       }
@@ -349,30 +361,27 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       // ---- kept block t - 1: O^T += V^T P^T ----
       const unsigned char *vb = sV[buf ^ 1] + tr_off;
       // paged: V^T row reads; keys past the sequence end hold arbitrary bytes and get V = 0
-      const unsigned char *vtb = sV[buf ^ 1] + l32 * VTROW + hi * 8;
+      const unsigned char *vtb = sV[buf ^ 1] + l32 * VTROW + hi * 16;
       const int vkey0 = (t - 1) * BC;
       const bool vtail = PAGED && vkey0 + BC > Lk;
 #pragma unroll
       for (int kk = 0; kk < KSV; ++kk) {
 #pragma unroll
         for (int mv = 0; mv < MTV; ++mv) {
-          v4i16 lo, up;
+          bf16x8 vf;
           if constexpr (PAGED) {
-            // keys 16 kk + 4 hi ... + 3 and 16 kk + 8 + 4 hi ... + 3 of dv row 32 mv + l32
-            lo = *(const v4i16 *)(vtb + mv * 32 * VTROW + kk * 32);
-            up = *(const v4i16 *)(vtb + mv * 32 * VTROW + kk * 32 + 16);
+            // keys 16 kk + 8 hi ... + 7 of dv row 32 mv + l32 (the paged key order of the scores)
+            vf = *(const bf16x8 *)(vtb + mv * 32 * VTROW + kk * 32);
             if (vtail) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                if (vkey0 + 16 * kk + 4 * hi + e >= Lk) lo[e] = 0;
-                if (vkey0 + 16 * kk + 8 + 4 * hi + e >= Lk) up[e] = 0;
-              }
+              for (int e = 0; e < 8; ++e)
+                if (vkey0 + 16 * kk + 8 * hi + e >= Lk) vf[e] = (__bf16)0.f;
             }
           } else {
-            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + kk * 16 * VROW + mv * 64));
-            up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + (kk * 16 + 8) * VROW + mv * 64));
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + kk * 16 * VROW + mv * 64));
+            const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + (kk * 16 + 8) * VROW + mv * 64));
+            vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
           }
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
           o_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf_pend[kk], o_acc[mv], 0, 0, 0);
         }
       }
