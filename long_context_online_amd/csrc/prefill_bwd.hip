@@ -439,10 +439,14 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
       const unsigned char *qtr = sQ[buf] + tr_off;
       const unsigned char *otr = sO[buf] + tr_off;
       // one k-step of 32 rows = two 16-row slices: S and dP (C layout: lane holds key my_key and
-      // rows 16 sl + 4 q4 ... + 3), then P and dS as B operands, then dV^T and dK^T
-#pragma unroll 2
-      for (int ks = 0; ks < NSL / 2; ++ks) {
-        f32x4 s[2] = {f32x4{}, f32x4{}}, dp[2] = {f32x4{}, f32x4{}};
+      // rows 16 sl + 4 q4 ... + 3), then P and dS as B operands, then dV^T and dK^T.  Software-
+      // pipelined by one k-step: the S and dP products of k-step ks + 1 are issued before the
+      // exponentials and the dV^T / dK^T products of k-step ks, so the MFMA and LDS pipes are fed
+      // while a k-step's products are still in flight.
+      f32x4 s[2][2], dp[2][2];   // [k-step parity][slice]
+      auto sdp = [&](int ks) {
+        const int u = ks & 1;
+        s[u][0] = s[u][1] = dp[u][0] = dp[u][1] = f32x4{};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
@@ -450,9 +454,15 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
             const int sl = 2 * ks + h2;
             const bf16x8 qa = *(const bf16x8 *)(qb + sl * 16 * ROWB + kk * 64);
             const bf16x8 oa = *(const bf16x8 *)(ob + sl * 16 * ROWB + kk * 64);
-            s[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[kk], s[h2], 0, 0, 0);
-            dp[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[kk], dp[h2], 0, 0, 0);
+            s[u][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[kk], s[u][h2], 0, 0, 0);
+            dp[u][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[kk], dp[u][h2], 0, 0, 0);
           }
+      };
+      sdp(0);
+#pragma unroll
+      for (int ks = 0; ks < NSL / 2; ++ks) {
+        if (ks + 1 < NSL / 2) sdp(ks + 1);
+        const int u = ks & 1;
         bf16x8 pf, dsf;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
@@ -461,10 +471,10 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
           const f32x4 d4 = *(const f32x4 *)&sD[buf][rr];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float p = fast_exp2(__builtin_fmaf(s[h2][e], a.scale_log2, -l4[e]));
+            float p = fast_exp2(__builtin_fmaf(s[u][h2][e], a.scale_log2, -l4[e]));
             if (need_mask && my_key > row0 + rr + e + off) p = 0.f;
             pf[4 * h2 + e] = (__bf16)p;
-            dsf[4 * h2 + e] = (__bf16)(p * (dp[h2][e] - d4[e]) * a.scale);
+            dsf[4 * h2 + e] = (__bf16)(p * (dp[u][h2][e] - d4[e]) * a.scale);
           }
         }
 #pragma unroll
