@@ -258,8 +258,8 @@ __global__ __launch_bounds__(NT, 1) void decode_mla_kernel(DecodeArgs a) {
         const float base = (m_ref == kNegInf) ? 0.f : m_ref * a.scale_log2;
         const unsigned char *vb = sK[buf] + tr_off;
         const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-#pragma unroll
-        for (int kk = 0; kk < KSV; ++kk) {
+        // bf16 probabilities of k-step kk (the B operand) and their sums
+        auto make_pf = [&](int kk) -> bf16x8 {
           bf16x8 pf;
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -268,29 +268,43 @@ __global__ __launch_bounds__(NT, 1) void decode_mla_kernel(DecodeArgs a) {
           l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), one2, l_part2, false);
           l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), one2, l_part, false);
           l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, l_part2, false);
-          // V^T fragments are read PF m-tiles ahead into a ring of PF + 1 slots (with one wave per
-          // SIMD nothing else hides the LDS latency; the written-out MFMAs keep their order, so the
-          // reads are placed ahead of them in program order)
-          constexpr int PF = 7;
-          bf16x8 vring[PF + 1];
-          auto read_v = [&](int mv) {
-            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + kk * 16 * ROW + mv * 64));
-            const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + (kk * 16 + 8) * ROW + mv * 64));
-            vring[mv % (PF + 1)] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
-          };
+          return pf;
+        };
+        // One pass over (k-step kk, dv tile mv) = step q: V^T fragments are read PF steps ahead into a
+        // ring of PF + 1 slots, continuing across k-steps (with one wave per SIMD nothing else hides
+        // the LDS latency; the written-out MFMAs keep their order, so the reads are placed ahead of
+        // them in program order), and the probabilities of k-step kk + 1 are formed halfway through
+        // the MFMAs of k-step kk, so their VALU work overlaps MFMAs in flight.
+        constexpr int PF = 7, NQ = KSV * MTV;
+        bf16x8 vring[PF + 1];
+        auto read_v = [&](int q) {
+          const int kk = q / MTV, mv = q % MTV;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + kk * 16 * ROW + mv * 64));
+          const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + (kk * 16 + 8) * ROW + mv * 64));
+          vring[q % (PF + 1)] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        bf16x8 pfs[2];
+        pfs[0] = make_pf(0);
 #pragma unroll
-          for (int mv = 0; mv < PF; ++mv) read_v(mv);
+        for (int q = 0; q < PF; ++q) read_v(q);
 #pragma unroll
-          for (int mv = 0; mv < MTV; ++mv) {
-            if (mv + PF < MTV) read_v(mv + PF);
-            // s_nop 3: wait states after the VALU writes of the operands (the compiler does not
-            // track hazards of inline assembly)
-            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                         : "+a"(o_acc[mv])
-                         : "v"(vring[mv % (PF + 1)]), "v"(pf));
+        for (int q = 0; q < NQ; ++q) {
+          const int kk = q / MTV, mv = q % MTV;
+          if (q + PF < NQ) read_v(q + PF);
+          // s_nop 3: wait states after the VALU writes of the operands (the compiler does not
+          // track hazards of inline assembly)
+          asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                       : "+a"(o_acc[mv])
+                       : "v"(vring[q % (PF + 1)]), "v"(pfs[kk & 1]));
+          if (mv == MTV / 2 && kk + 1 < KSV) {
+            // the slot written here was last read by the MFMAs of k-step kk - 1, at least MTV / 2
+            // MFMAs ago
+            __builtin_amdgcn_sched_barrier(0);
+            pfs[(kk + 1) & 1] = make_pf(kk + 1);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (has_next) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
