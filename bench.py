@@ -42,9 +42,12 @@ D_TARGET = 0.73
 CALIB_TILES = 8  # prefill calibration sample: 8 query tiles of 128 rows (1024 rows)
 # latent (MLA-shaped) decode
 M_B, M_HQ, M_D, M_DV, M_CTX, M_TARGETS = 64, 128, 576, 512, 32768, (0.5, 0.73)
+# 8 splits: 512 workgroups of 64 blocks; with 16 the per-split first blocks (always kept) cap the
+# sparsity at 65 % even at lambda = 1, and the partials to merge double (see mla_decode.splits_sweep)
+M_SPLITS = 8
 DEC_KERNEL = {False: "decode_gqa_kernel<false>", True: "decode_mla_kernel<false, false>"}
 MLA_WORKLOAD = ("latent decode, DeepSeek-shaped: batch 64, 128 q heads on one latent head, 576-dim scores, "
-                "V = first 512 channels, context 32768, 16-token pages, 64-token blocks, 16 splits, 128-head "
+                "V = first 512 channels, context 32768, 16-token pages, 64-token blocks, 8 splits, 128-head "
                 "tiles, bf16")
 # calibration sweep
 C_L_VALUES = (4096, 8192, 16384, 32768, 65536, 131072)
@@ -237,10 +240,12 @@ class Prefill:
 
 
 class Decode:
-    def __init__(self, m, torch, synth, ctx=D_CTX, latent=False, seed=None, num_q_tokens=None, tile_rows=None):
+    def __init__(self, m, torch, synth, ctx=D_CTX, latent=False, seed=None, num_q_tokens=None, tile_rows=None,
+                 splits=None):
         self.m = m
         self.torch = torch
         self.latent = latent
+        self.splits = splits if splits is not None else (M_SPLITS if latent else D_SPLITS)
         self.ctx = ctx
         self.T = 1 if num_q_tokens is None else num_q_tokens
         dev = "cuda"
@@ -263,7 +268,7 @@ class Decode:
         self.ws = torch.empty(n, dtype=torch.uint8, device=dev)
 
     def _kw(self, lam):
-        return dict(page_size=D_PAGE, block_k=D_BLK, num_splits=D_SPLITS, lam=lam, lse=self.lse,
+        return dict(page_size=D_PAGE, block_k=D_BLK, num_splits=self.splits, lam=lam, lse=self.lse,
                     tile_rows=self.tile_rows, head_dim_v=self.Dv)
 
     def run(self, lam, **diag):
@@ -294,7 +299,7 @@ class Decode:
         rows = self.B * self.T * self.Hq          # query rows (tokens x heads)
         q_bytes = rows * self.D * 2
         table = self.d.block_table.numel() * 4
-        parts = rows * D_SPLITS * (self.Dv + 1) * 4 * 2
+        parts = rows * self.splits * (self.Dv + 1) * 4 * 2
         out = rows * self.Dv * 2 + rows * 4
         dense_v = 0 if self.latent else self.B * self.Hkv * self.ctx * self.Dv * 2
         return (k_bytes + v_bytes + q_bytes + table + parts + out,
@@ -725,6 +730,17 @@ def main():
             result["mla_decode"][f"s{tgt}"] = r
         del mla
         torch.cuda.empty_cache()
+        result["mla_decode"]["splits_sweep"] = []
+        for sp in (4, 8, 16):
+            mla = Decode(m, torch, synth, ctx=M_CTX, latent=True, splits=sp)
+            lam = mla.calibrate(M_TARGETS[-1])
+            r = mla.measure(lam, args.steps)
+            result["mla_decode"]["splits_sweep"].append(
+                {"splits": sp, "target": M_TARGETS[-1], "sparsity": r["sparsity"], "ms": r["ms"],
+                 "dense_ms": r["dense_ms"], "speedup_vs_dense": r["speedup_vs_dense"], "hbm_gbps": r["hbm_gbps"],
+                 "lambda": r["lambda"]})
+            del mla
+            torch.cuda.empty_cache()
         result["calibration"] = calibration_sweep(m, torch, synth, args.steps)
         result["ceilings"] = practical_ceilings(torch)
     result["config"] = config

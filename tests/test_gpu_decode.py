@@ -174,14 +174,16 @@ def test_latent_mla_ragged(tile_rows, splits, a):
         assert rep.skipped == 0
 
 
-def test_latent_mla_full_size_sampled():
+@pytest.mark.parametrize("splits", [8, 16])
+def test_latent_mla_full_size_sampled(splits):
     """Batch 64, 128 q heads on one latent head (576 / 512), context 32768, 16-token pages, 64-token
-    blocks, 16 splits, 128-head tiles: sampled sequences against the oracle."""
+    blocks, 128-head tiles, 8 splits (the benchmarked launch) and 16: sampled sequences against the
+    oracle."""
     m = _lib()
     d = synth.decode_inputs(batch=64, hq=128, hkv=1, ctx=32768, d=576, dv=512, seed=synth.config_seed(5),
                             device="cuda", latent=True)
     a = 0.02 * 32768
-    res = _run(m, d, splits=16, a=a, tile_rows=128, out_dtype=torch.bfloat16)
+    res = _run(m, d, splits=splits, a=a, tile_rows=128, out_dtype=torch.bfloat16)
     o, lse, mask, crit, cnt = res
     ln_lam = math.log(min(1.0, a / 32768))
     mh, ch = mask.cpu().numpy(), crit.cpu().numpy()
@@ -190,7 +192,7 @@ def test_latent_mla_full_size_sampled():
     band = live & (np.abs(ch - ln_lam) < 1e-3)
     assert np.array_equal(decided[~band], mh[~band])
     assert torch.isfinite(o.float()).all()
-    rep = _compare(d, res, splits=16, a=a, tiles=[(0, 0, 0), (37, 0, 0), (63, 0, 0)], tile_rows=128,
+    rep = _compare(d, res, splits=splits, a=a, tiles=[(0, 0, 0), (37, 0, 0), (63, 0, 0)], tile_rows=128,
                    out_bf16=True)
     print(f"sparsity {float((mh == 1).sum()) / live.sum():.3f}; {rep}")
 
