@@ -42,7 +42,6 @@
 
 namespace blasst {
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((ext_vector_type(4))) short v4i16;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
