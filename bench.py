@@ -55,10 +55,9 @@ C_S_VALUES = (0.3, 0.5, 0.7)
 C_FINAL_L, C_FINAL_S = 131072, 0.75
 
 
-def profiled_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary (FETCH_SIZE and
-    WRITE_SIZE, each scaled by what the counter reads for a plain device copy of known size), or None
-    when the kernel's sources have changed since those counters were taken."""
+def profile_record(kernel):
+    """The committed rocprofv3 record of `kernel` (profiles/traffic.json), or None when the kernel's
+    sources have changed since it was taken."""
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[kernel]
         h = hashlib.sha256()
@@ -66,7 +65,23 @@ def profiled_traffic(kernel):
             h.update(open(os.path.join(ROOT, f), "rb").read())
     except (OSError, KeyError, ValueError):
         return None
-    return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
+    return rec if h.hexdigest() == rec["source_sha256"] else None
+
+
+def profiled_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by what the counter reads for a plain device copy of known size), or None
+    when the kernel's sources have changed since those counters were taken."""
+    rec = profile_record(kernel)
+    return rec["traffic_bytes"] if rec else None
+
+
+def profiled_counters(kernel):
+    """MFMA work and busy fraction and LDS bank conflicts of `kernel` per launch, from the committed
+    rocprofv3 SQ counter pass (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flops, SQ_VALU_MFMA_BUSY_CYCLES over
+    4 SIMDs x SQ_BUSY_CU_CYCLES, SQ_LDS_BANK_CONFLICT over SQ_LDS_IDX_ACTIVE), or None."""
+    rec = profile_record(kernel)
+    return rec.get("sq") if rec else None
 
 
 def parse():
@@ -650,6 +665,7 @@ def main():
                               "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                               "traffic": profiled_traffic("prefill_bf16_kernel<128, 128, 2, false, false, true, false>"),
                               "traffic_unit": "HBM bytes per launch",
+                              "counters": profiled_counters("prefill_bf16_kernel<128, 128, 2, false, false, true, false>"),
                               "min_bytes": pre.min_bytes,
                               "kernel": "prefill_bf16_kernel<128, 128, 2, bf16 out>",
                               "algorithmic": "QK^T on every live 128x128 tile-block + PV on kept ones, "
@@ -682,6 +698,7 @@ def main():
                                      "unit": "GB/s", "frac": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
                                      "traffic": profiled_traffic(DEC_KERNEL[dec.latent]),
                                      "traffic_unit": f"HBM bytes per launch of {DEC_KERNEL[dec.latent]}",
+                                     "counters": profiled_counters(DEC_KERNEL[dec.latent]),
                                      "kernel": f"{DEC_KERNEL[dec.latent]} + decode_combine_kernel"}
         if not pre:
             result.update({"value": r["hbm_gbps"], "unit": "GB/s"})
