@@ -39,6 +39,9 @@ C_B, C_L, C_T = 4, 32768, 2048      # chunked prefill: sequences, context length
 # decode workload
 D_B, D_HQ, D_HKV, D_CTX, D_D, D_PAGE, D_BLK, D_SPLITS = 32, 32, 8, 32768, 128, 16, 64, 16
 D_TARGET = 0.73
+# multi-token decode: 8 splits (with 16, the per-split first blocks that every tile keeps cap the
+# sparsity of tiles with T x 4 voting rows at 67-70 % even at lambda = 1)
+MT_SPLITS = 8
 CALIB_TILES = 8  # prefill calibration sample: 8 query tiles of 128 rows (1024 rows)
 # latent (MLA-shaped) decode
 M_B, M_HQ, M_D, M_DV, M_CTX, M_TARGETS = 64, 128, 576, 512, 32768, (0.5, 0.73)
@@ -728,15 +731,18 @@ def main():
         torch.cuda.empty_cache()
         result["decode_multi_token"] = {}
         for T in (2, 4):
-            mt = Decode(m, torch, synth, seed=synth.config_seed(3, 2), num_q_tokens=T, tile_rows=D_HQ // D_HKV)
-            lam = mt.calibrate(D_TARGET)
-            r = mt.measure(lam, args.steps)
-            r.update({"target_sparsity": D_TARGET, "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
-                      "workload": f"the decode workload with {T} query tokens per sequence (the last {T} "
-                                  f"positions), tiles of {T} tokens x 4 heads"})
-            result["decode_multi_token"][f"T{T}"] = r
-            del mt
-            torch.cuda.empty_cache()
+            for sp in (MT_SPLITS, D_SPLITS):
+                mt = Decode(m, torch, synth, seed=synth.config_seed(3, 2), num_q_tokens=T, tile_rows=D_HQ // D_HKV,
+                            splits=sp)
+                lam = mt.calibrate(D_TARGET)
+                r = mt.measure(lam, args.steps)
+                r.update({"target_sparsity": D_TARGET, "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
+                          "splits": sp,
+                          "workload": f"the decode workload with {T} query tokens per sequence (the last {T} "
+                                      f"positions), tiles of {T} tokens x 4 heads, {sp} splits"})
+                result["decode_multi_token"][f"T{T}" if sp == MT_SPLITS else f"T{T}_splits{sp}"] = r
+                del mt
+                torch.cuda.empty_cache()
         mla = Decode(m, torch, synth, ctx=M_CTX, latent=True)
         result["mla_decode"] = {"workload": MLA_WORKLOAD}
         for tgt in M_TARGETS:
