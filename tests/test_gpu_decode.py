@@ -235,6 +235,28 @@ def test_multi_token_decode(T, tile_rows, splits, a):
         assert rep.skipped == 0
 
 
+def test_multi_token_decode_full_size_sampled():
+    """The multi-token benchmark launch: batch 32, 32 q / 8 kv heads, d = 128, context 32768, the last
+    4 positions of each sequence as queries, tiles of 4 tokens x 4 heads, 8 splits; sampled tiles
+    against the oracle, all masks consistent with the critical values."""
+    m = _lib()
+    ctx, T = 32768, 4
+    d = synth.decode_inputs(batch=32, hq=32, hkv=8, ctx=ctx, d=128, seed=synth.config_seed(3, 2), device="cuda",
+                            num_q_tokens=T)
+    a = 0.05 * ctx
+    res = _run(m, d, splits=8, a=a, tile_rows=4)
+    o, lse, mask, crit, cnt = res
+    ln_lam = math.log(min(1.0, a / ctx))
+    mh, ch = mask.cpu().numpy(), crit.cpu().numpy()
+    live = mh != 2
+    decided = np.where(live, np.where(ch < ln_lam, 1, 0), 2)
+    band = live & (np.abs(ch - ln_lam) < 1e-3)
+    assert np.array_equal(decided[~band], mh[~band])
+    assert torch.isfinite(o).all()
+    rep = _compare(d, res, splits=8, a=a, tile_rows=4, tiles=[(0, 0, 0), (13, 5, 0), (31, 7, 0)])
+    print(f"sparsity {float((mh == 1).sum()) / live.sum():.3f}; {rep}")
+
+
 def test_multi_token_decode_short_sequence_rows_without_keys():
     """seq_lens below T: the first T - seq_len tokens see no key and get o = 0, lse = -inf; the others
     match the oracle (the cache holds more keys than seq_lens admits, and they must stay unread)."""
