@@ -133,15 +133,28 @@ def cpu_baseline(seconds: float):
     import torch
 
     import synth
+    import oracle
     global _CPU_INPUT
-    cores = min(16, len(os.sched_getaffinity(0)))
+    # every core this process may run on, up to 16: the host's CPU share of one GPU on the box
+    avail = len(os.sched_getaffinity(0))
+    cores = min(16, avail)
     # one kv head's keys at the full length, one q head of it; tiles at the causal end (256 blocks)
     inp = synth.prefill_inputs(batch=1, hq=1, hkv=1, L=P_L, d=P_D, block_k=P_BLK, window=True,
                                seed=2000, device="cpu")
     q = inp.q.float().double().numpy()
     k = inp.k.float().double().numpy()
     v = inp.v.float().double().numpy()
-    ln_lam = math.log(0.02)
+    # the benchmark's operating point on these inputs: ln(lambda) for 75 % sparsity from the critical
+    # values of an 8-tile sample, the same recipe as the GPU calibration, in the oracle's arithmetic
+    nqt = P_L // P_BLK
+    crit = []
+    for i in range(CALIB_TILES):
+        qt = int((i + 0.5) * nqt / CALIB_TILES)
+        rows = np.arange(qt * P_BLK, (qt + 1) * P_BLK)
+        vis = oracle.blasst_oracle.causal_visible(rows, P_L, P_L, P_L)
+        _, c = oracle.keep_mask_closed_form(q[0, 0, rows], k[0, 0], vis, P_BLK, 1, -math.inf, 1.0 / math.sqrt(P_D))
+        crit.append(c[~np.isnan(c)])
+    ln_lam = oracle.quantile_ln_lambda(np.concatenate(crit), P_TARGET)
     _CPU_INPUT = (q, k, v)
     # size the sample: time one tile, then run enough tiles for about `seconds` of wall time
     t_one = _oracle_worker((255, ln_lam))
@@ -164,7 +177,9 @@ def cpu_baseline(seconds: float):
     return {
         "value": flops / wall / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": cores, "kind": "oracle",
         "sample": f"{n_tiles} prefill query tiles of 128 rows x up to 32768 keys (q tiles 192-255 of one "
-                  f"head, lambda=0.02), fp64 numpy, one BLAS thread per worker; {wall:.1f} s; CPU {model}",
+                  f"head), lambda={math.exp(ln_lam):.5g} calibrated for {P_TARGET:.0%} sparsity on an 8-tile "
+                  f"sample as on the GPU; fp64 numpy, one BLAS thread per worker on {cores} of the {avail} cores "
+                  f"this process may use (16 = the host CPU share of one GPU); {wall:.1f} s; CPU {model}",
     }
 
 
@@ -256,6 +271,17 @@ class Prefill:
                 "dense_tflops": round(self.dense_flops / (dense_ms * 1e-3) / 1e12, 2),
                 "lambda": lam, "sparsity": round(skipped / live, 4)}
 
+    def deviation_from_dense(self, lam):
+        """max |O(lambda) - O(0)| over every output element (both bf16, as the benchmark writes them)."""
+        self.run(0.0)
+        dense = self.o.float().clone()
+        self.run(lam)
+        dev = (self.o.float() - dense).abs()
+        r = {"max_abs_dev_from_dense": round(float(dev.max()), 5),
+             "mean_abs_dev_from_dense": round(float(dev.mean()), 6)}
+        del dense, dev
+        return r
+
 
 class Decode:
     def __init__(self, m, torch, synth, ctx=D_CTX, latent=False, seed=None, num_q_tokens=None, tile_rows=None,
@@ -293,6 +319,35 @@ class Decode:
         d = self.d
         self.m.blasst_decode(d.q, d.k_cache, d.v_cache_t, d.block_table, d.seq_lens, self.o, workspace=self.ws,
                              **self._kw(lam), **diag)
+
+    def run_no_decision(self):
+        d = self.d
+        kw = self._kw(0.0)
+        del kw["lam"]
+        self.m.blasst_decode(d.q, d.k_cache, d.v_cache_t, d.block_table, d.seq_lens, self.o, workspace=self.ws,
+                             no_decision=True, **kw)
+
+    def decision_overhead(self, steps):
+        """The same dense work with and without the decision logic: lambda = 0 (every block voted on
+        and kept) against threshold mode NONE (the kernel variant without votes)."""
+        t0 = timed(self.torch, lambda: self.run(0.0), steps)
+        t1 = timed(self.torch, self.run_no_decision, steps)
+        t0 = min(t0, timed(self.torch, lambda: self.run(0.0), steps))
+        t1 = min(t1, timed(self.torch, self.run_no_decision, steps))
+        return {"lambda0_ms": round(t0, 4), "no_decision_ms": round(t1, 4),
+                "no_decision_over_lambda0_throughput": round(t1 / t0, 4)}
+
+    def deviation_from_dense(self, lam):
+        """max |O(lambda) - O(0)| over every output element (both bf16, as the benchmark writes them):
+        what skipping costs in output terms at this operating point."""
+        self.run(0.0)
+        dense = self.o.float().clone()
+        self.run(lam)
+        dev = (self.o.float() - dense).abs()
+        r = {"max_abs_dev_from_dense": round(float(dev.max()), 5),
+             "mean_abs_dev_from_dense": round(float(dev.mean()), 6)}
+        del dense, dev
+        return r
 
     def mask_shape(self):
         G = self.Hq // self.Hkv
@@ -561,7 +616,16 @@ def practical_ceilings(torch):
     y.copy_(x)
     ms = timed(torch, lambda: y.copy_(x), 5)
     out["copy_4gib_gbps_read_plus_write"] = round(2 * x.numel() * 2 / (ms * 1e-3) / 1e9, 1)
-    del x, y
+    del y
+    # read-only streaming (what a decode kernel mostly does): a max-reduction over the same 4 GiB,
+    # whose output is a few bytes; the best of two reductions
+    best = 0.0
+    for fn in (lambda: torch.amax(x), lambda: torch.sum(x, dtype=torch.float32)):
+        fn()
+        ms = timed(torch, fn, 5)
+        best = max(best, x.numel() * 2 / (ms * 1e-3) / 1e9)
+    out["read_4gib_gbps"] = round(best, 1)
+    del x
     torch.cuda.empty_cache()
     return out
 
@@ -672,11 +736,14 @@ def main():
                               "min_bytes": pre.min_bytes,
                               "kernel": "prefill_bf16_kernel<128, 128, 2, bf16 out>",
                               "algorithmic": "QK^T on every live 128x128 tile-block + PV on kept ones, "
-                                             "4.19 MFLOP each; launch average from HIP events in the timed region"}
+                                             "4.19 MFLOP each",
+                              "time_source": "mean launch time from HIP events on the launch stream over the "
+                                             "timed steps (the profiler's kernel average is in profiles/)"}
         config["workload"] = ("GQA prefill, Llama-3.1-8B-shaped: batch 1, 32 q / 8 kv heads, d 128, L 32768, causal, "
                               "128x128 blocks, bf16 in/out, lambda calibrated for 75% sparsity")
         config.update({"batch": P_B, "seq_len": P_L, "q_heads": P_HQ, "kv_heads": P_HKV, "head_dim": P_D})
         if not args.quick:
+            r.update(pre.deviation_from_dense(lam_p))
             lam50 = pre.calibrate(0.5)
             result["prefill_s050"] = pre.measure(lam50, max(3, args.steps // 2))
             result["prefill_s050"]["target_sparsity"] = 0.5
@@ -695,14 +762,19 @@ def main():
                                "pages, 64-token blocks, 16 splits, bf16")})
         r["timed_step_ms_p10_p50_p90"] = percentiles(dec_all)
         result["decode"] = r
+        if not args.quick:
+            r.update(dec.deviation_from_dense(lam_d))
         if not args.quick and not dec.latent:
+            result["decode_decision_overhead"] = dec.decision_overhead(args.steps)
             result["decode_speedup_vs_sparsity"] = sparsity_sweep(dec, args.steps)
         result["roofline_decode"] = {"bound": "hbm", "achieved": r["hbm_gbps"], "peak": PEAK_HBM_GBPS,
                                      "unit": "GB/s", "frac": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
                                      "traffic": profiled_traffic(DEC_KERNEL[dec.latent]),
                                      "traffic_unit": f"HBM bytes per launch of {DEC_KERNEL[dec.latent]}",
                                      "counters": profiled_counters(DEC_KERNEL[dec.latent]),
-                                     "kernel": f"{DEC_KERNEL[dec.latent]} + decode_combine_kernel"}
+                                     "kernel": f"{DEC_KERNEL[dec.latent]} + decode_combine_kernel",
+                                     "time_source": "mean time of the split and combine launches from HIP events "
+                                                    "on the launch stream over the timed steps"}
         if not pre:
             result.update({"value": r["hbm_gbps"], "unit": "GB/s"})
             config["workload"] = r["workload"]
@@ -719,6 +791,7 @@ def main():
         lam = d128.calibrate(D_TARGET)
         r = d128.measure(lam, args.steps)
         r.update({"target_sparsity": D_TARGET, "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4)})
+        r.update(d128.deviation_from_dense(lam))
         result["decode_131072"] = r
         del d128
         torch.cuda.empty_cache()
@@ -750,6 +823,7 @@ def main():
             r = mla.measure(lam, args.steps)
             r.update({"target_sparsity": tgt, "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
                       "profiled_traffic_bytes_per_launch": profiled_traffic(DEC_KERNEL[True])})
+            r.update(mla.deviation_from_dense(lam))
             result["mla_decode"][f"s{tgt}"] = r
         del mla
         torch.cuda.empty_cache()

@@ -59,9 +59,12 @@ typedef enum {
   BLASST_THR_A_OVER_L = 1, /* lambda = min(1, a / L), L = seqlen_k (prefill) or seq_lens[b] (decode) */
   BLASST_THR_NONE = 2      /* no threshold: every live block is kept (the result of lambda = 0), and
                               the bf16 prefill kernel for head dim 128, 128 x 128 blocks and an even
-                              GQA group runs without any decision logic (no vote); used to measure the
-                              cost of the decisions.  skip_mask and crit must be NULL and stats_only 0.
-                              Other kernels treat it as lambda = 0. */
+                              GQA group, and the GQA/MHA/MQA decode kernel, run without any decision
+                              logic (no vote); used to measure the cost of the decisions.  skip_mask
+                              and crit must be NULL and stats_only 0 (BLASST_ERR_INVALID_ARG
+                              otherwise); counters count live blocks and no skipped ones.  lambda and
+                              a are not read.  Other kernels (fp32 and paged prefill, latent decode)
+                              run with lambda = 0. */
 } blasst_threshold_mode;
 
 typedef struct {
@@ -103,7 +106,9 @@ enum { BLASST_CNT_LIVE = 0, BLASST_CNT_SKIPPED = 1, BLASST_NUM_COUNTERS = 2 };
  * are not written (calibration pass).
  * softmax_scale <= 0 selects 1/sqrt(head_dim_qk).
  * Supported kernels: bf16 in, bf16 or fp32 out, head_dim_qk == head_dim_v in {64, 128},
- * block_q == block_k in {64, 128}; fp32 in/out, head_dim 64 or 128, block_q == block_k == 64.
+ * block_q == block_k in {64, 128}, k and v token strides in [head_dim, 2^22) elements (rows that do
+ * not overlap); fp32 in/out, head_dim 64 or 128, block_q == block_k == 64.  All strides are
+ * multiples of 16 bytes and the tensors 16-byte aligned (BLASST_ERR_UNSUPPORTED otherwise).
  */
 typedef struct {
   size_t struct_size;        /* sizeof(blasst_prefill_params), for ABI checking */
@@ -255,6 +260,14 @@ typedef struct {
 
 /* Prefill forward (see the struct comment).  stream: hipStream_t or NULL. */
 blasst_status blasst_prefill(const blasst_prefill_params *params, void *stream);
+
+/* Workspace bytes that blasst_prefill needs for these params: always 0, since one workgroup owns a
+ * query tile for its whole key range (splits restart only the running max of the skip rule, and
+ * their chunks accumulate in the same registers), so no partial results leave the kernel.  The query
+ * exists so that callers can size buffers uniformly across entry points.  Returns 0 and sets the last
+ * error when the params are invalid (pointers are not checked), 0 with the last error cleared
+ * otherwise. */
+size_t blasst_prefill_workspace_size(const blasst_prefill_params *params);
 
 /* Chunked prefill against a paged cache (see the struct comment).  stream: hipStream_t or NULL. */
 blasst_status blasst_prefill_paged(const blasst_prefill_paged_params *params, void *stream);

@@ -4,6 +4,7 @@
 from .blasst import (  # noqa: F401
     BlasstError,
     blasst_prefill,
+    blasst_prefill_workspace_size,
     blasst_prefill_backward,
     blasst_prefill_paged,
     paged_prefill_params,

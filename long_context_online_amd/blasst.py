@@ -10,7 +10,6 @@ another implementation.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import numpy as np
@@ -24,7 +23,7 @@ THR_LAMBDA, THR_A_OVER_L, THR_NONE = 0, 1, 2
 KEPT, SKIPPED, NOT_LIVE = 0, 1, 2
 
 EXPORTED = [
-    "blasst_prefill", "blasst_decode", "blasst_decode_workspace_size", "blasst_calib_quantile",
+    "blasst_prefill", "blasst_prefill_workspace_size", "blasst_decode", "blasst_decode_workspace_size", "blasst_calib_quantile",
     "blasst_calibrate", "blasst_lambda_for", "blasst_status_string", "blasst_last_error",
     "blasst_version", "blasst_prefill_params_size", "blasst_decode_params_size",
     "blasst_prefill_backward", "blasst_prefill_backward_workspace_size", "blasst_prefill_backward_params_size",
@@ -134,6 +133,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.blasst_prefill.argtypes = [ctypes.POINTER(PrefillParams), ctypes.c_void_p]
         L.blasst_prefill.restype = ctypes.c_int
+        L.blasst_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillParams)]
+        L.blasst_prefill_workspace_size.restype = ctypes.c_size_t
         L.blasst_decode.argtypes = [ctypes.POINTER(DecodeParams), ctypes.c_void_p]
         L.blasst_decode.restype = ctypes.c_int
         L.blasst_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeParams)]
@@ -238,6 +239,17 @@ def prefill_params(q, k, v, o, *, causal, block_q, block_k, num_splits=1, lam=No
     return p
 
 
+def blasst_prefill_workspace_size(q, k, v, o, **kw) -> int:
+    """Workspace bytes of blasst_prefill for these arguments (always 0: the prefill keeps every
+    partial result on chip); raises on invalid arguments."""
+    p = prefill_params(q, k, v, o, **kw)
+    n = lib().blasst_prefill_workspace_size(ctypes.byref(p))
+    err = lib().blasst_last_error().decode()
+    if err:
+        raise BlasstError(ERR_INVALID_ARG, err)
+    return int(n)
+
+
 def blasst_prefill(q, k, v, o, *, stream=None, **kw):
     """BLASST prefill forward.  q [B, Hq, Lq, D], k/v [B, Hkv, Lk, D], o [B, Hq, Lq, Dv]
     (last dim contiguous).  Keyword args follow the C params (causal, block_q, block_k,
@@ -324,7 +336,7 @@ def blasst_prefill_backward(q, k, v, o, dout, lse, dq, dk, dv, *, stream=None, *
 def decode_params(q, k_cache, v_cache, block_table, seq_lens, o, *, page_size, block_k, num_splits,
                   lam=None, a=None, tile_rows=0, head_dim_v=None, softmax_scale=0.0, lse=None,
                   skip_mask=None, crit=None, counters=None, workspace=None, stats_only=False,
-                  out_dtype=None):
+                  out_dtype=None, no_decision=False):
     """Fills the C params struct for blasst_decode from tensors (no call)."""
     p = DecodeParams()
     p.struct_size = ctypes.sizeof(DecodeParams)
@@ -334,7 +346,7 @@ def decode_params(q, k_cache, v_cache, block_table, seq_lens, o, *, page_size, b
     p.skip_mask, p.crit, p.counters = _ptr(skip_mask), _ptr(crit), _ptr(counters)
     p.workspace = _ptr(workspace)
     p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    p.thr = _threshold(lam, a)
+    p.thr = _threshold(lam, a, no_decision)
     p.in_dtype = _dtype_code(q)
     p.out_dtype = _dtype_code(o) if o is not None else (p.in_dtype if out_dtype is None else out_dtype)
     if q.dim() == 4:
@@ -400,12 +412,4 @@ def blasst_lambda_for(alpha: float, beta: float, s: float, L: float) -> float:
 
 
 def _check_host(status: int):
-    if status != OK:
-        raise BlasstError(status, "invalid calibration input")
-
-
-def ln_lambda(lam=None, a=None, L=None) -> float:
-    """ln(lambda) for reporting (lambda = a / L capped at 1)."""
-    if lam is None:
-        lam = min(1.0, a / L)
-    return -math.inf if lam == 0 else math.log(lam)
+    _check(status)

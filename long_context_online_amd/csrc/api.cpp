@@ -9,6 +9,7 @@
 
 #include "../../include/blasst.h"
 #include "common.hpp"
+#include "host.hpp"
 
 namespace blasst {
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int D, int BC, bool out_f32, hipStream_t st);
@@ -20,8 +21,10 @@ hipError_t launch_prefill_paged(const PrefillArgs &a, bool out_f32, hipStream_t 
 }  // namespace blasst
 
 namespace {
-
 thread_local char g_err[512] = "";
+}  // namespace
+
+namespace blasst {
 
 blasst_status fail(blasst_status st, const char *fmt, ...) {
   va_list ap;
@@ -35,6 +38,13 @@ blasst_status ok() {
   g_err[0] = '\0';
   return BLASST_OK;
 }
+
+}  // namespace blasst
+
+namespace {
+
+using blasst::fail;
+using blasst::ok;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -112,6 +122,8 @@ blasst_status blasst_prefill_paged(const blasst_prefill_paged_params *p, void *s
   double ln_lam;
   const char *why = "";
   if (!resolve_threshold(p->thr, 1.0, &ln_lam, &why)) return fail(BLASST_ERR_INVALID_ARG, "%s", why);
+  if (p->thr.mode == BLASST_THR_NONE && (p->skip_mask || p->crit || p->stats_only))
+    return fail(BLASST_ERR_INVALID_ARG, "threshold mode NONE takes no skip_mask, crit or stats_only");
   // ---- kernel coverage ----
   if (p->in_dtype != BLASST_BF16) return fail(BLASST_ERR_UNSUPPORTED, "paged prefill supports bf16 inputs");
   if (p->head_dim_qk != 128 || p->head_dim_v != 128 || p->block_q != 128 || p->block_k != 128 || p->page_size != 16)
@@ -152,12 +164,14 @@ blasst_status blasst_prefill_paged(const blasst_prefill_paged_params *p, void *s
   return ok();
 }
 
-blasst_status blasst_prefill(const blasst_prefill_params *p, void *stream) {
+static blasst_status validate_prefill(const blasst_prefill_params *p, bool need_ptrs) {
   if (!p) return fail(BLASST_ERR_INVALID_ARG, "params is NULL");
   if (p->struct_size != sizeof(blasst_prefill_params))
     return fail(BLASST_ERR_INVALID_ARG, "struct_size %zu != %zu", p->struct_size, sizeof(blasst_prefill_params));
-  if (!p->q || !p->k || !p->v) return fail(BLASST_ERR_INVALID_ARG, "q, k and v must be non-NULL");
-  if (!p->stats_only && !p->o) return fail(BLASST_ERR_INVALID_ARG, "o must be non-NULL unless stats_only");
+  if (need_ptrs) {
+    if (!p->q || !p->k || !p->v) return fail(BLASST_ERR_INVALID_ARG, "q, k and v must be non-NULL");
+    if (!p->stats_only && !p->o) return fail(BLASST_ERR_INVALID_ARG, "o must be non-NULL unless stats_only");
+  }
   if (p->batch < 1 || p->seqlen_q < 1 || p->seqlen_k < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 ||
       p->head_dim_qk < 1 || p->head_dim_v < 1)
     return fail(BLASST_ERR_INVALID_ARG, "sizes must be >= 1");
@@ -173,12 +187,10 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *stream) {
   for (int i = 0; i < 3; ++i)
     if (p->q_stride[i] < 0 || p->k_stride[i] < 0 || p->v_stride[i] < 0 || p->o_stride[i] < 0)
       return fail(BLASST_ERR_INVALID_ARG, "strides must be >= 0");
-  const double scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0 / std::sqrt((double)p->head_dim_qk);
   double ln_lam;
   const char *why = "";
   if (!resolve_threshold(p->thr, p->seqlen_k, &ln_lam, &why)) return fail(BLASST_ERR_INVALID_ARG, "%s", why);
-  const bool no_decision = p->thr.mode == BLASST_THR_NONE;
-  if (no_decision && (p->skip_mask || p->crit || p->stats_only))
+  if (p->thr.mode == BLASST_THR_NONE && (p->skip_mask || p->crit || p->stats_only))
     return fail(BLASST_ERR_INVALID_ARG, "threshold mode NONE takes no skip_mask, crit or stats_only");
 
   // ---- kernel coverage ----
@@ -193,16 +205,42 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *stream) {
     // K and V rows are addressed with 24-bit byte offsets inside a block
     if (p->k_stride[2] >= (1 << 22) || p->v_stride[2] >= (1 << 22))
       return fail(BLASST_ERR_UNSUPPORTED, "k and v token strides must be below 2^22 elements");
+    // a block is staged through one buffer resource that spans its rows back to back, so rows must
+    // not overlap (a token stride of 0, an expanded tensor, would read as zeros)
+    if (p->k_stride[2] < D || p->v_stride[2] < D)
+      return fail(BLASST_ERR_UNSUPPORTED, "bf16 prefill needs k and v token strides >= head_dim");
   } else {
     if (!((D == 64 || D == 128) && p->block_k == 64 && p->out_dtype == BLASST_FP32))
       return fail(BLASST_ERR_UNSUPPORTED, "fp32 prefill supports head dim 64/128, blocks 64, fp32 out");
   }
-  if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || (p->o && !aligned16(p->o)))
+  if (need_ptrs && (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || (p->o && !aligned16(p->o))))
     return fail(BLASST_ERR_UNSUPPORTED, "q, k, v and o must be 16-byte aligned");
   const int oelem = p->out_dtype == BLASST_BF16 ? 2 : 4;
   for (int i = 0; i < 3; ++i)
     if (p->q_stride[i] % vec || p->k_stride[i] % vec || p->v_stride[i] % vec || p->o_stride[i] % (16 / oelem))
       return fail(BLASST_ERR_UNSUPPORTED, "strides must be multiples of 16 bytes");
+  const double nqt = ((int64_t)p->seqlen_q + p->block_q - 1) / p->block_q;
+  const double nkb = ((int64_t)p->seqlen_k + p->block_k - 1) / p->block_k;
+  if ((double)p->batch * p->num_q_heads * nqt > 2147483647.0 || (double)p->batch * p->num_q_heads * nqt * nkb > 2147483647.0)
+    return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
+  return BLASST_OK;
+}
+
+size_t blasst_prefill_workspace_size(const blasst_prefill_params *p) {
+  if (validate_prefill(p, false) != BLASST_OK) return 0;
+  ok();
+  return 0;
+}
+
+blasst_status blasst_prefill(const blasst_prefill_params *p, void *stream) {
+  const blasst_status st = validate_prefill(p, true);
+  if (st != BLASST_OK) return st;
+  const int D = p->head_dim_qk;
+  const double scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0 / std::sqrt((double)p->head_dim_qk);
+  double ln_lam;
+  const char *why = "";
+  resolve_threshold(p->thr, p->seqlen_k, &ln_lam, &why);
+  const bool no_decision = p->thr.mode == BLASST_THR_NONE;
 
   blasst::PrefillArgs a{};
   a.q = p->q; a.k = p->k; a.v = p->v; a.o = p->o; a.lse = p->lse;
@@ -219,8 +257,6 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *stream) {
   a.scale_log2 = (float)(scale * 1.4426950408889634);
   a.thr_raw = thr_raw_from(ln_lam, scale);
   a.decide = no_decision ? 0 : 1;
-  if ((double)a.B * a.Hq * a.nqt > 2147483647.0 || (double)a.B * a.Hq * a.nqt * a.nkb > 2147483647.0)
-    return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
 
   hipError_t e;
   if (p->in_dtype == BLASST_BF16)
@@ -254,6 +290,8 @@ static blasst_status validate_decode(const blasst_decode_params *p, bool need_pt
   double ln_lam;
   const char *why = "";
   if (!resolve_threshold(p->thr, 1.0, &ln_lam, &why)) return fail(BLASST_ERR_INVALID_ARG, "%s", why);
+  if (p->thr.mode == BLASST_THR_NONE && (p->skip_mask || p->crit || p->stats_only))
+    return fail(BLASST_ERR_INVALID_ARG, "threshold mode NONE takes no skip_mask, crit or stats_only");
   if (need_ptrs) {
     if (!p->q || !p->k_cache || !p->block_table || !p->seq_lens)
       return fail(BLASST_ERR_INVALID_ARG, "q, k_cache, block_table and seq_lens must be non-NULL");
@@ -377,26 +415,40 @@ size_t blasst_decode_workspace_size(const blasst_decode_params *p) {
 
 blasst_status blasst_decode(const blasst_decode_params *p, void *stream) {
   size_t ws = 0;
-  blasst_status st = validate_decode(p, true, &ws);
+  blasst_status st = blasst::decode_validate(p, &ws);
   if (st != BLASST_OK) return st;
-  if (ws > 0 && !p->stats_only) {
+  if (ws > 0) {
     if (!p->workspace || p->workspace_bytes < ws)
       return fail(BLASST_ERR_WORKSPACE, "workspace of %zu bytes required", ws);
     if (reinterpret_cast<uintptr_t>(p->workspace) & 255u)
       return fail(BLASST_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   }
+  return blasst::decode_launch(p, p->workspace, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace blasst {
+
+blasst_status decode_validate(const blasst_decode_params *p, size_t *ws_bytes) {
+  const blasst_status st = validate_decode(p, true, ws_bytes);
+  if (st == BLASST_OK && p->stats_only) *ws_bytes = 0;   // a stats pass writes no partials
+  return st;
+}
+
+blasst_status decode_launch(const blasst_decode_params *p, void *workspace, hipStream_t stream) {
   const double scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0 / std::sqrt((double)p->head_dim_qk);
   const int G = p->num_q_heads / p->num_kv_heads;
   const int tr = p->tile_rows == 0 ? G : p->tile_rows;
-  blasst::DecodeArgs a{};
+  DecodeArgs a{};
   a.q = p->q; a.kc = p->k_cache; a.vc = p->v_cache; a.table = p->block_table; a.seq_lens = p->seq_lens;
   a.o = p->o; a.lse = p->lse; a.mask = p->skip_mask; a.crit = p->crit; a.counters = p->counters;
   const int T = p->num_q_tokens == 0 ? 1 : p->num_q_tokens;
-  if (ws > 0 && !p->stats_only) {
+  if (p->num_splits > 1 && !p->stats_only) {   // the layout decode_validate sized
     const size_t parts = (size_t)p->batch * T * p->num_q_heads * p->num_splits;
     const size_t o_bytes = (parts * p->head_dim_v * sizeof(float) + 255) / 256 * 256;
-    a.ws_o = (float *)p->workspace;
-    a.ws_lse = (float *)((char *)p->workspace + o_bytes);
+    a.ws_o = (float *)workspace;
+    a.ws_lse = (float *)((char *)workspace + o_bytes);
   }
   a.B = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = G; a.tile_rows = tr; a.n_rt = G / tr;
   a.T = T;
@@ -405,18 +457,22 @@ blasst_status blasst_decode(const blasst_decode_params *p, void *stream) {
   a.num_splits = p->num_splits; a.stats_only = p->stats_only ? 1 : 0; a.out_f32 = p->out_dtype == BLASST_FP32;
   a.scale = (float)scale;
   a.scale_log2 = (float)(scale * 1.4426950408889634);
-  if (p->thr.mode == BLASST_THR_LAMBDA) {
-    a.thr_mode = 0;
-    a.thr_raw = thr_raw_from(p->thr.lambda == 0.0 ? -INFINITY : std::log(p->thr.lambda), scale);
-  } else {
+  a.decide = 1;
+  if (p->thr.mode == BLASST_THR_A_OVER_L) {
     a.thr_mode = 1;
     a.a = (float)p->thr.a;
+  } else {
+    // a fixed lambda; NONE keeps every block (lambda = 0) and, for the GQA kernel, runs the variant
+    // without any decision logic
+    a.thr_mode = 0;
+    a.thr_raw = thr_raw_from(p->thr.mode == BLASST_THR_NONE || p->thr.lambda == 0.0 ? -INFINITY
+                                                                                    : std::log(p->thr.lambda), scale);
+    if (p->thr.mode == BLASST_THR_NONE) a.decide = 0;
   }
-  hipError_t e = p->v_cache ? blasst::launch_decode_gqa(a, (hipStream_t)stream)
-                            : blasst::launch_decode_latent(a, (hipStream_t)stream);
+  hipError_t e = p->v_cache ? launch_decode_gqa(a, stream) : launch_decode_latent(a, stream);
   if (e == hipErrorNotSupported) return fail(BLASST_ERR_UNSUPPORTED, "no decode kernel for this shape");
   if (e != hipSuccess) return fail(BLASST_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }
 
-}  // extern "C"
+}  // namespace blasst

@@ -9,22 +9,28 @@
 #include <vector>
 
 #include "../../include/blasst.h"
+#include "host.hpp"
+
+using blasst::fail;
+using blasst::ok;
 
 extern "C" {
 
 blasst_status blasst_calib_quantile(const float *crit, int64_t n, double target_s, double *ln_lambda) {
-  if (!crit || !ln_lambda || n < 1 || !(target_s >= 0.0 && target_s <= 1.0)) return BLASST_ERR_INVALID_ARG;
+  if (!crit || !ln_lambda) return fail(BLASST_ERR_INVALID_ARG, "crit and ln_lambda must be non-NULL");
+  if (n < 1) return fail(BLASST_ERR_INVALID_ARG, "n must be >= 1");
+  if (!(target_s >= 0.0 && target_s <= 1.0)) return fail(BLASST_ERR_INVALID_ARG, "target_s must lie in [0, 1]");
   std::vector<double> c;
   c.reserve((size_t)n);
   for (int64_t i = 0; i < n; ++i)
     if (!std::isnan(crit[i])) c.push_back((double)crit[i]);
-  if (c.empty()) return BLASST_ERR_INVALID_ARG;
+  if (c.empty()) return fail(BLASST_ERR_INVALID_ARG, "every critical value is NaN");
   std::sort(c.begin(), c.end());
   const int64_t N = (int64_t)c.size();
   const int64_t k = (int64_t)std::ceil(target_s * (double)N);
   if (k <= 0) {
     *ln_lambda = -INFINITY;
-    return BLASST_OK;
+    return ok();
   }
   const double lo = c[(size_t)(k - 1)];
   const double hi = k < N ? c[(size_t)k] : INFINITY;
@@ -39,15 +45,18 @@ blasst_status blasst_calib_quantile(const float *crit, int64_t n, double target_
     mid = lo + 1.0;
   }
   *ln_lambda = std::min(0.0, mid);
-  return BLASST_OK;
+  return ok();
 }
 
 blasst_status blasst_calibrate(const double *L, const double *s, const double *lambda, int32_t n, double *alpha,
                                double *beta, double *rmse) {
-  if (!L || !s || !lambda || !alpha || !beta || n < 2) return BLASST_ERR_INVALID_ARG;
+  if (!L || !s || !lambda || !alpha || !beta) return fail(BLASST_ERR_INVALID_ARG, "L, s, lambda, alpha and beta must be non-NULL");
+  if (n < 2) return fail(BLASST_ERR_INVALID_ARG, "at least two points are needed, got %d", (int)n);
   double xm = 0, ym = 0;
   for (int32_t i = 0; i < n; ++i) {
-    if (!(lambda[i] > 0.0) || !(L[i] > 0.0) || !std::isfinite(s[i])) return BLASST_ERR_INVALID_ARG;
+    if (!(lambda[i] > 0.0) || !(L[i] > 0.0) || !std::isfinite(s[i]) || !std::isfinite(lambda[i]) ||
+        !std::isfinite(L[i]))
+      return fail(BLASST_ERR_INVALID_ARG, "point %d: lambda and L must be finite and > 0, s finite", (int)i);
     xm += s[i];
     ym += std::log(lambda[i] * L[i]);
   }
@@ -59,7 +68,7 @@ blasst_status blasst_calibrate(const double *L, const double *s, const double *l
     sxx += dx * dx;
     sxy += dx * (std::log(lambda[i] * L[i]) - ym);
   }
-  if (sxx == 0.0) return BLASST_ERR_INVALID_ARG;
+  if (sxx == 0.0) return fail(BLASST_ERR_INVALID_ARG, "the points need at least two distinct s values");
   const double b = sxy / sxx;
   const double la = ym - b * xm;
   double sse = 0;
@@ -70,7 +79,7 @@ blasst_status blasst_calibrate(const double *L, const double *s, const double *l
   *alpha = std::exp(la);
   *beta = b;
   if (rmse) *rmse = std::sqrt(sse / n);
-  return BLASST_OK;
+  return ok();
 }
 
 double blasst_lambda_for(double alpha, double beta, double s, double L) {

@@ -79,6 +79,7 @@ struct DecodeArgs {
   float thr_raw;   // ln(lambda) / scale
   float a;         // for thr_mode 1
   float scale, scale_log2;
+  int decide;      // 0: no threshold at all (every live block kept; the GQA kernel runs without votes)
 };
 
 // Row vote of the skip rule on raw (unscaled) logits: the row votes "skip" when

@@ -37,7 +37,9 @@ namespace {
 constexpr int D = 128, PAGE = 16, BK = 64, NWAVE = 4, NB = 4;
 }
 
-template <bool OUT_F32>
+// DEC = false: no threshold at all (every live block kept, no vote, no diagnostics but the
+// counters); the same kernel without the decision logic, used to measure what the decisions cost.
+template <bool OUT_F32, bool DEC = true>
 __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
   __shared__ float sPmax[2][NB][NWAVE][16];  // double-buffered by batch parity
   __shared__ float sRed[NWAVE][16][D + 4];
@@ -163,7 +165,10 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
       float mb = fmaxf(fmaxf(pm[0][n], pm[1][n]), fmaxf(pm[2][n], pm[3][n]));
       if (!col_ok) mb = kNegInf;
       mblk[i] = mb;
-      if (i < nb) {
+      if (i < nb && !DEC) {
+        keep_bits |= 1 << i;
+        ++live_cnt;
+      } else if (i < nb) {
         const int j = jb + i;
         const bool skip_row = row_votes_skip(mb, m_dec, thr);
         const bool keep = __ballot(!skip_row) != 0ull;
@@ -389,10 +394,16 @@ hipError_t launch_decode_combine(const DecodeArgs &a, int Dv, hipStream_t st) {
 
 hipError_t launch_decode_gqa(const DecodeArgs &a, hipStream_t st) {
   const int grid = a.B * a.Hkv * a.n_rt * a.num_splits;
-  if (a.out_f32)
-    hipLaunchKernelGGL(decode_gqa_kernel<true>, dim3(grid), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(decode_gqa_kernel<false>, dim3(grid), dim3(256), 0, st, a);
+  if (!a.decide) {
+    if (a.out_f32)
+      hipLaunchKernelGGL((decode_gqa_kernel<true, false>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_gqa_kernel<false, false>), dim3(grid), dim3(256), 0, st, a);
+  } else if (a.out_f32) {
+    hipLaunchKernelGGL((decode_gqa_kernel<true, true>), dim3(grid), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((decode_gqa_kernel<false, true>), dim3(grid), dim3(256), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1 || a.stats_only) return e;
   return launch_decode_combine(a, D, st);

@@ -82,6 +82,9 @@ PREFILL_BAD = [
     ({"thr": (2, 0, 0.0, 0.0), "stats_only": 1}, 1),
     ({"head_dim_qk": 96, "head_dim_v": 96}, 2), ({"block_q": 64}, 2), ({"block_q": 32, "block_k": 32}, 2),
     ({"q": FAKE + 2}, 2), ({"in_dtype": 1, "out_dtype": 0}, 2), ({"in_dtype": 1, "out_dtype": 1}, 2),
+    # bf16 K/V rows must not overlap (token stride >= head_dim): an expanded tensor (stride 0) and a
+    # stride below the row length are refused
+    ({"k_stride": (128 * 256 * 128, 256 * 128, 0)}, 2), ({"v_stride": (128 * 256 * 128, 256 * 128, 64)}, 2),
 ]
 
 
@@ -92,6 +95,20 @@ def test_prefill_rejects_invalid_arguments(m, over, status):
     assert lib.blasst_prefill(ctypes.byref(p), None) == status
     assert lib.blasst_last_error()
     assert lib.blasst_prefill(None, None) == 1
+
+
+def test_prefill_workspace_size(m):
+    """The prefill keeps every partial result on chip: 0 bytes for valid params with the last error
+    cleared; invalid params give 0 with a message (pointers are not checked)."""
+    lib = m.lib()
+    lib.blasst_prefill(None, None)                       # leaves a message behind
+    assert lib.blasst_prefill_workspace_size(ctypes.byref(_prefill(num_splits=4))) == 0
+    assert lib.blasst_last_error() == b""
+    assert lib.blasst_prefill_workspace_size(ctypes.byref(_prefill(q=None, k=None, v=None, o=None))) == 0
+    assert lib.blasst_last_error() == b""
+    assert lib.blasst_prefill_workspace_size(ctypes.byref(_prefill(num_kv_heads=3))) == 0
+    assert b"multiple" in lib.blasst_last_error()
+    assert lib.blasst_prefill_workspace_size(None) == 0 and lib.blasst_last_error()
 
 
 def _decode(**over):
@@ -123,6 +140,9 @@ DECODE_BAD = [
     ({"num_q_tokens": 5}, 2), ({"num_q_tokens": 9, "tile_rows": 2}, 2),
     ({"v_cache": None, "num_kv_heads": 1, "num_q_heads": 128, "head_dim_qk": 576, "head_dim_v": 512,
       "tile_rows": 128, "num_q_tokens": 2}, 2),
+    # threshold mode NONE (no decisions) takes no decision diagnostics, whatever `a` holds
+    ({"thr": (2, 0, 0.0, 5.0), "skip_mask": FAKE}, 1), ({"thr": (2, 0, 0.0, 5.0), "crit": FAKE}, 1),
+    ({"thr": (2, 0, 0.0, float("nan")), "stats_only": 1}, 1),
 ]
 
 
@@ -164,6 +184,43 @@ def test_calibration_matches_oracle(m):
     assert a1 == pytest.approx(a2, rel=1e-12) and b1 == pytest.approx(b2, rel=1e-12) and r1 == pytest.approx(r2, rel=1e-9)
     assert m.blasst_lambda_for(a1, b1, 0.5, 8192) == pytest.approx(oracle.lambda_for(a2, b2, 0.5, 8192), rel=1e-12)
     with pytest.raises(m.BlasstError):
+        m.blasst_calibrate([1, 2], [0.5, 0.5], [0.1, 0.1])
+
+
+def test_calibration_errors_set_the_message(m):
+    """Every error return of the host calibration calls sets the calling thread's message, and a
+    success clears it."""
+    lib = m.lib()
+    dp = ctypes.POINTER(ctypes.c_double)
+    out = ctypes.c_double()
+    c = np.array([-1.0, -2.0, np.nan], dtype=np.float32)
+    cp = c.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    nan3 = np.full(3, np.nan, dtype=np.float32)
+    cases = [
+        (lambda: lib.blasst_calib_quantile(None, 3, 0.5, ctypes.byref(out)), b"non-NULL"),
+        (lambda: lib.blasst_calib_quantile(cp, 0, 0.5, ctypes.byref(out)), b"n must"),
+        (lambda: lib.blasst_calib_quantile(cp, 3, 1.5, ctypes.byref(out)), b"target_s"),
+        (lambda: lib.blasst_calib_quantile(nan3.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), 3, 0.5,
+                                           ctypes.byref(out)), b"NaN"),
+    ]
+    L = np.array([4096.0, 8192.0]); s2 = np.array([0.5, 0.5]); lam = np.array([0.1, 0.1])
+    args = [x.ctypes.data_as(dp) for x in (L, s2, lam)]
+    a_, b_, r_ = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    outs = (ctypes.byref(a_), ctypes.byref(b_), ctypes.byref(r_))
+    cases += [
+        (lambda: lib.blasst_calibrate(*args, 1, *outs), b"two points"),
+        (lambda: lib.blasst_calibrate(*args, 2, *outs), b"distinct"),
+        (lambda: lib.blasst_calibrate(args[0], args[1], None, 2, *outs), b"non-NULL"),
+    ]
+    bad = np.array([0.1, -0.1])
+    cases.append((lambda: lib.blasst_calibrate(args[0], np.array([0.3, 0.5]).ctypes.data_as(dp),
+                                                bad.ctypes.data_as(dp), 2, *outs), b"point 1"))
+    for call, text in cases:
+        lib.blasst_calib_quantile(cp, 3, 0.5, ctypes.byref(out))   # a success clears the message
+        assert lib.blasst_last_error() == b""
+        assert call() == 1
+        assert text in lib.blasst_last_error(), (text, lib.blasst_last_error())
+    with pytest.raises(m.BlasstError, match="distinct"):
         m.blasst_calibrate([1, 2], [0.5, 0.5], [0.1, 0.1])
 
 
@@ -237,6 +294,7 @@ PAGED_BAD = [
     ({"num_splits": 0}, 1), ({"thr": (0, 0, 1.5, 0.0)}, 1), ({"struct_size": 16}, 1), ({"page_size": 0}, 1),
     ({"in_dtype": 1}, 2), ({"page_size": 32}, 2), ({"block_q": 64, "block_k": 64}, 2),
     ({"head_dim_qk": 64, "head_dim_v": 64}, 2), ({"q": FAKE + 4}, 2),
+    ({"thr": (2, 0, 0.0, 0.0), "skip_mask": FAKE}, 1), ({"thr": (2, 0, 0.0, 0.0), "stats_only": 1}, 1),
 ]
 
 

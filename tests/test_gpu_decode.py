@@ -1,5 +1,6 @@
 """GPU parity of blasst_decode (paged split-KV, through the C ABI) against the fp64 oracle."""
 
+import ctypes
 import math
 
 import numpy as np
@@ -43,15 +44,19 @@ def _run(m, d, *, splits, lam=None, a=None, tile_rows=0, out_dtype=torch.float32
     return o, lse, mask, crit, cnt
 
 
-def _tile_inputs(d, b):
-    """Host fp64 copies of what one sequence's tiles read: its query, its pages (renumbered 0..n-1)."""
+def _tile_inputs(d, b, g):
+    """Host fp64 copies of what the tiles of sequence b and kv head g read: the queries of the q heads
+    that share kv head g, and that head's slice of the sequence's pages (renumbered 0..n-1), as a
+    problem with one sequence and one kv head."""
     L = int(d.seq_lens[b])
     npg = -(-L // d.page_size)
     ids = d.block_table[b, :npg].long()
-    kc = host64(d.k_cache[ids])
-    vc = host64(d.v_cache_t[ids]) if d.v_cache_t is not None else None
+    Hq, Hkv = d.q.shape[-2], d.k_cache.shape[1]
+    G = Hq // Hkv
+    kc = host64(d.k_cache[ids, g:g + 1])
+    vc = host64(d.v_cache_t[ids, g:g + 1]) if d.v_cache_t is not None else None
     bt = np.arange(npg, dtype=np.int64)[None, :]
-    return host64(d.q[b:b + 1]), kc, vc, bt, np.array([L])
+    return host64(d.q[b:b + 1, ..., g * G:(g + 1) * G, :]), kc, vc, bt, np.array([L])
 
 
 def _compare(d, res, *, splits, lam=None, a=None, tiles=None, tile_rows=0, out_bf16=False):
@@ -70,18 +75,18 @@ def _compare(d, res, *, splits, lam=None, a=None, tiles=None, tile_rows=0, out_b
         tiles = [(b, g, rt) for b in range(B) for g in range(Hkv) for rt in range(G // tr)]
     cache = {}
     for (b, g, rt) in tiles:
-        if b not in cache:
-            cache = {b: _tile_inputs(d, b)}
-        qh, kc, vc, bt, sl1 = cache[b]
+        if (b, g) not in cache:
+            cache = {(b, g): _tile_inputs(d, b, g)}
+        qh, kc, vc, bt, sl1 = cache[(b, g)]
         ln_lam = oracle.ln_threshold(lam=lam) if lam is not None else oracle.ln_threshold(a=a, L=int(sl[b]))
         kw = dict(page_size=d.page_size, block_k=64, num_splits=splits, ln_lam=ln_lam, tile_rows=tr,
                   head_dim_v=d.head_dim_v)
-        ref = oracle.decode_tile(qh, kc, vc, bt, sl1, 0, g, rt, **kw)
+        ref = oracle.decode_tile(qh, kc, vc, bt, sl1, 0, 0, rt, **kw)
         h0 = g * G + rt * tr
         nb = ref["mask"].shape[0]
         assert np.all(mh[b, g, rt, nb:] == 2)
         check_tile(rep, ref, mh[b, g, rt], ch[b, g, rt], ln_lam,
-                   lambda f: oracle.decode_tile(qh, kc, vc, bt, sl1, 0, g, rt, force=f, **kw),
+                   lambda f: oracle.decode_tile(qh, kc, vc, bt, sl1, 0, 0, rt, force=f, **kw),
                    None if oh is None else (oh[b, :, h0:h0 + tr].reshape(-1, oh.shape[-1]) if multi
                                             else oh[b, h0:h0 + tr]),
                    None if oh is None else (lh[b, :, h0:h0 + tr].reshape(-1) if multi else lh[b, h0:h0 + tr]),
@@ -135,26 +140,89 @@ def test_stats_only_matches_full_pass():
     assert torch.allclose(full[3], st[3], rtol=0, atol=0, equal_nan=True)
 
 
-@pytest.mark.parametrize("ctx", [32768])
-def test_gqa_decode_full_size_sampled(ctx):
-    """Batch 32, 32 q / 8 kv heads, d = 128, 16-token pages, 64-token blocks, 16 splits (the
-    benchmark's launch configuration); sampled tiles against the oracle, all masks consistent with
-    the critical values."""
-    m = _lib()
-    d = synth.decode_inputs(batch=32, hq=32, hkv=8, ctx=ctx, d=128, seed=synth.config_seed(3), device="cuda")
-    a = 0.02 * ctx
-    res = _run(m, d, splits=16, a=a)
+def _calibrated_lambda(m, d, *, splits, target, tile_rows=0):
+    """lambda at a target sparsity the way the benchmark sets it: one stats-only pass over every tile
+    of the batch (critical values only), then the library's quantile of all of them."""
+    if target == 0.0:
+        return 0.0
+    crit = _run(m, d, splits=splits, lam=0.0, tile_rows=tile_rows, stats_only=True)[3].cpu().numpy()
+    return math.exp(m.blasst_calib_quantile(crit, target))
+
+
+def _seeded_tiles(B, Hkv, n_rt, count, seed, must=()):
+    """`count` distinct (sequence, kv head, row tile) picks from a seeded generator, plus `must`,
+    sorted so that the tiles of one (sequence, kv head) are compared together."""
+    rng = np.random.default_rng(seed)
+    every = [(b, g, rt) for b in range(B) for g in range(Hkv) for rt in range(n_rt)]
+    pick = {every[i] for i in rng.choice(len(every), size=min(count, len(every)), replace=False)}
+    return sorted(pick | set(must))
+
+
+def _check_whole_mask(res, ln_lam, target):
+    """Every tile of the launch: the mask is its critical values compared with ln(lambda) (outside
+    the margin band), the counters are the mask's counts, and the sparsity is the calibrated one."""
     o, lse, mask, crit, cnt = res
-    ln_lam = math.log(min(1.0, a / ctx))
     mh, ch = mask.cpu().numpy(), crit.cpu().numpy()
     live = mh != 2
     decided = np.where(live, np.where(ch < ln_lam, 1, 0), 2)
     band = live & (np.abs(ch - ln_lam) < 1e-3)
     assert np.array_equal(decided[~band], mh[~band])
-    assert torch.isfinite(o).all()
-    tiles = [(0, 0, 0), (5, 3, 0), (17, 7, 0), (31, 4, 0)]
-    rep = _compare(d, res, splits=16, a=a, tiles=tiles)
-    print(f"sparsity {float((mh == 1).sum()) / live.sum():.3f}; {rep}")
+    assert int(cnt[0]) == int(live.sum()) and int(cnt[1]) == int((mh == 1).sum())
+    assert torch.isfinite(o.float()).all()
+    sp = float((mh == 1).sum()) / live.sum()
+    if target == 0.0:
+        assert sp == 0.0
+    else:
+        assert abs(sp - target) < 0.02, f"sparsity {sp} at target {target}"
+    return sp
+
+
+@pytest.mark.parametrize("target", [0.73, 0.0])
+@pytest.mark.parametrize("ctx", [32768, 131072])
+def test_gqa_decode_full_size_at_benchmark_threshold(ctx, target):
+    """The benchmarked decode launches: batch 32, 32 q / 8 kv heads, d = 128, context 32768 and
+    131072, 16-token pages, 64-token blocks, 16 splits, bf16 output, lambda calibrated for 73 %
+    sparsity exactly as the benchmark does it (and lambda = 0).  26 seeded tiles (all 16 splits of
+    each) against the oracle, and every tile's mask against its critical values."""
+    m = _lib()
+    seed = synth.config_seed(3) if ctx == 32768 else synth.config_seed(3, 1)
+    d = synth.decode_inputs(batch=32, hq=32, hkv=8, ctx=ctx, d=128, seed=seed, device="cuda")
+    lam = _calibrated_lambda(m, d, splits=16, target=target)
+    res = _run(m, d, splits=16, lam=lam, out_dtype=torch.bfloat16)
+    ln_lam = oracle.ln_threshold(lam=lam)
+    sp = _check_whole_mask(res, ln_lam, target)
+    tiles = _seeded_tiles(32, 8, 1, 24, seed, must=[(0, 0, 0), (31, 7, 0)])
+    rep = _compare(d, res, splits=16, lam=lam, tiles=tiles, out_bf16=True)
+    print(f"ctx={ctx} lambda={lam:.6g} sparsity {sp:.4f}; {rep}")
+    assert rep.live == len(tiles) * (ctx // 64)
+
+
+def test_gqa_decode_no_decision_mode_equals_lambda_zero():
+    """Threshold mode NONE (the decode kernel without any decision logic) gives the bits of
+    lambda = 0 (which the oracle checks here too), keeps every block whatever `a` holds (here 5,
+    which as a / L would skip), and is refused with decision diagnostics."""
+    m = _lib()
+    from long_context_online_amd import blasst as bl
+    d = synth.decode_inputs(batch=4, hq=32, hkv=8, ctx=None, d=128, seq_lens=[3000, 64, 1, 777], seed=12,
+                            device="cuda")
+    ref = _run(m, d, splits=4, lam=0.0)
+    print(_compare(d, ref, splits=4, lam=0.0))
+    o = torch.full((4, 32, 128), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((4, 32), float("nan"), dtype=torch.float32, device="cuda")
+    cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+    kw = dict(page_size=16, block_k=64, num_splits=4, lse=lse, counters=cnt, no_decision=True)
+    ws = torch.empty(m.blasst_decode_workspace_size(d.q, d.k_cache, d.v_cache_t, d.block_table, d.seq_lens, o, **kw),
+                     dtype=torch.uint8, device="cuda")
+    p = bl.decode_params(d.q, d.k_cache, d.v_cache_t, d.block_table, d.seq_lens, o, workspace=ws, **kw)
+    p.thr.a = 5.0       # not read in mode NONE
+    assert m.lib().blasst_decode(ctypes.byref(p), bl._stream(None)) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1])
+    assert int(cnt[1]) == 0 and int(cnt[0]) == int(ref[4][0]) > 0
+    mask = torch.empty_like(ref[2])
+    with pytest.raises(m.BlasstError):
+        m.blasst_decode(d.q, d.k_cache, d.v_cache_t, d.block_table, d.seq_lens, o, page_size=16, block_k=64,
+                        num_splits=1, no_decision=True, skip_mask=mask)
 
 
 @pytest.mark.parametrize("tile_rows", [128, 64])
@@ -174,27 +242,45 @@ def test_latent_mla_ragged(tile_rows, splits, a):
         assert rep.skipped == 0
 
 
-@pytest.mark.parametrize("splits", [8, 16])
-def test_latent_mla_full_size_sampled(splits):
-    """Batch 64, 128 q heads on one latent head (576 / 512), context 32768, 16-token pages, 64-token
-    blocks, 128-head tiles, 8 splits (the benchmarked launch) and 16: sampled sequences against the
-    oracle."""
+def _mla_full_size():
+    return synth.decode_inputs(batch=64, hq=128, hkv=1, ctx=32768, d=576, dv=512, seed=synth.config_seed(5),
+                               device="cuda", latent=True)
+
+
+@pytest.mark.parametrize("splits,target", [(8, 0.73), (8, 0.5), (4, 0.73)])
+def test_latent_mla_full_size_at_benchmark_threshold(splits, target):
+    """The benchmarked latent decode: batch 64, 128 q heads on one latent head (576 / 512), context
+    32768, 16-token pages, 64-token blocks, 128-head tiles, bf16 output, lambda calibrated for the
+    target as the benchmark does (8 splits at 73 % and 50 %; 4 splits from its split sweep).  24
+    seeded sequences against the oracle, every tile's mask against its critical values."""
     m = _lib()
-    d = synth.decode_inputs(batch=64, hq=128, hkv=1, ctx=32768, d=576, dv=512, seed=synth.config_seed(5),
-                            device="cuda", latent=True)
-    a = 0.02 * 32768
-    res = _run(m, d, splits=splits, a=a, tile_rows=128, out_dtype=torch.bfloat16)
-    o, lse, mask, crit, cnt = res
-    ln_lam = math.log(min(1.0, a / 32768))
-    mh, ch = mask.cpu().numpy(), crit.cpu().numpy()
-    live = mh != 2
-    decided = np.where(live, np.where(ch < ln_lam, 1, 0), 2)
-    band = live & (np.abs(ch - ln_lam) < 1e-3)
-    assert np.array_equal(decided[~band], mh[~band])
-    assert torch.isfinite(o.float()).all()
-    rep = _compare(d, res, splits=splits, a=a, tiles=[(0, 0, 0), (37, 0, 0), (63, 0, 0)], tile_rows=128,
-                   out_bf16=True)
-    print(f"sparsity {float((mh == 1).sum()) / live.sum():.3f}; {rep}")
+    d = _mla_full_size()
+    lam = _calibrated_lambda(m, d, splits=splits, target=target, tile_rows=128)
+    res = _run(m, d, splits=splits, lam=lam, tile_rows=128, out_dtype=torch.bfloat16)
+    sp = _check_whole_mask(res, oracle.ln_threshold(lam=lam), target)
+    tiles = _seeded_tiles(64, 1, 1, 22, synth.config_seed(5), must=[(0, 0, 0), (63, 0, 0)])
+    rep = _compare(d, res, splits=splits, lam=lam, tiles=tiles, tile_rows=128, out_bf16=True)
+    print(f"S={splits} lambda={lam:.6g} sparsity {sp:.4f}; {rep}")
+
+
+def test_latent_mla_full_size_redo_with_splits():
+    """The 128-head latent kernel's redo path at full size and in the benchmark's launch (8 splits):
+    in four sequences a key inside a split, past that split's first block, gets a scaled logit of +60
+    (against a first-block maximum near +10), so those splits raise their reference max and start
+    over; at lambda = 0 every sequence still matches the oracle and nothing is skipped."""
+    m = _lib()
+    d = _mla_full_size()
+    scale = 1.0 / math.sqrt(576)
+    planted = {3: 4096 + 700, 17: 2 * 4096 + 64 * 9 + 5, 40: 7 * 4096 + 4095, 63: 5 * 4096 + 2000}
+    for b, key in planted.items():
+        pid = int(d.block_table[b, key // d.page_size])
+        d.k_cache[pid, 0, key % d.page_size, 574] = 60.0 / scale   # the sink channel: q = 1 there
+    res = _run(m, d, splits=8, lam=0.0, tile_rows=128, out_dtype=torch.float32)
+    _check_whole_mask(res, -math.inf, 0.0)
+    tiles = sorted({(b, 0, 0) for b in planted} | {(0, 0, 0), (30, 0, 0)})
+    rep = _compare(d, res, splits=8, lam=0.0, tiles=tiles, tile_rows=128)
+    print(rep)
+    assert rep.skipped == 0
 
 
 @pytest.mark.parametrize("splits", [1, 4])
@@ -235,26 +321,22 @@ def test_multi_token_decode(T, tile_rows, splits, a):
         assert rep.skipped == 0
 
 
-def test_multi_token_decode_full_size_sampled():
-    """The multi-token benchmark launch: batch 32, 32 q / 8 kv heads, d = 128, context 32768, the last
-    4 positions of each sequence as queries, tiles of 4 tokens x 4 heads, 8 splits; sampled tiles
-    against the oracle, all masks consistent with the critical values."""
+@pytest.mark.parametrize("T", [2, 4])
+def test_multi_token_decode_full_size_at_benchmark_threshold(T):
+    """The benchmarked multi-token launches: batch 32, 32 q / 8 kv heads, d = 128, context 32768, the
+    last T positions of each sequence as queries, tiles of T tokens x 4 heads, 8 splits, bf16 output,
+    lambda calibrated for 73 % as the benchmark does; 24 seeded tiles against the oracle, every
+    tile's mask against its critical values."""
     m = _lib()
-    ctx, T = 32768, 4
+    ctx = 32768
     d = synth.decode_inputs(batch=32, hq=32, hkv=8, ctx=ctx, d=128, seed=synth.config_seed(3, 2), device="cuda",
                             num_q_tokens=T)
-    a = 0.05 * ctx
-    res = _run(m, d, splits=8, a=a, tile_rows=4)
-    o, lse, mask, crit, cnt = res
-    ln_lam = math.log(min(1.0, a / ctx))
-    mh, ch = mask.cpu().numpy(), crit.cpu().numpy()
-    live = mh != 2
-    decided = np.where(live, np.where(ch < ln_lam, 1, 0), 2)
-    band = live & (np.abs(ch - ln_lam) < 1e-3)
-    assert np.array_equal(decided[~band], mh[~band])
-    assert torch.isfinite(o).all()
-    rep = _compare(d, res, splits=8, a=a, tile_rows=4, tiles=[(0, 0, 0), (13, 5, 0), (31, 7, 0)])
-    print(f"sparsity {float((mh == 1).sum()) / live.sum():.3f}; {rep}")
+    lam = _calibrated_lambda(m, d, splits=8, target=0.73, tile_rows=4)
+    res = _run(m, d, splits=8, lam=lam, tile_rows=4, out_dtype=torch.bfloat16)
+    sp = _check_whole_mask(res, oracle.ln_threshold(lam=lam), 0.73)
+    tiles = _seeded_tiles(32, 8, 1, 22, synth.config_seed(3, 2) + T, must=[(0, 0, 0), (31, 7, 0)])
+    rep = _compare(d, res, splits=8, lam=lam, tile_rows=4, tiles=tiles, out_bf16=True)
+    print(f"T={T} lambda={lam:.6g} sparsity {sp:.4f}; {rep}")
 
 
 def test_multi_token_decode_short_sequence_rows_without_keys():

@@ -59,15 +59,20 @@ def _compare_all(q, k, v, res, *, causal, bq, bk, splits, ln_lam, tiles=None, ou
     if full:
         tiles = [(b, h, t) for b in range(B) for h in range(Hq) for t in range(nqt)]
         qh, kh, vh = host64(q), host64(k), host64(v)
+    cache = {}
     for (b, h, t) in tiles:
         r0, r1 = t * bq, min((t + 1) * bq, Lq)
         if full:
             qt_, kt_, vt_, bb, hh, tt = qh, kh, vh, b, h, t
         else:
-            # host copies of this tile's rows and of its kv head only
-            qt_ = host64(q[b:b + 1, h:h + 1])
-            kt_ = host64(k[b:b + 1, h // G:h // G + 1])
-            vt_ = host64(v[b:b + 1, h // G:h // G + 1])
+            # host copies of this head's queries and of its kv head only (kept while consecutive tiles
+            # share them)
+            if (b, h) not in cache:
+                kv = cache.get("kv") if cache.get("kv_id") == (b, h // G) else \
+                    (host64(k[b:b + 1, h // G:h // G + 1]), host64(v[b:b + 1, h // G:h // G + 1]))
+                cache = {(b, h): host64(q[b:b + 1, h:h + 1]), "kv": kv, "kv_id": (b, h // G)}
+            qt_ = cache[(b, h)]
+            kt_, vt_ = cache["kv"]
             bb, hh, tt = 0, 0, t
         kw = dict(causal=causal, block_q=bq, block_k=bk, num_splits=splits, ln_lam=ln_lam)
         ref = oracle.prefill_tile(qt_, kt_, vt_, bb, hh, tt, **kw)
@@ -151,28 +156,70 @@ def test_stats_only_matches_full_pass():
     assert torch.equal(full[5], st[5])
 
 
-def test_llama8b_gqa_32k_sampled_tiles():
-    """Full-size GQA prefill (32 q / 8 kv heads, d = 128, L = 32768, causal, 128 x 128 blocks) in the
-    launch configuration the benchmark times; sampled tiles against the oracle, and for every tile
-    the mask is the critical value compared with ln(lambda)."""
-    m = _lib()
-    L = 32768
-    inp = synth.prefill_inputs(batch=1, hq=32, hkv=8, L=L, d=128, block_k=128, window=True,
-                               seed=synth.config_seed(2), device="cuda")
-    lam = 0.02   # a sparse operating point (about 3/4 of the blocks skipped on this generator)
-    res = _run(m, inp.q, inp.k, inp.v, causal=True, bq=128, bk=128, splits=1, lam=lam)
+def benchmark_lambda(m, inp, target):
+    """lambda for a target sparsity, set the way the benchmark sets it: a stats-only pass (critical
+    values of every tile), the benchmark's seeded 8-tile (1024-row) calibration sample, and the
+    library's quantile of that sample's critical values."""
+    import bench
+    if target == 0.0:
+        return 0.0
+    B, Hq, L, _ = inp.q.shape
+    nqt = -(-L // 128)
+    crit = torch.empty(B, Hq, nqt, -(-inp.k.shape[2] // 128), dtype=torch.float32, device=inp.q.device)
+    m.blasst_prefill(inp.q, inp.k, inp.v, None, causal=True, block_q=128, block_k=128, lam=0.0, crit=crit,
+                     stats_only=True)
+    torch.cuda.synchronize()
+    sample = torch.stack([crit[0, h, t] for h, t in bench.stratified_tiles(torch, nqt, Hq, bench.CALIB_TILES, 4242)])
+    return math.exp(m.blasst_calib_quantile(sample.cpu().numpy(), target))
+
+
+def seeded_prefill_tiles(Hq, nqt, count, seed):
+    """Tiles of the last, a middle and the first causal level of a few heads, plus `count` seeded
+    picks over all (head, query tile)."""
+    rng = np.random.default_rng(seed)
+    must = {(0, nqt - 1), (Hq - 1, nqt - 1), (Hq // 2, nqt // 2), (Hq // 3, nqt // 2 - 1), (1, 0), (Hq - 2, 1)}
+    picks = {(int(h), int(t)) for h, t in zip(rng.integers(0, Hq, count), rng.integers(0, nqt, count))}
+    return sorted((0, h, t) for h, t in must | picks)
+
+
+def check_full_size_prefill(m, inp, lam, target, *, seed, count=20):
+    """Runs the benchmark's prefill launch (bf16 out) at lambda and checks it: the sampled tiles against
+    the oracle (mask, critical values, O, LSE), every tile's mask against its critical values, the
+    counters against the mask, and the achieved sparsity against the calibration target."""
+    B, Hq, L, _ = inp.q.shape
+    res = _run(m, inp.q, inp.k, inp.v, causal=True, bq=128, bk=128, splits=1, lam=lam, out_dtype=torch.bfloat16)
     o, lse, mask, crit, cnt, _ = res
-    ln_lam = math.log(lam)
+    ln_lam = oracle.ln_threshold(lam=lam)
     mh, ch = mask.cpu().numpy(), crit.cpu().numpy()
     live = mh != 2
-    assert live.sum() == 32 * 256 * 257 // 2
+    nqt = L // 128
+    assert live.sum() == B * Hq * nqt * (nqt + 1) // 2
     decided = np.where(live, np.where(ch < ln_lam, 1, 0), 2)
     band = live & (np.abs(ch - ln_lam) < 1e-3)
     assert np.array_equal(decided[~band], mh[~band])
-    tiles = [(0, 0, 255), (0, 13, 128), (0, 31, 0), (0, 7, 201), (0, 20, 64)]
-    rep = _compare_all(inp.q, inp.k, inp.v, res, causal=True, bq=128, bk=128, splits=1, ln_lam=ln_lam,
-                       tiles=tiles)
-    print(f"sparsity {float((mh == 1).sum()) / live.sum():.3f}; {rep}")
+    sp = float((mh == 1).sum()) / live.sum()
+    if target == 0.0:
+        assert sp == 0.0
+    elif target is not None:
+        assert abs(sp - target) < 0.05, f"sparsity {sp} at target {target}"
+    tiles = seeded_prefill_tiles(Hq, nqt, count, seed)
+    rep = _compare_all(inp.q, inp.k, inp.v, res, causal=True, bq=128, bk=128, splits=1, ln_lam=ln_lam, tiles=tiles,
+                       out_bf16=True)
+    return sp, len(tiles), rep
+
+
+@pytest.mark.parametrize("target", [0.75, 0.5, 0.0])
+def test_llama8b_gqa_32k_at_benchmark_thresholds(target):
+    """The benchmarked prefill launch (32 q / 8 kv heads, d = 128, L = 32768, causal, 128 x 128 blocks,
+    bf16 in/out, on the benchmark's own seeded inputs) at lambda calibrated for 75 % and 50 % sparsity
+    exactly as the benchmark does it, and at lambda = 0: 26 tiles against the oracle, every tile's
+    mask against its critical values."""
+    m = _lib()
+    inp = synth.prefill_inputs(batch=1, hq=32, hkv=8, L=32768, d=128, block_k=128, window=True,
+                               seed=synth.config_seed(2), device="cuda")
+    lam = benchmark_lambda(m, inp, target)
+    sp, n, rep = check_full_size_prefill(m, inp, lam, target, seed=int(target * 100) + 7)
+    print(f"lambda={lam:.6g} sparsity {sp:.4f} over all tiles; {n} tiles vs oracle: {rep}")
 
 
 def test_no_decision_mode_equals_lambda_zero():

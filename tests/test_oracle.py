@@ -387,3 +387,48 @@ def test_multi_token_decode_rows_without_keys():
         for h in range(8):
             logits = 0.4 * Kc[1][h // 4][:n] @ q[1, t, h]
             assert np.max(np.abs(r["o"][1, t, h] - softmax(logits) @ Vc[1][h // 4][:n])) < 1e-12
+
+
+# ---------------------------------------------------------------------------------------------
+# the dense reference itself
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["causal", "random", "causal_offset", "full"])
+def test_softmax_attention_equals_library_attention(kind):
+    """oracle.softmax_attention against torch's scaled_dot_product_attention (fp64, CPU, boolean
+    mask) for the output and scipy's logsumexp for the LSE, on masks built here independently:
+    bottom-right causal, causal with more rows than keys (rows without any visible key), a seeded
+    random mask with empty rows, and no mask.  A non-default scale catches a dropped or doubled
+    scale; the random mask catches a dropped visibility test."""
+    import torch
+    rng = np.random.default_rng({"causal": 1, "random": 2, "causal_offset": 3, "full": 4}[kind])
+    R, N, D, Dv = 23, 31, 12, 7
+    if kind == "causal_offset":
+        R, N = 40, 29          # rows 0..10 see no key under bottom-right alignment
+    q = rng.standard_normal((R, D)) * 1.7
+    k = rng.standard_normal((N, D))
+    v = rng.standard_normal((N, Dv))
+    if kind in ("causal", "causal_offset"):
+        vis = np.array([[c <= r + (N - R) for c in range(N)] for r in range(R)])
+    elif kind == "random":
+        vis = rng.random((R, N)) < 0.3
+        vis[[2, 9]] = False
+        vis[5] = False
+        vis[5, 17] = True      # a row with exactly one visible key
+    else:
+        vis = np.ones((R, N), dtype=bool)
+    scale = 0.29
+    o, lse = oracle.softmax_attention(q, k, v, vis, scale)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x))[None, None]
+    want = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=t(vis),
+                                                            scale=scale)[0, 0].numpy()
+    empty = ~vis.any(axis=1)
+    assert (kind in ("random", "causal_offset")) == bool(empty.any())
+    assert np.max(np.abs(o[~empty] - want[~empty])) < 1e-12
+    assert np.all(o[empty] == 0.0) and np.all(lse[empty] == -np.inf)
+    logits = scale * (q @ k.T)
+    for r in np.nonzero(~empty)[0]:
+        assert abs(lse[r] - logsumexp(logits[r][vis[r]])) < 1e-12
+    if kind == "random":
+        # a single visible key gets all the weight
+        assert np.max(np.abs(o[5] - v[17])) < 1e-14 and abs(lse[5] - logits[5, 17]) < 1e-14
