@@ -286,6 +286,25 @@ blasst_status blasst_decode(const blasst_decode_params *params, void *stream);
  * and sets the last error when the params are invalid. */
 size_t blasst_decode_workspace_size(const blasst_decode_params *params);
 
+/* Bytes of the scratch array behind blasst_decode_no_alloc (one array per GPU). */
+#define BLASST_NO_ALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * blasst_decode without a workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops or harnesses that forbid hipMalloc).  It computes exactly what
+ * blasst_decode computes, with the same kernels; params->workspace and workspace_bytes are ignored.
+ * The per-split partials go to a device array of BLASST_NO_ALLOC_SCRATCH_BYTES bytes that the
+ * library holds on every GPU it runs on, until the process ends; params whose
+ * blasst_decode_workspace_size() exceeds it are refused with BLASST_ERR_WORKSPACE before any HIP
+ * call (GQA decode at batch 32, 32 q heads, 16 splits needs 8.5 MB; latent decode at batch 64 and 8
+ * splits, 134 MB, is refused).  The call allocates nothing: on the first call on a device it looks
+ * up that device's address of the array (hipGetSymbolAddress), and every later call reuses it.
+ * Every call on one GPU shares that GPU's array and nothing in it needs clearing (every partial is
+ * rewritten), so calls that may overlap on one GPU (two streams, or two host threads without
+ * ordering) race on it: order them on one stream, or use blasst_decode with separate workspaces.
+ */
+blasst_status blasst_decode_no_alloc(const blasst_decode_params *params, void *stream);
+
 /*
  * Host-only calibration [xllm-io review, 核心公式 calibration model lambda * L = alpha * exp(beta s);
  * 模型组件 calibration module: one forward pass over a sample].

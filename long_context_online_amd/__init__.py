@@ -12,6 +12,7 @@ from .blasst import (  # noqa: F401
     backward_params,
     blasst_decode,
     blasst_decode_workspace_size,
+    blasst_decode_no_alloc,
     blasst_calib_quantile,
     blasst_calibrate,
     blasst_lambda_for,

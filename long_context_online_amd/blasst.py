@@ -27,7 +27,7 @@ EXPORTED = [
     "blasst_calibrate", "blasst_lambda_for", "blasst_status_string", "blasst_last_error",
     "blasst_version", "blasst_prefill_params_size", "blasst_decode_params_size",
     "blasst_prefill_backward", "blasst_prefill_backward_workspace_size", "blasst_prefill_backward_params_size",
-    "blasst_prefill_paged", "blasst_prefill_paged_params_size",
+    "blasst_prefill_paged", "blasst_prefill_paged_params_size", "blasst_decode_no_alloc",
 ]
 
 
@@ -139,6 +139,8 @@ def lib():
         L.blasst_decode.restype = ctypes.c_int
         L.blasst_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeParams)]
         L.blasst_decode_workspace_size.restype = ctypes.c_size_t
+        L.blasst_decode_no_alloc.argtypes = [ctypes.POINTER(DecodeParams), ctypes.c_void_p]
+        L.blasst_decode_no_alloc.restype = ctypes.c_int
         L.blasst_prefill_paged.argtypes = [ctypes.POINTER(PagedPrefillParams), ctypes.c_void_p]
         L.blasst_prefill_paged.restype = ctypes.c_int
         L.blasst_prefill_paged_params_size.restype = ctypes.c_size_t
@@ -383,6 +385,15 @@ def blasst_decode(q, k_cache, v_cache, block_table, seq_lens, o, *, stream=None,
     block_table [B, max_pages] int32; seq_lens [B] int32; o [B, Hq, Dv] or [B, T, Hq, Dv]."""
     p = decode_params(q, k_cache, v_cache, block_table, seq_lens, o, **kw)
     _check(lib().blasst_decode(ctypes.byref(p), _stream(stream)))
+
+
+def blasst_decode_no_alloc(q, k_cache, v_cache, block_table, seq_lens, o, *, stream=None, **kw):
+    """blasst_decode with the split partials in the library's own per-GPU scratch array instead of
+    a workspace (for callers that cannot allocate); same arguments, no `workspace`."""
+    if kw.get("workspace") is not None:
+        raise ValueError("blasst_decode_no_alloc takes no workspace")
+    p = decode_params(q, k_cache, v_cache, block_table, seq_lens, o, **kw)
+    _check(lib().blasst_decode_no_alloc(ctypes.byref(p), _stream(stream)))
 
 
 def blasst_calib_quantile(crit, target_s: float) -> float:

@@ -154,6 +154,26 @@ def test_decode_rejects_invalid_arguments(m, over, status):
     assert lib.blasst_last_error()
 
 
+def test_decode_no_alloc_rejects_before_any_hip_call(m):
+    """The allocation-free decode checks its arguments like blasst_decode (no GPU needed to reach
+    them), and refuses params whose split partials exceed the library's scratch array."""
+    lib = m.lib()
+    cap = 64 << 20
+    for over, status in DECODE_BAD:
+        if over == {"workspace": None}:
+            continue          # ignored here: there is no workspace
+        p = _decode(**over)
+        assert lib.blasst_decode_no_alloc(ctypes.byref(p), None) == status
+        assert lib.blasst_last_error()
+    big = _decode(batch=512, num_splits=16)       # 512 x 32 x 16 partials of 129 floats > 64 MiB
+    assert lib.blasst_decode_workspace_size(ctypes.byref(big)) > cap
+    assert lib.blasst_decode_no_alloc(ctypes.byref(big), None) == 4
+    assert b"scratch" in lib.blasst_last_error()
+    latent = _decode(v_cache=None, batch=64, num_q_heads=128, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
+                     tile_rows=128, num_splits=8)
+    assert lib.blasst_decode_no_alloc(ctypes.byref(latent), None) == 4
+
+
 def test_decode_workspace_size(m):
     lib = m.lib()
     p = _decode()
