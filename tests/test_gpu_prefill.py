@@ -283,3 +283,22 @@ def test_more_queries_than_keys(splits):
     assert torch.all(o[:, :, :200] == 0) and torch.all(lse[:, :, :200] == float("-inf"))
     rep = _compare_all(inp.q, k, v, res, causal=True, bq=128, bk=128, splits=splits, ln_lam=math.log(0.01))
     print(rep)
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.01])
+def test_late_large_logit_raises_the_reference_with_probabilities_pending(lam):
+    """A key of block 3 gets a scaled logit of about +40 for every query that sees it (first-block
+    maxima are near +10), so the accumulation reference of those rows jumps at block 3 while block 2's
+    probabilities are still waiting for their P.V product: the kernel must rescale O, the row sums and
+    those pending probabilities alike.  Every tile against the oracle, fp32 and bf16 output."""
+    m = _lib()
+    L = 640
+    for out_dtype in (torch.float32, torch.bfloat16):
+        inp = synth.prefill_inputs(batch=1, hq=4, hkv=2, L=L, d=128, block_k=128, window=True, seed=91,
+                                   device="cuda")
+        scale = 1.0 / math.sqrt(128)
+        inp.k[0, :, 3 * 128 + 17, 126] = 40.0 / scale   # channel D - 2 carries the sink: q = 1 there
+        res = _run(m, inp.q, inp.k, inp.v, causal=True, bq=128, bk=128, splits=1, lam=lam, out_dtype=out_dtype)
+        rep = _compare_all(inp.q, inp.k, inp.v, res, causal=True, bq=128, bk=128, splits=1,
+                           ln_lam=oracle.ln_threshold(lam=lam), out_bf16=out_dtype == torch.bfloat16)
+        print(f"lambda={lam} {out_dtype}: {rep}")
