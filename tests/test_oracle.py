@@ -304,6 +304,43 @@ def test_latent_decode_equals_gqa_with_copied_values():
     assert np.max(np.abs(r1["o"] - r2["o"])) == 0.0
 
 
+@pytest.mark.parametrize("T,tile_rows,S", [(2, 3, 1), (4, 6, 2), (3, 2, 3)])
+def test_multi_token_latent_decode_equals_gqa_with_copied_values(T, tile_rows, S):
+    """Several query tokens per sequence on latent attention (one shared head, V = the first Dv
+    channels of K) equal multi-token decode with a separate V cache holding a copy of those channels
+    (masks and outputs, at a threshold that skips), and at lambda = 0 they equal causal softmax over
+    those keys and values written out with scipy: token t of a sequence of length L sees keys
+    0 ... L - T + t."""
+    rng = np.random.default_rng(41 + T)
+    lens = (23, 16, T + 1)
+    _, kc, _, table, lens, Kc, _ = _random_paged(rng, Hq=6, Hkv=1, D=10, latent=True, lens=lens)
+    q = _token_queries(rng, 3, T, 6, 10)
+    # an attention sink at token 0 (the last channel, outside the V channels) so that blocks skip
+    q[..., -1] = 1.0
+    for b in range(3):
+        kc[table[b, 0], 0, 0, -1] = 30.0
+        Kc[b][0, 0, -1] = 30.0
+    Dv = 7
+    vc = np.transpose(kc[..., :Dv], (0, 1, 3, 2)).copy()
+    kw = dict(page_size=4, block_k=4, num_splits=S, scale=0.3, tile_rows=tile_rows)
+    for lam in (0.2, 0.0):
+        r1 = oracle.decode(q, kc, None, table, lens, head_dim_v=Dv, lam=lam, **kw)
+        r2 = oracle.decode(q, kc, vc, table, lens, lam=lam, **kw)
+        assert np.array_equal(r1["mask"], r2["mask"])
+        assert np.max(np.abs(r1["o"] - r2["o"])) == 0.0
+        assert np.array_equal(r1["lse"], r2["lse"])
+        if lam > 0:
+            assert np.any(r1["mask"] == SKIPPED)
+    for b in range(3):
+        L = int(lens[b])
+        K = Kc[b][0]
+        for t in range(T):
+            logits = 0.3 * (q[b, t] @ K.T)[:, :L - T + t + 1]
+            want = softmax(logits, axis=1) @ K[:L - T + t + 1, :Dv]
+            assert np.max(np.abs(r1["o"][b, t] - want)) < 1e-12
+            assert np.max(np.abs(r1["lse"][b, t] - logsumexp(logits, axis=1))) < 1e-12
+
+
 def test_decode_a_over_L_uses_each_sequence_length():
     rng = np.random.default_rng(41)
     q, kc, vc, table, lens, Kc, Vc = _random_paged(rng)
