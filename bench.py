@@ -231,6 +231,18 @@ class Prefill:
         return {"lambda0_ms": round(t0, 4), "no_decision_ms": round(t1, 4),
                 "no_decision_over_lambda0_throughput": round(t1 / t0, 4)}
 
+    def v_staging_ablation(self, lam, steps):
+        """What not loading the V blocks of skipped blocks is worth: the same threshold with V staged
+        for every live block (the pages' policy) against V staged for kept blocks only."""
+        kept = timed(self.torch, lambda: self.run(lam), steps)
+        every = timed(self.torch, lambda: self.run(lam, v_staging=1), steps)
+        kept = min(kept, timed(self.torch, lambda: self.run(lam), steps))
+        every = min(every, timed(self.torch, lambda: self.run(lam, v_staging=1), steps))
+        dense = timed(self.torch, lambda: self.run(0.0), steps)
+        return {"v_kept_only_ms": round(kept, 4), "v_every_block_ms": round(every, 4),
+                "speedup_from_skipping_v_loads": round(every / kept, 3),
+                "speedup_vs_dense_with_v_every_block": round(dense / every, 3), "lambda": lam}
+
     def head_stats(self, lam):
         """Distribution over q heads of the sparsity one threshold gives each head (per-head counters)."""
         from long_context_online_amd import analysis
@@ -748,6 +760,7 @@ def main():
             result["prefill_s050"] = pre.measure(lam50, max(3, args.steps // 2))
             result["prefill_s050"]["target_sparsity"] = 0.5
             result["prefill_decision_overhead"] = pre.decision_overhead(max(3, args.steps // 2))
+            result["prefill_v_staging"] = pre.v_staging_ablation(lam_p, max(3, args.steps // 2))
             result["prefill_heads"] = head_heterogeneity(m, torch, synth, pre, lam_p, max(3, args.steps // 2))
             bw = Backward(m, torch, pre, lam_p)
             result["prefill_backward"] = bw.measure(max(3, args.steps // 2))
@@ -837,6 +850,19 @@ def main():
                  "dense_ms": r["dense_ms"], "speedup_vs_dense": r["speedup_vs_dense"], "hbm_gbps": r["hbm_gbps"],
                  "lambda": r["lambda"]})
             del mla
+            torch.cuda.empty_cache()
+        result["mla_decode"]["multi_token"] = {}
+        for T in (2, 4):
+            mt = Decode(m, torch, synth, ctx=M_CTX, latent=True, seed=synth.config_seed(5, T), num_q_tokens=T,
+                        tile_rows=64 // T, splits=M_SPLITS)
+            lam = mt.calibrate(M_TARGETS[-1])
+            r = mt.measure(lam, args.steps)
+            r.update({"target_sparsity": M_TARGETS[-1], "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
+                      "splits": M_SPLITS,
+                      "workload": f"the latent decode workload with {T} query tokens per sequence (the last {T} "
+                                  f"positions), tiles of {T} tokens x {64 // T} heads, {M_SPLITS} splits"})
+            result["mla_decode"]["multi_token"][f"T{T}"] = r
+            del mt
             torch.cuda.empty_cache()
         result["calibration"] = calibration_sweep(m, torch, synth, args.steps)
         result["ceilings"] = practical_ceilings(torch)

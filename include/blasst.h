@@ -74,6 +74,16 @@ typedef struct {
   double a;         /* mode BLASST_THR_A_OVER_L, a >= 0 */
 } blasst_threshold;
 
+/* V staging of the bf16 prefill (blasst_prefill_params.v_staging).  The result does not depend on
+ * it: a skipped block never enters P.V.
+ *   BLASST_V_KEPT (default): the V block of a key block is loaded only when a tile of the workgroup
+ *     kept that block, so a skipped block costs neither V bytes nor V staging;
+ *   BLASST_V_ALL: the V block of every live key block is loaded whether it is skipped or not, the
+ *     pages' policy (xllm-io review, 预填充内核优化: the value block is still loaded from HBM so that
+ *     prefetching stays regular), for measuring what skipping the V loads is worth.  Supported by
+ *     the bf16 kernels; the fp32 kernel stages every V block anyway. */
+typedef enum { BLASST_V_KEPT = 0, BLASST_V_ALL = 1 } blasst_v_staging;
+
 /* Counter slots written (accumulated with atomics) when `counters` is not NULL; the caller zeroes
  * the buffer before the call if it wants per-call numbers. */
 enum { BLASST_CNT_LIVE = 0, BLASST_CNT_SKIPPED = 1, BLASST_NUM_COUNTERS = 2 };
@@ -125,6 +135,7 @@ typedef struct {
   int32_t causal, block_q, block_k, num_splits, stats_only;
   float softmax_scale;
   unsigned long long *head_counters; /* nullable, see above */
+  int32_t v_staging;         /* blasst_v_staging: which V blocks the bf16 kernels stage in LDS */
 } blasst_prefill_params;
 
 /*

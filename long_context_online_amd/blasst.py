@@ -21,6 +21,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
 BF16, FP32 = 0, 1
 THR_LAMBDA, THR_A_OVER_L, THR_NONE = 0, 1, 2
 KEPT, SKIPPED, NOT_LIVE = 0, 1, 2
+V_KEPT, V_ALL = 0, 1
 
 EXPORTED = [
     "blasst_prefill", "blasst_prefill_workspace_size", "blasst_decode", "blasst_decode_workspace_size", "blasst_calib_quantile",
@@ -59,6 +60,7 @@ class PrefillParams(ctypes.Structure):
         ("num_splits", ctypes.c_int32), ("stats_only", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("head_counters", ctypes.c_void_p),
+        ("v_staging", ctypes.c_int32),
     ]
 
 
@@ -219,7 +221,7 @@ def _strides3(t):
 
 def prefill_params(q, k, v, o, *, causal, block_q, block_k, num_splits=1, lam=None, a=None,
                    softmax_scale=0.0, lse=None, skip_mask=None, crit=None, counters=None,
-                   stats_only=False, out_dtype=None, no_decision=False, head_counters=None):
+                   stats_only=False, out_dtype=None, no_decision=False, head_counters=None, v_staging=V_KEPT):
     """Fills the C params struct for blasst_prefill from tensors (no call)."""
     p = PrefillParams()
     p.struct_size = ctypes.sizeof(PrefillParams)
@@ -238,6 +240,7 @@ def prefill_params(q, k, v, o, *, causal, block_q, block_k, num_splits=1, lam=No
     p.num_splits, p.stats_only = num_splits, int(bool(stats_only))
     p.softmax_scale = float(softmax_scale)
     p.head_counters = _ptr(head_counters)
+    p.v_staging = int(v_staging)
     return p
 
 
@@ -256,7 +259,7 @@ def blasst_prefill(q, k, v, o, *, stream=None, **kw):
     """BLASST prefill forward.  q [B, Hq, Lq, D], k/v [B, Hkv, Lk, D], o [B, Hq, Lq, Dv]
     (last dim contiguous).  Keyword args follow the C params (causal, block_q, block_k,
     num_splits, lam or a, softmax_scale, lse, skip_mask, crit, counters, head_counters,
-    stats_only)."""
+    stats_only, v_staging)."""
     p = prefill_params(q, k, v, o, **kw)
     _check(lib().blasst_prefill(ctypes.byref(p), _stream(stream)))
 

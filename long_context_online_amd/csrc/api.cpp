@@ -184,6 +184,8 @@ static blasst_status validate_prefill(const blasst_prefill_params *p, bool need_
   if (p->out_dtype != BLASST_BF16 && p->out_dtype != BLASST_FP32) return fail(BLASST_ERR_INVALID_ARG, "bad out_dtype");
   if (p->causal != 0 && p->causal != 1) return fail(BLASST_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (!std::isfinite(p->softmax_scale)) return fail(BLASST_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (p->v_staging != BLASST_V_KEPT && p->v_staging != BLASST_V_ALL)
+    return fail(BLASST_ERR_INVALID_ARG, "v_staging must be BLASST_V_KEPT or BLASST_V_ALL");
   for (int i = 0; i < 3; ++i)
     if (p->q_stride[i] < 0 || p->k_stride[i] < 0 || p->v_stride[i] < 0 || p->o_stride[i] < 0)
       return fail(BLASST_ERR_INVALID_ARG, "strides must be >= 0");
@@ -257,6 +259,7 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *stream) {
   a.scale_log2 = (float)(scale * 1.4426950408889634);
   a.thr_raw = thr_raw_from(ln_lam, scale);
   a.decide = no_decision ? 0 : 1;
+  a.v_all = p->v_staging == BLASST_V_ALL ? 1 : 0;
 
   hipError_t e;
   if (p->in_dtype == BLASST_BF16)
@@ -304,10 +307,10 @@ static blasst_status validate_decode(const blasst_decode_params *p, bool need_pt
   const int T = p->num_q_tokens == 0 ? 1 : p->num_q_tokens;
   if (latent) {
     if (p->num_kv_heads != 1 || p->num_q_heads != 128 || p->head_dim_qk != 576 || p->head_dim_v != 512 ||
-        (tr != 128 && tr != 64) || T != 1)
+        !((tr == 128 && T == 1) || (int64_t)T * tr == 64))
       return fail(BLASST_ERR_UNSUPPORTED,
-                  "latent decode supports 128 q heads on 1 kv head, dims 576/512, tile_rows 128 or 64, one "
-                  "query token");
+                  "latent decode supports 128 q heads on 1 kv head, dims 576/512, and tiles of 128 heads (one "
+                  "query token) or 64 rows (num_q_tokens * tile_rows == 64)");
   } else {
     if (p->head_dim_qk != 128 || p->head_dim_v != 128 || (int64_t)T * tr > 16)
       return fail(BLASST_ERR_UNSUPPORTED, "decode supports head dim 128 and num_q_tokens * tile_rows <= 16");

@@ -38,6 +38,7 @@ struct PrefillArgs {
   float scale_log2;  // scale * log2(e): exp(scale*(s - m)) = exp2(scale_log2*(s - m))
   float thr_raw;     // ln(lambda) / scale: skip iff (m~ - m) < thr_raw on raw logits
   int decide;        // 0: no threshold at all (every live block kept, no vote)
+  int v_all;         // 1: stage V for every live block, skipped or not (else only for kept blocks)
   // Paged K/V (chunked prefill against a paged cache; the kernel's PAGED variant): k is the key
   // cache [pages][Hkv][16][D], v the value cache [pages][Hkv][D][16] (V transposed inside each
   // page), table [B][max_pages] page ids, seq_lens [B] the context length of each sequence, whose

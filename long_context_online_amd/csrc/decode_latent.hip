@@ -7,8 +7,12 @@
 //
 // MI355X design (64-head tiles; the 128-head tile runs the one-wave-per-SIMD kernel of
 // decode_mla.hip, which this file's launcher dispatches to):
-//   * one workgroup = (sequence, row tile, split); the row tile is TR = 64 q heads, one wave per 16
-//     heads; the tile's vote is a ballot per wave and one LDS flag per wave;
+//   * one workgroup = (sequence, row tile, split); the row tile is TR = 64 rows, one wave per 16
+//     rows; the tile's vote is a ballot per wave and one LDS flag per wave;
+//   * with T query tokens per sequence (the last T positions) the rows are (token, head) pairs,
+//     token-major: row t * tile_rows + i is token t of the tile's head i (tile_rows = TR / T heads),
+//     and keys past seq_len - T + t are masked for it like keys past the sequence end (the GQA
+//     kernel's multi-token tiles, on the latent cache);
 //   * the latent block (64 tokens x 576 channels = 72 KB) goes global -> LDS directly
 //     (global_load_lds_dwordx4, issued as assembly so the compiler does not wait for it before the
 //     current block's LDS reads), double-buffered and prefetched one block ahead, with the page
@@ -52,18 +56,15 @@ __global__ __launch_bounds__(TR / HPW * 64, 1) void decode_latent_kernel(DecodeA
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15;   // head inside the wave
+  const int n = lane & 15;   // row inside the wave
   const int grp = lane >> 4;
 
-  // workgroup -> (sequence, row tile, split); the row tiles of one (sequence, split) are 8 apart in
-  // launch order, so they land on the same XCD (round-robin dispatch) and share its L2 copy of K
-  int bid = blockIdx.x;
-  int rt = 0;
-  if (a.n_rt == 2) {
-    const int x = bid & 7, grp16 = bid >> 4;
-    rt = (bid >> 3) & 1;
-    bid = grp16 * 8 + x;
-  }
+  // workgroup -> (sequence, row tile, split); the n_rt row tiles of one (sequence, split) are 8
+  // apart in launch order, so they land on the same XCD (round-robin dispatch) and share its L2
+  // copy of K
+  const int x8 = blockIdx.x & 7;
+  const int rt = (blockIdx.x >> 3) % a.n_rt;
+  const int bid = (blockIdx.x >> 3) / a.n_rt * 8 + x8;
   const int split = bid % a.num_splits;
   const int b = bid / a.num_splits;
   if (b >= a.B) return;
@@ -74,7 +75,11 @@ __global__ __launch_bounds__(TR / HPW * 64, 1) void decode_latent_kernel(DecodeA
   const int j0 = split * chunk;
   const int j1 = min(J, j0 + chunk);
   const int npg = (L + PAGE - 1) / PAGE;
-  const int h = rt * TR + wave * HPW + n;    // q head of this lane
+  const int row = wave * HPW + n;            // row of the tile held by this lane
+  const int tok = row / a.tile_rows;         // its query token
+  const int h = rt * a.tile_rows + (row - tok * a.tile_rows);  // and q head
+  const int64_t qrow = ((int64_t)b * a.T + tok) * a.Hq + h;    // row of q (and of o, lse)
+  const int lim = L - a.T + tok;             // the last key this row sees
 
   float thr = a.thr_raw;
   if (a.thr_mode == 1) {
@@ -84,7 +89,7 @@ __global__ __launch_bounds__(TR / HPW * 64, 1) void decode_latent_kernel(DecodeA
 
   // q fragments: lane holds dims 32 kk + 8 grp .. +7 of head h
   bf16x8 qf[KSQ];
-  const __bf16 *qp = (const __bf16 *)a.q + ((int64_t)b * a.Hq + h) * DQK;
+  const __bf16 *qp = (const __bf16 *)a.q + qrow * DQK;
 #pragma unroll
   for (int kk = 0; kk < KSQ; ++kk) qf[kk] = *(const bf16x8 *)(qp + kk * 32 + grp * 8);
   // consume the q loads here, so their waits are not placed inside the block loop (where they
@@ -165,12 +170,12 @@ __global__ __launch_bounds__(TR / HPW * 64, 1) void decode_latent_kernel(DecodeA
       }
       if ((kk & 1) == 1) __builtin_amdgcn_sched_barrier(0);
     }
-    if (key0 + BK > L) {
+    if (key0 + BK > L - a.T + 1) {   // keys past a row's last visible key (or the sequence end)
 #pragma unroll
       for (int mt = 0; mt < MTK; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (key0 + mt * 16 + grp * 4 + r >= L) s[mt][r] = kNegInf;
+          if (key0 + mt * 16 + grp * 4 + r > lim) s[mt][r] = kNegInf;
     }
     float mx = kNegInf;
 #pragma unroll
@@ -263,7 +268,7 @@ __global__ __launch_bounds__(TR / HPW * 64, 1) void decode_latent_kernel(DecodeA
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? m_acc * a.scale + __logf(l_tot) : kNegInf;
   if (a.num_splits == 1) {
-    const int64_t ob = ((int64_t)b * a.Hq + h) * DV + grp * 4;
+    const int64_t ob = qrow * DV + grp * 4;
 #pragma unroll
     for (int dvt = 0; dvt < DVT; ++dvt) {
       if (OUT_F32) {
@@ -275,9 +280,9 @@ __global__ __launch_bounds__(TR / HPW * 64, 1) void decode_latent_kernel(DecodeA
         *(u32x2 *)((__bf16 *)a.o + ob + dvt * 16) = w;
       }
     }
-    if (a.lse && grp == 0) a.lse[(int64_t)b * a.Hq + h] = lse;
+    if (a.lse && grp == 0) a.lse[qrow] = lse;
   } else {
-    const int64_t pb = ((int64_t)b * a.Hq + h) * a.num_splits + split;
+    const int64_t pb = qrow * a.num_splits + split;
     float *wo = a.ws_o + pb * DV + grp * 4;
 #pragma unroll
     for (int dvt = 0; dvt < DVT; ++dvt) *(f32x4 *)(wo + dvt * 16) = o_acc[dvt] * inv;
@@ -307,10 +312,11 @@ hipError_t launch_decode_latent(const DecodeArgs &a, hipStream_t st) {
     const hipError_t e = launch_decode_mla128(a, st);
     if (e != hipSuccess || a.num_splits == 1 || a.stats_only) return e;
     return launch_decode_combine(a, DV, st);
-  } else if (a.tile_rows == 64) {
-    // two row tiles per (sequence, split): round the (sequence, split) count up to a multiple of 8
+  } else if (a.T * a.tile_rows == 64) {
+    // 64-row tiles (64 heads, or 2 tokens x 32 heads, or 4 tokens x 16 heads), n_rt per (sequence,
+    // split): round the (sequence, split) count up to a multiple of 8 (see the kernel's mapping)
     const int pairs = (a.B * a.num_splits + 7) / 8 * 8;
-    launch_tr<64>(a, pairs * 2, st);
+    launch_tr<64>(a, pairs * a.n_rt, st);
   } else {
     return hipErrorNotSupported;
   }

@@ -444,9 +444,9 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
         l_part2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, l_part2, false);
       }
     }
-    // V_t only for a block that a tile of the workgroup kept (the buffer held V_{t-2}, whose P.V
-    // every wave finished before this iteration's barrier)
-    if (!STATS && keep_any) load_v(t, buf);
+    // V_t only for a block that a tile of the workgroup kept, unless every live block's V is staged
+    // (the buffer held V_{t-2}, whose P.V every wave finished before this iteration's barrier)
+    if (!STATS && (keep_any || a.v_all)) load_v(t, buf);
     keep_pend = keep != 0;
   }
 

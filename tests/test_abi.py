@@ -85,6 +85,7 @@ PREFILL_BAD = [
     # bf16 K/V rows must not overlap (token stride >= head_dim): an expanded tensor (stride 0) and a
     # stride below the row length are refused
     ({"k_stride": (128 * 256 * 128, 256 * 128, 0)}, 2), ({"v_stride": (128 * 256 * 128, 256 * 128, 64)}, 2),
+    ({"v_staging": 2}, 1), ({"v_staging": -1}, 1),
 ]
 
 
@@ -140,6 +141,10 @@ DECODE_BAD = [
     ({"num_q_tokens": 5}, 2), ({"num_q_tokens": 9, "tile_rows": 2}, 2),
     ({"v_cache": None, "num_kv_heads": 1, "num_q_heads": 128, "head_dim_qk": 576, "head_dim_v": 512,
       "tile_rows": 128, "num_q_tokens": 2}, 2),
+    ({"v_cache": None, "num_kv_heads": 1, "num_q_heads": 128, "head_dim_qk": 576, "head_dim_v": 512,
+      "tile_rows": 32, "num_q_tokens": 3}, 2),
+    ({"v_cache": None, "num_kv_heads": 1, "num_q_heads": 128, "head_dim_qk": 576, "head_dim_v": 512,
+      "tile_rows": 64, "num_q_tokens": 2}, 2),
     # threshold mode NONE (no decisions) takes no decision diagnostics, whatever `a` holds
     ({"thr": (2, 0, 0.0, 5.0), "skip_mask": FAKE}, 1), ({"thr": (2, 0, 0.0, 5.0), "crit": FAKE}, 1),
     ({"thr": (2, 0, 0.0, float("nan")), "stats_only": 1}, 1),

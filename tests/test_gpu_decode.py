@@ -364,3 +364,39 @@ def test_multi_token_one_token_equals_single_token_layout():
     d.q = d.q[:, None].contiguous()
     r4 = _run(m, d, splits=4, lam=0.01)
     assert torch.equal(r1[0], r4[0][:, 0]) and torch.equal(r1[1], r4[1][:, 0]) and torch.equal(r1[2], r4[2])
+
+
+@pytest.mark.parametrize("T,splits", [(2, 1), (2, 3), (4, 1), (4, 5)])
+@pytest.mark.parametrize("a", [0.0, 4.0])
+def test_multi_token_latent_decode(T, splits, a):
+    """T query tokens per sequence on the latent cache (128 heads on one 576-channel latent head, V =
+    the first 512 channels): tiles of 64 rows = T tokens x 64 / T heads, each token seeing keys up to
+    seq_len - T + t; ragged lengths including sequences no longer than T, NaN-poisoned spare pages."""
+    m = _lib()
+    lens = [700, 64, T + 1, 333, T]
+    d = synth.decode_inputs(batch=len(lens), hq=128, hkv=1, ctx=None, d=576, dv=512, seq_lens=lens, seed=90 + T,
+                            device="cuda", latent=True, num_q_tokens=T)
+    tr = 64 // T
+    res = _run(m, d, splits=splits, a=a, tile_rows=tr)
+    rep = _compare(d, res, splits=splits, a=a, tile_rows=tr)
+    print(f"T={T} S={splits} a={a}: {rep}")
+    if a == 0.0:
+        assert rep.skipped == 0
+
+
+@pytest.mark.parametrize("T", [2, 4])
+def test_multi_token_latent_decode_full_size_at_benchmark_threshold(T):
+    """The benchmarked multi-token latent launch: batch 64, 128 heads on one latent head, context
+    32768, the last T positions of each sequence as queries, 64-row tiles (T tokens x 64 / T heads),
+    8 splits, bf16 output, lambda calibrated for 73 % as the benchmark does; 20 seeded tiles against
+    the oracle, every tile's mask against its critical values."""
+    m = _lib()
+    d = synth.decode_inputs(batch=64, hq=128, hkv=1, ctx=32768, d=576, dv=512, seed=synth.config_seed(5, T),
+                            device="cuda", latent=True, num_q_tokens=T)
+    tr = 64 // T
+    lam = _calibrated_lambda(m, d, splits=8, target=0.73, tile_rows=tr)
+    res = _run(m, d, splits=8, lam=lam, tile_rows=tr, out_dtype=torch.bfloat16)
+    sp = _check_whole_mask(res, oracle.ln_threshold(lam=lam), 0.73)
+    tiles = _seeded_tiles(64, 1, 128 // tr, 18, synth.config_seed(5, T), must=[(0, 0, 0), (63, 0, 128 // tr - 1)])
+    rep = _compare(d, res, splits=8, lam=lam, tile_rows=tr, tiles=tiles, out_bf16=True)
+    print(f"T={T} lambda={lam:.6g} sparsity {sp:.4f}; {rep}")

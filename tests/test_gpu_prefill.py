@@ -302,3 +302,28 @@ def test_late_large_logit_raises_the_reference_with_probabilities_pending(lam):
         rep = _compare_all(inp.q, inp.k, inp.v, res, causal=True, bq=128, bk=128, splits=1,
                            ln_lam=oracle.ln_threshold(lam=lam), out_bf16=out_dtype == torch.bfloat16)
         print(f"lambda={lam} {out_dtype}: {rep}")
+
+
+@pytest.mark.parametrize("D,blk", [(128, 128), (64, 64)])
+def test_v_staging_every_block_gives_the_same_bits(D, blk):
+    """Staging V for every live block (the pages' policy) instead of only for kept blocks changes
+    which bytes are loaded, not what is computed: outputs, LSE, masks and counters are bit-identical
+    at a threshold that skips, and the oracle agrees."""
+    m = _lib()
+    inp = synth.prefill_inputs(batch=1, hq=4, hkv=2, L=900, d=D, block_k=blk, window=True, seed=95, device="cuda")
+    outs = []
+    for vs in (m.blasst.V_KEPT, m.blasst.V_ALL):
+        o = torch.full((1, 4, 900, D), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.empty(1, 4, 900, dtype=torch.float32, device="cuda")
+        mask = torch.empty(1, 4, -(-900 // blk), -(-900 // blk), dtype=torch.uint8, device="cuda")
+        cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+        m.blasst_prefill(inp.q, inp.k, inp.v, o, causal=True, block_q=blk, block_k=blk, lam=0.01, lse=lse,
+                         skip_mask=mask, counters=cnt, v_staging=vs)
+        torch.cuda.synchronize()
+        outs.append((o, lse, mask, cnt))
+    for x, y in zip(outs[0], outs[1]):
+        assert torch.equal(x, y)
+    assert int(outs[0][3][1]) > 0
+    res = _run(m, inp.q, inp.k, inp.v, causal=True, bq=blk, bk=blk, splits=1, lam=0.01)
+    assert torch.equal(res[0], outs[0][0])
+    print(_compare_all(inp.q, inp.k, inp.v, res, causal=True, bq=blk, bk=blk, splits=1, ln_lam=math.log(0.01)))
