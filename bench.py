@@ -854,13 +854,13 @@ def main():
         result["mla_decode"]["multi_token"] = {}
         for T in (2, 4):
             mt = Decode(m, torch, synth, ctx=M_CTX, latent=True, seed=synth.config_seed(5, T), num_q_tokens=T,
-                        tile_rows=64 // T, splits=M_SPLITS)
+                        tile_rows=M_HQ // T, splits=M_SPLITS)
             lam = mt.calibrate(M_TARGETS[-1])
             r = mt.measure(lam, args.steps)
             r.update({"target_sparsity": M_TARGETS[-1], "frac_of_hbm_peak": round(r["hbm_gbps"] / PEAK_HBM_GBPS, 4),
                       "splits": M_SPLITS,
                       "workload": f"the latent decode workload with {T} query tokens per sequence (the last {T} "
-                                  f"positions), tiles of {T} tokens x {64 // T} heads, {M_SPLITS} splits"})
+                                  f"positions), tiles of {T} tokens x {M_HQ // T} heads, {M_SPLITS} splits"})
             result["mla_decode"]["multi_token"][f"T{T}"] = r
             del mt
             torch.cuda.empty_cache()

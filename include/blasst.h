@@ -202,7 +202,8 @@ typedef struct {
  * Supported kernels: bf16 in, bf16/fp32 out; page_size 16; block_k 64;
  *   GQA/MHA/MQA: head_dim_qk == head_dim_v == 128, T * tile_rows <= 16;
  *   latent (v_cache NULL): 128 q heads on 1 kv head, head_dim_qk == 576, head_dim_v == 512,
- *   tile_rows 128 (one tile of all heads) or 64 (MLA-shaped), T == 1.
+ *   T * tile_rows == 128 (128-row tiles: all heads of one token, or T = 2, 4 tokens x 64, 32 heads)
+ *   or 64 (64-row tiles: T = 1, 2, 4 tokens x 64, 32, 16 heads).
  */
 typedef struct {
   size_t struct_size;        /* sizeof(blasst_decode_params) */

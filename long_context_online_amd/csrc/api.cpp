@@ -307,10 +307,10 @@ static blasst_status validate_decode(const blasst_decode_params *p, bool need_pt
   const int T = p->num_q_tokens == 0 ? 1 : p->num_q_tokens;
   if (latent) {
     if (p->num_kv_heads != 1 || p->num_q_heads != 128 || p->head_dim_qk != 576 || p->head_dim_v != 512 ||
-        !((tr == 128 && T == 1) || (int64_t)T * tr == 64))
+        !((int64_t)T * tr == 128 || (int64_t)T * tr == 64))
       return fail(BLASST_ERR_UNSUPPORTED,
-                  "latent decode supports 128 q heads on 1 kv head, dims 576/512, and tiles of 128 heads (one "
-                  "query token) or 64 rows (num_q_tokens * tile_rows == 64)");
+                  "latent decode supports 128 q heads on 1 kv head, dims 576/512, and tiles of 128 or 64 rows "
+                  "(num_q_tokens * tile_rows == 128 or 64)");
   } else {
     if (p->head_dim_qk != 128 || p->head_dim_v != 128 || (int64_t)T * tr > 16)
       return fail(BLASST_ERR_UNSUPPORTED, "decode supports head dim 128 and num_q_tokens * tile_rows <= 16");

@@ -307,8 +307,9 @@ hipError_t launch_decode_mla128(const DecodeArgs &a, hipStream_t st);
 
 hipError_t launch_decode_latent(const DecodeArgs &a, hipStream_t st) {
   if (a.Hq != 128 || a.Hkv != 1 || a.page != PAGE || a.block_k != BK) return hipErrorNotSupported;
-  if (a.tile_rows == 128) {
-    // all 128 heads in one tile: the one-wave-per-SIMD kernel (decode_mla.hip)
+  if (a.T * a.tile_rows == 128) {
+    // 128-row tiles (all 128 heads, or T tokens x 128 / T heads): the one-wave-per-SIMD kernel
+    // (decode_mla.hip)
     const hipError_t e = launch_decode_mla128(a, st);
     if (e != hipSuccess || a.num_splits == 1 || a.stats_only) return e;
     return launch_decode_combine(a, DV, st);

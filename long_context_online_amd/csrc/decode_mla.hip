@@ -8,8 +8,10 @@
 //
 // MI355X design (the one-wave-per-SIMD layout; decode_latent.hip keeps the 16-heads-per-wave one
 // for 64-head tiles):
-//   * one workgroup = (sequence, split), 4 waves, one per SIMD, each with the full 512-register
-//     file; wave w owns heads 32 w .. 32 w + 31, so every operand fragment read from LDS feeds a
+//   * one workgroup = (sequence, row tile, split), 4 waves, one per SIMD, each with the full
+//     512-register file; wave w owns rows 32 w .. 32 w + 31 of the 128-row tile (the 128 heads, or
+//     with T query tokens per sequence T x 128 / T (token, head) pairs, token-major, each token
+//     seeing keys up to seq_len - T + t), so every operand fragment read from LDS feeds a
 //     32-wide MFMA (v_mfma_f32_32x32x16_bf16): 32 flops per LDS byte, twice what 16 heads per wave
 //     give, which is what bounds the latent decode on this chip (LDS, not MFMA or HBM);
 //   * S^T = K q^T: K rows (A operand) from LDS, the wave's 32 heads of q in 144 VGPRs (B operand);
@@ -69,8 +71,13 @@ __global__ __launch_bounds__(NT, 1) void decode_mla_kernel(DecodeArgs a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int split = blockIdx.x % a.num_splits;
-  const int b = blockIdx.x / a.num_splits;
+  // workgroup -> (sequence, row tile, split); the n_rt row tiles of one (sequence, split) are 8
+  // apart in launch order, so they land on the same XCD and share its L2 copy of the latent blocks
+  const int rt = (blockIdx.x >> 3) % a.n_rt;
+  const int ps = (blockIdx.x >> 3) / a.n_rt * 8 + (blockIdx.x & 7);
+  const int split = ps % a.num_splits;
+  const int b = ps / a.num_splits;
+  if (b >= a.B) return;
   const int cap = a.max_pages * PAGE;
   const int L = min(a.seq_lens[b], cap);
   const int J = (L + BK - 1) / BK;
@@ -78,7 +85,11 @@ __global__ __launch_bounds__(NT, 1) void decode_mla_kernel(DecodeArgs a) {
   const int j0 = split * chunk;
   const int j1 = min(J, j0 + chunk);
   const int npg = (L + PAGE - 1) / PAGE;
-  const int h = wave * HPW + l32;  // head of this lane's score / output column
+  const int row = wave * HPW + l32;                            // this lane's score / output column
+  const int tok = row / a.tile_rows;                           // its query token
+  const int h = rt * a.tile_rows + (row - tok * a.tile_rows);  // and q head
+  const int64_t qrow = ((int64_t)b * a.T + tok) * a.Hq + h;    // row of q (and of o, lse)
+  const int lim = L - a.T + tok;                               // the last key this row sees
 
   float thr = a.thr_raw;
   if (a.thr_mode == 1) {
@@ -88,7 +99,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mla_kernel(DecodeArgs a) {
 
   // q fragments (B operand of S^T = K q^T): lane holds dims 16 kk + 8 hi .. +7 of head h
   bf16x8 qf[KS];
-  const __bf16 *qp = (const __bf16 *)a.q + ((int64_t)b * a.Hq + h) * DQK;
+  const __bf16 *qp = (const __bf16 *)a.q + qrow * DQK;
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) qf[kk] = *(const bf16x8 *)(qp + kk * 16 + hi * 8);
   // consume the q loads here, so their waits are not placed inside the block loop
@@ -134,7 +145,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mla_kernel(DecodeArgs a) {
   float m_seen, m_dec, l_part, l_part2;
   f32x16 o_acc[MTV];
   unsigned live_cnt, skip_cnt;
-  const int mask_row = b * a.nkb;  // one kv head, one row tile
+  const int mask_row = (b * a.n_rt + rt) * a.nkb;  // one kv head
 
   // Pass loop: one pass over the split's blocks.  The accumulation takes probabilities relative to
   // the reference m_ref, set by the first kept block with a finite max; while every block max
@@ -204,12 +215,12 @@ __global__ __launch_bounds__(NT, 1) void decode_mla_kernel(DecodeArgs a) {
                                                           0, 0);
         if ((kk & 1) == 1) __builtin_amdgcn_sched_barrier(0);
       }
-      if (key0 + BK > L) {
+      if (key0 + BK > L - a.T + 1) {   // keys past a row's last visible key (or the sequence end)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (key0 + mt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) >= L) s[mt][r] = kNegInf;
+            if (key0 + mt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) > lim) s[mt][r] = kNegInf;
       }
 
       // ---- block row max, vote, critical value ----
@@ -342,7 +353,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mla_kernel(DecodeArgs a) {
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? m_ref * a.scale + __logf(l_tot) : kNegInf;
   if (a.num_splits == 1) {
-    const int64_t ob = ((int64_t)b * a.Hq + h) * DV + 4 * hi;
+    const int64_t ob = qrow * DV + 4 * hi;
 #pragma unroll
     for (int mv = 0; mv < MTV; ++mv)
 #pragma unroll
@@ -360,9 +371,9 @@ __global__ __launch_bounds__(NT, 1) void decode_mla_kernel(DecodeArgs a) {
           *(u32x2 *)((__bf16 *)a.o + oi) = w;
         }
       }
-    if (a.lse && hi == 0) a.lse[(int64_t)b * a.Hq + h] = lse;
+    if (a.lse && hi == 0) a.lse[qrow] = lse;
   } else {
-    const int64_t pb = ((int64_t)b * a.Hq + h) * a.num_splits + split;
+    const int64_t pb = qrow * a.num_splits + split;
     float *wo = a.ws_o + pb * DV + 4 * hi;
 #pragma unroll
     for (int mv = 0; mv < MTV; ++mv)
@@ -377,11 +388,12 @@ __global__ __launch_bounds__(NT, 1) void decode_mla_kernel(DecodeArgs a) {
   }
 }
 
-// 128 q heads on one latent head, 576/512 dims, page 16, block 64, all heads in one tile.
+// 128 q heads on one latent head, 576/512 dims, page 16, block 64, 128-row tiles (all heads, or T tokens x
+// 128 / T heads).
 hipError_t launch_decode_mla128(const DecodeArgs &a, hipStream_t st) {
-  if (a.Hq != 128 || a.Hkv != 1 || a.page != PAGE || a.block_k != BK || a.tile_rows != 128)
+  if (a.Hq != 128 || a.Hkv != 1 || a.page != PAGE || a.block_k != BK || a.T * a.tile_rows != 128)
     return hipErrorNotSupported;
-  const int grid = a.B * a.num_splits;
+  const int grid = (a.B * a.num_splits + 7) / 8 * 8 * a.n_rt;
   if (a.stats_only)
     hipLaunchKernelGGL((decode_mla_kernel<false, true>), dim3(grid), dim3(NT), 0, st, a);
   else if (a.out_f32)

@@ -144,7 +144,7 @@ DECODE_BAD = [
     ({"v_cache": None, "num_kv_heads": 1, "num_q_heads": 128, "head_dim_qk": 576, "head_dim_v": 512,
       "tile_rows": 32, "num_q_tokens": 3}, 2),
     ({"v_cache": None, "num_kv_heads": 1, "num_q_heads": 128, "head_dim_qk": 576, "head_dim_v": 512,
-      "tile_rows": 64, "num_q_tokens": 2}, 2),
+      "tile_rows": 16, "num_q_tokens": 2}, 2),
     # threshold mode NONE (no decisions) takes no decision diagnostics, whatever `a` holds
     ({"thr": (2, 0, 0.0, 5.0), "skip_mask": FAKE}, 1), ({"thr": (2, 0, 0.0, 5.0), "crit": FAKE}, 1),
     ({"thr": (2, 0, 0.0, float("nan")), "stats_only": 1}, 1),

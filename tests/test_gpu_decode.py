@@ -368,15 +368,17 @@ def test_multi_token_one_token_equals_single_token_layout():
 
 @pytest.mark.parametrize("T,splits", [(2, 1), (2, 3), (4, 1), (4, 5)])
 @pytest.mark.parametrize("a", [0.0, 4.0])
-def test_multi_token_latent_decode(T, splits, a):
+@pytest.mark.parametrize("rows", [64, 128])
+def test_multi_token_latent_decode(T, splits, a, rows):
     """T query tokens per sequence on the latent cache (128 heads on one 576-channel latent head, V =
-    the first 512 channels): tiles of 64 rows = T tokens x 64 / T heads, each token seeing keys up to
-    seq_len - T + t; ragged lengths including sequences no longer than T, NaN-poisoned spare pages."""
+    the first 512 channels): tiles of 64 or 128 rows = T tokens x rows / T heads (the 64-row and the
+    128-row kernels), each token seeing keys up to seq_len - T + t; ragged lengths including
+    sequences no longer than T, NaN-poisoned spare pages."""
     m = _lib()
     lens = [700, 64, T + 1, 333, T]
     d = synth.decode_inputs(batch=len(lens), hq=128, hkv=1, ctx=None, d=576, dv=512, seq_lens=lens, seed=90 + T,
                             device="cuda", latent=True, num_q_tokens=T)
-    tr = 64 // T
+    tr = rows // T
     res = _run(m, d, splits=splits, a=a, tile_rows=tr)
     rep = _compare(d, res, splits=splits, a=a, tile_rows=tr)
     print(f"T={T} S={splits} a={a}: {rep}")
@@ -384,16 +386,17 @@ def test_multi_token_latent_decode(T, splits, a):
         assert rep.skipped == 0
 
 
-@pytest.mark.parametrize("T", [2, 4])
-def test_multi_token_latent_decode_full_size_at_benchmark_threshold(T):
+@pytest.mark.parametrize("T,rows", [(2, 128), (4, 128), (2, 64)])
+def test_multi_token_latent_decode_full_size_at_benchmark_threshold(T, rows):
     """The benchmarked multi-token latent launch: batch 64, 128 heads on one latent head, context
-    32768, the last T positions of each sequence as queries, 64-row tiles (T tokens x 64 / T heads),
-    8 splits, bf16 output, lambda calibrated for 73 % as the benchmark does; 20 seeded tiles against
-    the oracle, every tile's mask against its critical values."""
+    32768, the last T positions of each sequence as queries, 128-row tiles (T tokens x 128 / T heads;
+    the benchmark's choice) or 64-row tiles, 8 splits, bf16 output, lambda calibrated for 73 % as the
+    benchmark does; 20 seeded tiles against the oracle, every tile's mask against its critical
+    values."""
     m = _lib()
     d = synth.decode_inputs(batch=64, hq=128, hkv=1, ctx=32768, d=576, dv=512, seed=synth.config_seed(5, T),
                             device="cuda", latent=True, num_q_tokens=T)
-    tr = 64 // T
+    tr = rows // T
     lam = _calibrated_lambda(m, d, splits=8, target=0.73, tile_rows=tr)
     res = _run(m, d, splits=8, lam=lam, tile_rows=tr, out_dtype=torch.bfloat16)
     sp = _check_whole_mask(res, oracle.ln_threshold(lam=lam), 0.73)
