@@ -48,7 +48,7 @@ M_B, M_HQ, M_D, M_DV, M_CTX, M_TARGETS = 64, 128, 576, 512, 32768, (0.5, 0.73)
 # 8 splits: 512 workgroups of 64 blocks; with 16 the per-split first blocks (always kept) cap the
 # sparsity at 65 % even at lambda = 1, and the partials to merge double (see mla_decode.splits_sweep)
 M_SPLITS = 8
-DEC_KERNEL = {False: "decode_gqa_kernel<false>", True: "decode_mla_kernel<false, false>"}
+DEC_KERNEL = {False: "decode_gqa_kernel<false, true>", True: "decode_mla_kernel<false, false>"}
 MLA_WORKLOAD = ("latent decode, DeepSeek-shaped: batch 64, 128 q heads on one latent head, 576-dim scores, "
                 "V = first 512 channels, context 32768, 16-token pages, 64-token blocks, 8 splits, 128-head "
                 "tiles, bf16")
