@@ -118,7 +118,7 @@ __global__ __launch_bounds__(TR / HPW * 64, 1) void decode_latent_kernel(DecodeA
       if (row >= BK) row = 0;
       const int pid = __shfl(tabv, row >> 4);
       if (ins < INS)
-        direct_load16(kc + (int64_t)pid * page_stride + (row & 15) * DQK + c * 8, lds_addr(sK[buf] + ins * 1024));
+        direct_load16_nt(kc + (int64_t)pid * page_stride + (row & 15) * DQK + c * 8, lds_addr(sK[buf] + ins * 1024));
     }
   };
   // transpose-read base for the V^T operand: source lane j = 4k + q of 16-lane group G points at
