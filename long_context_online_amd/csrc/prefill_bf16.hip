@@ -21,8 +21,8 @@
 //     source lane 4k + i/4's 8-byte read), so no transpose pass is needed anywhere;
 //   * K and V go global -> LDS directly (buffer_load ... lds, no registers) into double-buffered
 //     LDS; the block loop is software-pipelined by one block: iteration t computes QK^T and the
-//     vote of block t, then ONE barrier publishes the votes and makes K_{t+1} (prefetched at the
-//     top of the iteration) and V_{t-1} visible; then the P.V product of block t - 1 runs from its
+//     vote of block t, then ONE barrier publishes the votes and makes K_{t+1} (its loads spread
+//     over block t's score MFMAs) and V_{t-1} visible; then the P.V product of block t - 1 runs from its
 //     probabilities packed in registers, and only if block t was kept by a tile of the workgroup
 //     are its probabilities formed and V_t loaded, so a skipped block costs QK^T, the row max and
 //     the vote and nothing else;
@@ -162,10 +162,12 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   // (row p / CP, chunk p % CP); pad chunks load chunk 0 of their row.  Contiguous K/V go through a
   // buffer resource per block whose extent ends at the last key, so keys past the end read as zero
   // (and are masked) without any clamping, and a load costs a few 24-bit integer ops for its offset.
-  auto load_tile = [&](const __bf16 *base, int64_t stride, int j, unsigned char *dst, auto CPc, auto CHc,
-                       auto INSc) {
+  auto load_tile_part = [&](const __bf16 *base, int64_t stride, int j, unsigned char *dst, auto CPc, auto CHc,
+                            auto INSc, int i) {
     constexpr int CP = decltype(CPc)::value, CH = decltype(CHc)::value, INS = decltype(INSc)::value;
     const int key0 = j * BC;
+    const int ins = i * NW + wave;
+    if (ins >= INS) return;
     if constexpr (!PAGED) {
       static_assert(INS * 64 == BC * CP, "every position of a tile is one row chunk");
       const uint32_t row_b = (uint32_t)stride * 2u;
@@ -175,71 +177,60 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       rsrc[1] = (uint32_t)(addr >> 32) & 0xffffu;  // stride 0
       rsrc[2] = (uint32_t)min(Lk - key0, BC) * row_b;
       rsrc[3] = 0x00020000u;
-      const uint32_t lds0 = lds_addr(dst);
-#pragma unroll
-      for (int i = 0; i < (INS + NW - 1) / NW; ++i) {
-        const int ins = i * NW + wave;
-        if (ins < INS) {
-          const int p = ins * 64 + lane;
-          const int row = p / CP;
-          int c = p - row * CP;
-          if (c >= CH) c = 0;
-          buffer_load16_lds(rsrc, __mul24(row, row_b) + c * 16, lds0 + ins * 1024);
-        }
-      }
+      const int p = ins * 64 + lane;
+      const int row = p / CP;
+      int c = p - row * CP;
+      if (c >= CH) c = 0;
+      buffer_load16_lds(rsrc, __mul24(row, row_b) + c * 16, lds_addr(dst) + ins * 1024);
       return;
     }
     // the lane index through an empty asm: the per-lane offsets below are then recomputed at every
     // load instead of being kept in registers across the block loop (where they spilled)
     int ln = lane;
     asm volatile("" : "+v"(ln));
-#pragma unroll
-    for (int i = 0; i < (INS + NW - 1) / NW; ++i) {
-      const int ins = i * NW + wave;
-      if (ins < INS) {
-        const int p = ins * 64 + ln;
-        int row = p / CP, c = p - (p / CP) * CP;
-        if (c >= CH) c = 0;
-        if (row >= BC) row = 0;
-        const int key = min(key0 + paged_key_of_row(row), Lk - 1);
-        // K row of the key's page (16 tokens per page), the page id from the block's staged ids
-        const int pid = sIds[j & 3][(key >> 4) - (key0 >> 4)];
-        const __bf16 *src = base + ((int64_t)pid * a.Hkv + g) * (16 * D) + (key & 15) * D + c * 8;
-        direct_load16(src, lds_addr(dst + ins * 1024));
-      }
-    }
+    const int p = ins * 64 + ln;
+    int row = p / CP, c = p - (p / CP) * CP;
+    if (c >= CH) c = 0;
+    if (row >= BC) row = 0;
+    const int key = min(key0 + paged_key_of_row(row), Lk - 1);
+    // K row of the key's page (16 tokens per page), the page id from the block's staged ids
+    const int pid = sIds[j & 3][(key >> 4) - (key0 >> 4)];
+    const __bf16 *src = base + ((int64_t)pid * a.Hkv + g) * (16 * D) + (key & 15) * D + c * 8;
+    direct_load16(src, lds_addr(dst + ins * 1024));
   };
-  auto load_k = [&](int j, int buf) {
-    load_tile(kp, a.ks[2], j, sK[buf], std::integral_constant<int, KCP>{}, std::integral_constant<int, KCH>{},
-              std::integral_constant<int, KINS>{});
+  constexpr int NPK = (KINS + NW - 1) / NW;  // direct loads per wave per K tile
+  auto load_k_part = [&](int j, int buf, int i) {
+    load_tile_part(kp, a.ks[2], j, sK[buf], std::integral_constant<int, KCP>{}, std::integral_constant<int, KCH>{},
+                   std::integral_constant<int, KINS>{}, i);
   };
   // Paged V^T tile: row dv holds the block's 128 keys, 16 bytes (8 keys, half a page) per position;
   // row stride VTROW = 272 bytes (16 positions + 1 pad).  Keys past the sequence's last page read
   // that page (their values are zeroed before use).
   constexpr int VTCP = 17, VTROW = VTCP * 16, VTINS = D * VTCP / 64;
   static_assert(!PAGED || (D == 128 && BC == 128 && VTINS * 1024 <= VBUF), "paged tiles are 128 x 128");
-  auto load_v = [&](int j, int buf) {
+  constexpr int NPV = ((PAGED ? VTINS : VINS) + NW - 1) / NW;  // direct loads per wave per V tile
+  auto load_v_part = [&](int j, int buf, int i) {
     if constexpr (PAGED) {
-      int ln = lane;   // recomputed offsets, as for K
-      asm volatile("" : "+v"(ln));
-#pragma unroll
-      for (int i = 0; i < (VTINS + NW - 1) / NW; ++i) {
-        const int ins = i * NW + wave;
-        if (ins < VTINS) {
-          const int p = ins * 64 + ln;
-          const int dv = p / VTCP;
-          int c = p - dv * VTCP;
-          if (c >= 16) c = 0;
-          const int pid = sIds[j & 3][c >> 1];
-          const __bf16 *src = vp + (((int64_t)pid * a.Hkv + g) * D + dv) * 16 + (c & 1) * 8;
-          direct_load16(src, lds_addr(sV[buf] + ins * 1024));
-        }
+      const int ins = i * NW + wave;
+      if (ins < VTINS) {
+        int ln = lane;   // recomputed offsets, as for K
+        asm volatile("" : "+v"(ln));
+        const int p = ins * 64 + ln;
+        const int dv = p / VTCP;
+        int c = p - dv * VTCP;
+        if (c >= 16) c = 0;
+        const int pid = sIds[j & 3][c >> 1];
+        const __bf16 *src = vp + (((int64_t)pid * a.Hkv + g) * D + dv) * 16 + (c & 1) * 8;
+        direct_load16(src, lds_addr(sV[buf] + ins * 1024));
       }
     } else {
-      load_tile(vp, a.vs[2], j, sV[buf], std::integral_constant<int, VCP>{}, std::integral_constant<int, VCH>{},
-                std::integral_constant<int, VINS>{});
+      load_tile_part(vp, a.vs[2], j, sV[buf], std::integral_constant<int, VCP>{}, std::integral_constant<int, VCH>{},
+                     std::integral_constant<int, VINS>{}, i);
     }
   };
+  // The K tile of block t + 1 is loaded during block t's score MFMAs, spread evenly over them: a
+  // wave that issues a tile's loads at once sits in the stalled issue until the memory pipeline
+  // takes them, and issues no MFMA meanwhile.
   // Paged: wave 0 stages the ids of block j's 8 pages (clamped to the sequence's last page) into ring
   // slot j & 3, 4 bytes per lane.  Slot j & 3 is refilled (for block j + 4, at the top of iteration
   // j + 2) only after the barrier of iteration j + 1, which every wave reaches after its last read of
@@ -272,8 +263,8 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   const bool tile_leader = wit == 0 && lane == 0;
 
   // ---- block loop, software-pipelined by one block.  Iteration t computes QK^T, row max and vote
-  // of block t, then one barrier publishes the votes and makes K_{t+1} (prefetched at the top of
-  // the iteration) and V_{t-1} visible; then the P.V product of block t - 1 (its probabilities
+  // of block t, then one barrier publishes the votes and makes K_{t+1} (loaded during block t's
+  // score MFMAs) and V_{t-1} visible; then the P.V product of block t - 1 (its probabilities
   // packed in registers), and for a kept block t its probabilities and the direct loads of V_t.
   // So V is staged only for blocks that a tile of the workgroup kept. ----
   f32x16 s[MT];            // scores of block t
@@ -285,7 +276,10 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-  if (J > 0) load_k(0, 0);
+  if (J > 0) {
+#pragma unroll
+    for (int i = 0; i < NPK; ++i) load_k_part(0, 0, i);
+  }
   // a wait the compiler sees (not inline asm), on every path into the loop: without it the compiler
   // takes the Q fragments as possibly in flight at the loop head and waits for vmcnt(0), i.e. for the
   // K prefetch just issued, before the first QK^T product of every block
@@ -294,52 +288,46 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   for (int t = 0; t <= J; ++t) {
     const int buf = t & 1;
     if (t + 2 < J) stage_ids(t + 2);
-    if (t + 1 < J) load_k(t + 1, buf ^ 1);
+    const bool k_next = t + 1 < J;
     float mx = kNegInf;
     if (t < J) {
       if ((t % chunk) == 0) m_dec = kNegInf;
 
-      // ---- S^T = K_t Q^T ----
+      // ---- S^T = K_t Q^T one 32-key m-tile at a time; a finished tile is masked (blocks that need
+      // it) and folded into the row max while the next tile's MFMAs run ----
       const unsigned char *kb = sK[buf] + l32 * KROW + hi * 16;
-      // K fragments are read one k-step ahead of the MFMAs that consume them, so LDS latency
-      // overlaps the previous k-step's MFMAs instead of stalling every MFMA
-      bf16x8 kf[2][MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) kf[0][mt] = *(const bf16x8 *)(kb + mt * 32 * KROW);
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        if (kk + 1 < KS) {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            kf[(kk + 1) & 1][mt] = *(const bf16x8 *)(kb + mt * 32 * KROW + (kk + 1) * 32);
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk & 1][mt], qf[kk], kk == 0 ? f32x16{} : s[mt], 0,
-                                                          0, 0);
-        __builtin_amdgcn_sched_barrier(0);  // keep the next k-step's reads ahead of these MFMAs
-      }
-
-      // ---- causal / tail mask (only blocks that need it) ----
       const int key0 = t * BC;
       const bool need_mask = (key0 + BC > Lk) || (a.causal && key0 + BC - 1 > r0 + off);
-      if (need_mask) {
-        const int lim = a.causal ? min(my_row + off, Lk - 1) : Lk - 1;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+      const int lim = a.causal ? min(my_row + off, Lk - 1) : Lk - 1;
+      auto fold = [&](int mt) {
+        if (need_mask) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kr = mt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);   // K tile row
             const int key = key0 + (PAGED ? paged_key_of_row(kr) : kr);
             if (key > lim) s[mt][r] = kNegInf;
           }
-      }
-
-      // ---- block row max, vote, critical value ----
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+      };
+      constexpr int NQ = MT * KS;
+      // K fragments two MFMAs ahead of their use, in a ring of three
+      bf16x8 kf[3];
+      kf[0] = *(const bf16x8 *)(kb);
+      kf[1] = *(const bf16x8 *)(kb + (1 / KS) * 32 * KROW + (1 % KS) * 32);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int mt = q / KS, kk = q % KS;
+        if (q + 2 < NQ) kf[(q + 2) % 3] = *(const bf16x8 *)(kb + ((q + 2) / KS) * 32 * KROW + ((q + 2) % KS) * 32);
+#pragma unroll
+        for (int i = 0; i < NPK; ++i)
+          if (k_next && i * NQ / NPK == q) load_k_part(t + 1, buf ^ 1, i);
+        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[q % 3], qf[kk], kk == 0 ? f32x16{} : s[mt], 0, 0, 0);
+        if (mt > 0 && kk == 1) fold(mt - 1);
+        if (q & 1) __builtin_amdgcn_sched_barrier(0);
+      }
+      fold(MT - 1);
       mx = max_xor32(mx);
       if (!row_ok) mx = kNegInf;
       if (DEC) {
@@ -446,7 +434,10 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     }
     // V_t only for a block that a tile of the workgroup kept, unless every live block's V is staged
     // (the buffer held V_{t-2}, whose P.V every wave finished before this iteration's barrier)
-    if (!STATS && (keep_any || a.v_all)) load_v(t, buf);
+    if (!STATS && (keep_any || a.v_all)) {
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) load_v_part(t, buf, i);
+    }
     keep_pend = keep != 0;
   }
 
