@@ -285,13 +285,18 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   // K prefetch just issued, before the first QK^T product of every block
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
+  int to_split = 0;  // blocks left in the current split
   for (int t = 0; t <= J; ++t) {
     const int buf = t & 1;
     if (t + 2 < J) stage_ids(t + 2);
     const bool k_next = t + 1 < J;
     float mx = kNegInf;
     if (t < J) {
-      if ((t % chunk) == 0) m_dec = kNegInf;
+      if (to_split == 0) {  // a split starts at this block
+        m_dec = kNegInf;
+        to_split = chunk;
+      }
+      --to_split;
 
       // ---- S^T = K_t Q^T one 32-key m-tile at a time; a finished tile is masked (blocks that need
       // it) and folded into the row max while the next tile's MFMAs run ----
