@@ -67,6 +67,22 @@ __device__ __forceinline__ void stage_tile(const __bf16 *base, int64_t stride, i
   }
 }
 
+// Instruction i of stage_tile's loop only (ins = wave + i * nw), if it exists.
+template <int ROWB>
+__device__ __forceinline__ void stage_tile_part(const __bf16 *base, int64_t stride, int row0, int nrows,
+                                                unsigned char *dst, int wave, int nw, int lane, int i) {
+  constexpr int CPR = ROWB / 16;
+  const int ins = wave + i * nw;
+  if (ins < tile_ins<ROWB>()) {
+    const int p = ins * 64 + lane;
+    const int row = p / CPR;
+    int c = p - row * CPR;
+    if (c >= 16) c = 0;
+    const int src = min(row0 + row, nrows - 1);
+    direct_load16(base + (int64_t)src * stride + c * 8, lds_addr(dst + ins * 1024));
+  }
+}
+
 // Transpose read of one k-step (16 rows of the tile) for an A operand X^T, X row-major in LDS:
 // output lane l holds column 32 mv + l % 32 of X and the 8 rows of its lane half in the order of the
 // B operand taken from accumulator registers 8 (ks % 2) ... + 7 of m-tile ks / 2.
@@ -211,6 +227,11 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
     stage_tile<ROW_DQ_K>(kp, a.ks[2], j * BB, a.Lk, sK[buf], wave, NW, lane);
     stage_tile<ROW_DQ_V>(vp, a.vs[2], j * BB, a.Lk, sV[buf], wave, NW, lane);
   };
+  constexpr int NSPQ = (tile_ins<ROW_DQ_K>() + NW - 1) / NW;   // >= the V tile's count
+  auto stage_part = [&](int j, int buf, int i) {
+    stage_tile_part<ROW_DQ_K>(kp, a.ks[2], j * BB, a.Lk, sK[buf], wave, NW, lane, i);
+    stage_tile_part<ROW_DQ_V>(vp, a.vs[2], j * BB, a.Lk, sV[buf], wave, NW, lane, i);
+  };
 
   const int tr_off = tr_lane_offset<ROW_DQ_K>(lane);
   f32x16 dq_acc[MV];
@@ -226,7 +247,7 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
     const bool keep_n = jn < J && mine(jn);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block jc has landed in LDS
     __syncthreads();                                   // ... for every wave; buffer buf ^ 1 is free
-    if (jn < J) stage(jn, buf ^ 1);
+    if (jn < J && !keep_c) stage(jn, buf ^ 1);   // no products to spread the loads over
     if (keep_c) {
       const unsigned char *kb = sK[buf] + l32 * ROW_DQ_K + hi * 16;
       const unsigned char *vb = sV[buf] + l32 * ROW_DQ_V + hi * 16;
@@ -236,6 +257,11 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
       const int lim = a.causal ? min(my_row + off, a.Lk - 1) : a.Lk - 1;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
+        // the next block's staging, spread over the first m-tiles (issued at once, the loads held each
+        // wave in the stalled issue)
+#pragma unroll
+        for (int i = 0; i < NSPQ; ++i)
+          if (jn < J && i * (MT - 1) / NSPQ == mt) stage_part(jn, buf ^ 1, i);
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
@@ -376,6 +402,23 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
   // 2-3: D, 64 rows each; rows past the end read the last row), all in flight while the previous
   // pair is processed.
   static_assert(BB == 128, "four 64-row instructions cover LSE and D of a tile");
+  constexpr int NSP = (tile_ins<ROWB>() + NW - 1) / NW;   // instructions per wave per tile
+  // part i < NSP: instruction i of the Q and the dO tile; part NSP: the LSE and D values
+  auto stage_part = [&](int p, int buf, int i) {
+    const int h = p / a.nqt, t = p - (p / a.nqt) * a.nqt;
+    const int hq = g * a.G + h;
+    if (i < NSP) {
+      stage_tile_part<ROWB>((const __bf16 *)a.q + b * a.qs[0] + hq * a.qs[1], a.qs[2], t * BB, a.Lq, sQ[buf], wave,
+                            NW, lane, i);
+      stage_tile_part<ROWB>((const __bf16 *)a.dout + b * a.dos[0] + hq * a.dos[1], a.dos[2], t * BB, a.Lq, sO[buf],
+                            wave, NW, lane, i);
+    } else if (wave < 4) {
+      const int row = min(t * BB + (wave & 1) * 64 + lane, a.Lq - 1);
+      const int64_t idx = ((int64_t)b * a.Hq + hq) * a.Lq + row;
+      const float *src = (wave < 2 ? (const float *)a.lse : (const float *)a.dvec) + idx;
+      direct_load4(src, lds_addr((wave < 2 ? sL[buf] : sD[buf]) + (wave & 1) * 64));
+    }
+  };
   auto stage = [&](int p, int buf) {
     const int h = p / a.nqt, t = p - (p / a.nqt) * a.nqt;
     const int hq = g * a.G + h;
@@ -429,7 +472,6 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
     const int pn = next(pc + 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // pair pc's tiles have landed in LDS
     __syncthreads();                                   // ... for every wave; buffer buf ^ 1 is free
-    if (pn < npairs) stage(pn, buf ^ 1);
     {
       const int t = pc - (pc / a.nqt) * a.nqt;
       const int row0 = t * BB;
@@ -461,6 +503,11 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
       sdp(0);
 #pragma unroll
       for (int ks = 0; ks < NSL / 2; ++ks) {
+        // the next pair's staging, parts spread over the first k-steps (issued at once, the loads held
+        // each wave in the stalled issue)
+#pragma unroll
+        for (int i = 0; i <= NSP; ++i)
+          if (pn < npairs && i * (NSL / 2 - 1) / (NSP + 1) == ks) stage_part(pn, buf ^ 1, i);
         if (ks + 1 < NSL / 2) sdp(ks + 1);
         const int u = ks & 1;
         bf16x8 pf, dsf;
