@@ -242,6 +242,24 @@ def test_latent_mla_ragged(tile_rows, splits, a):
         assert rep.skipped == 0
 
 
+@pytest.mark.parametrize("tile_rows", [128, 64])
+@pytest.mark.parametrize("splits,a", [(1, 8.0), (2, 0.0)])
+def test_latent_mla_long_splits(tile_rows, splits, a):
+    """Latent decode with splits of more than 128 blocks (one sequence of 20000 tokens, 313 blocks,
+    another of 9000): the 128-head kernel reads its page ids a 64-block window at a time, so these
+    splits run through several window refills; every row against the oracle."""
+    m = _lib()
+    d = synth.decode_inputs(batch=2, hq=128, hkv=1, ctx=None, d=576, dv=512, seq_lens=[20000, 9000], seed=13,
+                            device="cuda", latent=True)
+    res = _run(m, d, splits=splits, a=a, tile_rows=tile_rows)
+    rep = _compare(d, res, splits=splits, a=a, tile_rows=tile_rows)
+    print(f"tile_rows={tile_rows} S={splits} a={a}: {rep}")
+    if a == 0.0:
+        assert rep.skipped == 0
+    else:
+        assert rep.skipped > 0
+
+
 def _mla_full_size():
     return synth.decode_inputs(batch=64, hq=128, hkv=1, ctx=32768, d=576, dv=512, seed=synth.config_seed(5),
                                device="cuda", latent=True)
