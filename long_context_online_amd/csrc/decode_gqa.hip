@@ -14,8 +14,8 @@
 //   * the tile's query columns are (token, head) pairs, token-major: with T query tokens per
 //     sequence (the last T positions) column t * tile_rows + i is token t of the tile's head i, and
 //     its keys past seq_len - T + t are masked like keys past the sequence end;
-//   * K-first batch of NB blocks: each wave loads its NB K pages straight into MFMA operand
-//     registers (16 bytes per lane per k-step), computes S^T = K q^T with
+//   * K-first batch of NB blocks: each wave stages its NB K pages in LDS (whole rows per load, a
+//     swizzled layout: see load_k), computes S^T = K q^T with
 //     v_mfma_f32_16x16x32_bf16 (the tile's <= 16 q heads are the N columns), and publishes its
 //     per-page row maxima in LDS; after one barrier every thread derives the block maxima and the
 //     sequential decisions of the whole batch (the same values in every wave, so the branch is
