@@ -317,6 +317,9 @@ def gather_pages(k_cache, v_cache_t, block_table, b, g, seq_len, page_size, head
     page; None means V is the first Dv channels of K (latent attention, MLA).
     """
     n_pages = -(-seq_len // page_size)
+    if n_pages == 0:  # an empty sequence (a reading: no keys, so nothing to attend to)
+        dv = head_dim_v if head_dim_v is not None else (v_cache_t.shape[2] if v_cache_t is not None else k_cache.shape[-1])
+        return np.zeros((0, k_cache.shape[-1])), np.zeros((0, dv))
     ks, vs = [], []
     for p in range(n_pages):
         pid = int(block_table[b][p])
@@ -392,7 +395,10 @@ def decode(q, k_cache, v_cache_t, block_table, seq_lens, *, page_size, block_k, 
     mask = np.full((B, Hkv, n_rt, nkb), NOT_LIVE, dtype=np.int8)
     crit = np.full((B, Hkv, n_rt, nkb), np.nan)
     for b in range(B):
-        ln_lam = ln_threshold(lam=lam, a=a, L=int(seq_lens[b])) if lam is None else ln_threshold(lam=lam)
+        if lam is None and int(seq_lens[b]) == 0:
+            ln_lam = NEG_INF  # a / L is undefined for an empty sequence, which has no block to decide on
+        else:
+            ln_lam = ln_threshold(lam=lam, a=a, L=int(seq_lens[b])) if lam is None else ln_threshold(lam=lam)
         for g in range(Hkv):
             for rt in range(n_rt):
                 r = decode_tile(q4, k_cache, v_cache_t, block_table, seq_lens, b, g, rt,

@@ -78,7 +78,10 @@ def _compare(d, res, *, splits, lam=None, a=None, tiles=None, tile_rows=0, out_b
         if (b, g) not in cache:
             cache = {(b, g): _tile_inputs(d, b, g)}
         qh, kc, vc, bt, sl1 = cache[(b, g)]
-        ln_lam = oracle.ln_threshold(lam=lam) if lam is not None else oracle.ln_threshold(a=a, L=int(sl[b]))
+        if lam is not None:
+            ln_lam = oracle.ln_threshold(lam=lam)
+        else:  # an empty sequence has no block to decide on
+            ln_lam = -math.inf if int(sl[b]) == 0 else oracle.ln_threshold(a=a, L=int(sl[b]))
         kw = dict(page_size=d.page_size, block_k=64, num_splits=splits, ln_lam=ln_lam, tile_rows=tr,
                   head_dim_v=d.head_dim_v)
         ref = oracle.decode_tile(qh, kc, vc, bt, sl1, 0, 0, rt, **kw)
@@ -112,6 +115,28 @@ def test_gqa_paged_ragged(splits, a):
     assert int(cnt[0]) == int((mh != 2).sum()) and int(cnt[1]) == int((mh == 1).sum())
     if a == 0.0:
         assert rep.skipped == 0
+
+
+@pytest.mark.parametrize("latent", [False, True])
+@pytest.mark.parametrize("splits,a", [(1, 2.0), (3, 2.0), (3, 0.0)])
+def test_decode_empty_sequence(latent, splits, a):
+    """A sequence of length 0 between others (its table row points at valid pages, none is read): o = 0,
+    lse = -inf, no live block; the other sequences as the oracle gives them."""
+    m = _lib()
+    if latent:
+        d = synth.decode_inputs(batch=3, hq=128, hkv=1, ctx=None, d=576, dv=512, seq_lens=[300, 1, 70], seed=14,
+                                device="cuda", latent=True)
+    else:
+        d = synth.decode_inputs(batch=3, hq=32, hkv=8, ctx=None, d=128, seq_lens=[300, 1, 70], seed=14,
+                                device="cuda")
+    d.seq_lens[1] = 0
+    tr = 128 if latent else 0
+    res = _run(m, d, splits=splits, a=a, tile_rows=tr)
+    o, lse, mask, _, _ = res
+    assert torch.all(o[1] == 0).item() and torch.all(lse[1] == -math.inf).item()
+    assert torch.all(mask[1] == 2).item()
+    rep = _compare(d, res, splits=splits, a=a, tile_rows=tr)
+    print(f"latent={latent} S={splits} a={a}: {rep}")
 
 
 @pytest.mark.parametrize("tile_rows", [1, 2, 4])

@@ -426,6 +426,25 @@ def test_multi_token_decode_rows_without_keys():
             assert np.max(np.abs(r["o"][1, t, h] - softmax(logits) @ Vc[1][h // 4][:n])) < 1e-12
 
 
+def test_decode_empty_sequence():
+    """A sequence of length 0 (a reading: it has no key, so nothing to attend to) gives o = 0,
+    lse = -inf and no live block, for a fixed lambda, for a / L and at lambda = 0, and leaves the other
+    sequences exactly as they are in a batch without it."""
+    rng = np.random.default_rng(64)
+    q, kc, vc, table, lens, Kc, Vc = _random_paged(rng, lens=(23, 5, 9))
+    lens0 = lens.copy()
+    lens0[1] = 0
+    others = [0, 2]
+    for kw in (dict(lam=0.3), dict(a=2.0), dict(lam=0.0)):
+        r = oracle.decode(q, kc, vc, table, lens0, page_size=4, block_k=8, num_splits=2, scale=0.4, **kw)
+        assert np.all(r["o"][1] == 0.0) and np.all(r["lse"][1] == -np.inf)
+        assert np.all(r["mask"][1] == NOT_LIVE) and np.all(np.isnan(r["crit"][1]))
+        r2 = oracle.decode(q[others], kc, vc, table[others], lens[others], page_size=4, block_k=8, num_splits=2,
+                           scale=0.4, **kw)
+        assert np.array_equal(r["o"][others], r2["o"]) and np.array_equal(r["lse"][others], r2["lse"])
+        assert np.array_equal(r["mask"][others], r2["mask"])
+
+
 # ---------------------------------------------------------------------------------------------
 # the dense reference itself
 # ---------------------------------------------------------------------------------------------
