@@ -611,9 +611,55 @@ def percentiles(xs):
     return [round(pick(0.1), 4), round(pick(0.5), 4), round(pick(0.9), 4)]
 
 
+def stream_ceilings(torch, x):
+    """Read-only streaming ceilings from this package's own probe kernels (libblasst_ceiling.so:
+    16-byte non-temporal loads, nothing written but one word per thread) over the 4 GiB buffer x:
+    a contiguous sweep, and 4 KB pages in a seeded random order (the access pattern of a paged KV
+    cache of 16-token pages of a 128-dim bf16 head).  Best over a few grid sizes."""
+    import ctypes
+    path = os.path.join(ROOT, "long_context_online_amd", "libblasst_ceiling.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m long_context_online_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.blasst_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                               ctypes.c_void_p]
+    lib.blasst_ceiling_stream_pages.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                                ctypes.c_int, ctypes.c_void_p]
+    nbytes = x.numel() * x.element_size()
+    page = lib.blasst_ceiling_page_bytes()
+    n_pages = nbytes // page
+    gen = torch.Generator().manual_seed(11)
+    table = torch.randperm(n_pages, generator=gen).to(torch.int32).to("cuda")
+    grids = (1024, 2048, 4096)
+    out = torch.empty(max(grids) * 256, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run(fn):
+        rc = fn()
+        if rc != 0:
+            raise RuntimeError(f"streaming ceiling kernel failed: {rc}")
+
+    res = {}
+    for name, nb, call in (
+            ("read_contiguous_4gib_gbps", nbytes,
+             lambda g: lib.blasst_ceiling_stream_read(x.data_ptr(), nbytes, out.data_ptr(), g, stream)),
+            ("read_4kb_pages_random_4gib_gbps", n_pages * page,
+             lambda g: lib.blasst_ceiling_stream_pages(x.data_ptr(), table.data_ptr(), n_pages, out.data_ptr(), g,
+                                                       stream))):
+        best = 0.0
+        for g in grids:
+            run(lambda: call(g))
+            ms = timed(torch, lambda: run(lambda: call(g)), 10)
+            best = max(best, nb / (ms * 1e-3) / 1e9)
+        res[name] = round(best, 1)
+    del table, out
+    return res
+
+
 def practical_ceilings(torch):
     """Measured ceilings on this GPU, as context for the roofline fractions: a bf16 GEMM through the
-    vendor BLAS (torch.matmul, 8192^3) and a plain device-to-device copy of 4 GiB."""
+    vendor BLAS (torch.matmul, 8192^3), a plain device-to-device copy of 4 GiB, library reductions
+    over it, and this package's read-only streaming probes (contiguous and random 4 KB pages)."""
     out = {}
     n = 8192
     a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
@@ -629,14 +675,14 @@ def practical_ceilings(torch):
     ms = timed(torch, lambda: y.copy_(x), 5)
     out["copy_4gib_gbps_read_plus_write"] = round(2 * x.numel() * 2 / (ms * 1e-3) / 1e9, 1)
     del y
-    # read-only streaming (what a decode kernel mostly does): a max-reduction over the same 4 GiB,
-    # whose output is a few bytes; the best of two reductions
+    # library reductions over the same 4 GiB (output a few bytes); the best of two
     best = 0.0
     for fn in (lambda: torch.amax(x), lambda: torch.sum(x, dtype=torch.float32)):
         fn()
         ms = timed(torch, fn, 5)
         best = max(best, x.numel() * 2 / (ms * 1e-3) / 1e9)
-    out["read_4gib_gbps"] = round(best, 1)
+    out["reduction_4gib_gbps"] = round(best, 1)
+    out.update(stream_ceilings(torch, x))
     del x
     torch.cuda.empty_cache()
     return out
@@ -866,6 +912,11 @@ def main():
             torch.cuda.empty_cache()
         result["calibration"] = calibration_sweep(m, torch, synth, args.steps)
         result["ceilings"] = practical_ceilings(torch)
+        # the paged GQA decode against the read rate of its own access pattern (random 4 KB pages)
+        paged = result["ceilings"]["read_4kb_pages_random_4gib_gbps"]
+        for key in ("decode", "decode_131072"):
+            if key in result and paged > 0:
+                result[key]["frac_of_paged_read_ceiling"] = round(result[key]["hbm_gbps"] / paged, 4)
     result["config"] = config
     result["context"] = {"pages_prefill_speedup": "1.62x at 74.7% sparsity (B200/H200, pages' abstract)",
                          "pages_decode_speedup": "1.48x at 73.2% sparsity"}

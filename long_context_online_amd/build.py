@@ -1,4 +1,5 @@
-"""Builds the HIP library libblasst.so in-tree for gfx950 (hipcc cross-compiles without a GPU)."""
+"""Builds the HIP library libblasst.so in-tree for gfx950 (hipcc cross-compiles without a GPU), and
+beside it libblasst_ceiling.so, the benchmark's read-only streaming ceilings (measurement only)."""
 
 from __future__ import annotations
 
@@ -10,6 +11,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libblasst.so")
+CEILING_SRC = os.path.join(HERE, "ceiling", "stream_read.hip")
+CEILING_OUT = os.path.join(HERE, "libblasst_ceiling.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -57,6 +60,14 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, OUT)
     if verbose:
         print(f"built {OUT}")
+    tmp = CEILING_OUT + ".tmp"
+    cmd = [HIPCC, *COMMON, "-shared", "-x", "hip", CEILING_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {CEILING_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CEILING_OUT)
+    if verbose:
+        print(f"built {CEILING_OUT}")
     return OUT
 
 

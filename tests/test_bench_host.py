@@ -46,3 +46,25 @@ def test_profile_record_follows_the_source_hash(tmp_path, monkeypatch):
 def test_profile_record_missing_file(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.profiled_traffic("kern<1>") is None
+
+
+def test_ceiling_library_exports_and_rejects_bad_arguments():
+    """The streaming-ceiling probe library the benchmark loads: its three entry points exist, and
+    invalid arguments are refused before any launch (so this needs no GPU)."""
+    import ctypes
+    path = os.path.join(ROOT, "long_context_online_amd", "libblasst_ceiling.so")
+    if not os.path.exists(path):
+        from long_context_online_amd import build
+        build.build()
+    lib = ctypes.CDLL(path)
+    assert lib.blasst_ceiling_page_bytes() == 4096
+    lib.blasst_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                               ctypes.c_void_p]
+    lib.blasst_ceiling_stream_pages.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                                ctypes.c_int, ctypes.c_void_p]
+    assert lib.blasst_ceiling_stream_read(None, 1024, 16, 8, None) == -1        # no source
+    assert lib.blasst_ceiling_stream_read(16, 1000, 16, 8, None) == -1          # not whole 16-byte vectors
+    assert lib.blasst_ceiling_stream_read(24, 1024, 16, 8, None) == -1          # misaligned
+    assert lib.blasst_ceiling_stream_read(16, 1024, 16, 0, None) == -1          # empty grid
+    assert lib.blasst_ceiling_stream_pages(16, None, 4, 16, 8, None) == -1      # no table
+    assert lib.blasst_ceiling_stream_pages(16, 16, 0, 16, 8, None) == -1        # no pages
