@@ -47,7 +47,9 @@ extern "C" {
 typedef enum {
   BLASST_OK = 0,
   BLASST_ERR_INVALID_ARG = 1,   /* a pointer, size, stride or threshold is invalid */
-  BLASST_ERR_UNSUPPORTED = 2,   /* valid request, but no kernel for this head dim / block / dtype */
+  BLASST_ERR_UNSUPPORTED = 2,   /* valid request, but no kernel for this head dim / block / dtype, or a
+                                   problem whose workgroup count, context length or skip-mask size
+                                   does not fit the kernels' 32-bit indexing */
   BLASST_ERR_HIP = 3,           /* a HIP call or kernel launch failed */
   BLASST_ERR_WORKSPACE = 4      /* workspace missing or smaller than *_workspace_size() */
 } blasst_status;

@@ -134,6 +134,8 @@ blasst_status blasst_prefill_paged(const blasst_prefill_paged_params *p, void *s
       return fail(BLASST_ERR_UNSUPPORTED, "strides must be multiples of 16 bytes");
   if (!aligned16(p->q) || !aligned16(p->k_cache) || !aligned16(p->v_cache) || (p->o && !aligned16(p->o)))
     return fail(BLASST_ERR_UNSUPPORTED, "q, caches and o must be 16-byte aligned");
+  if ((double)p->max_pages_per_seq * p->page_size > 2147483647.0)
+    return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
   const double scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0 / std::sqrt((double)p->head_dim_qk);
   blasst::PrefillArgs a{};
   a.q = p->q; a.k = p->k_cache; a.v = p->v_cache; a.o = p->o; a.lse = p->lse;
@@ -318,6 +320,12 @@ static blasst_status validate_decode(const blasst_decode_params *p, bool need_pt
   if (need_ptrs && (!aligned16(p->q) || !aligned16(p->k_cache) || (p->v_cache && !aligned16(p->v_cache)) ||
                     (p->o && !aligned16(p->o))))
     return fail(BLASST_ERR_UNSUPPORTED, "q, caches and o must be 16-byte aligned");
+  // the kernels index contexts, workgroups and mask rows with 32-bit integers
+  const double nkb = std::ceil((double)p->max_pages_per_seq * p->page_size / p->block_k);
+  if ((double)p->max_pages_per_seq * p->page_size > 2147483647.0 ||
+      (double)p->batch * T * p->num_q_heads * p->num_splits > 2147483647.0 ||
+      (double)p->batch * p->num_q_heads * nkb > 2147483647.0)
+    return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
   const size_t parts = (size_t)p->batch * T * p->num_q_heads * p->num_splits;
   size_t bytes = 0;
   if (p->num_splits > 1) {

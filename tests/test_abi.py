@@ -148,6 +148,9 @@ DECODE_BAD = [
     # threshold mode NONE (no decisions) takes no decision diagnostics, whatever `a` holds
     ({"thr": (2, 0, 0.0, 5.0), "skip_mask": FAKE}, 1), ({"thr": (2, 0, 0.0, 5.0), "crit": FAKE}, 1),
     ({"thr": (2, 0, 0.0, float("nan")), "stats_only": 1}, 1),
+    # 32-bit indexing in the kernels: context length, workgroup count and mask rows
+    ({"max_pages_per_seq": 1 << 28}, 2), ({"batch": 1 << 12, "num_splits": 1 << 16}, 2),
+    ({"batch": 1 << 12, "max_pages_per_seq": 1 << 16}, 2),
 ]
 
 
@@ -320,6 +323,7 @@ PAGED_BAD = [
     ({"in_dtype": 1}, 2), ({"page_size": 32}, 2), ({"block_q": 64, "block_k": 64}, 2),
     ({"head_dim_qk": 64, "head_dim_v": 64}, 2), ({"q": FAKE + 4}, 2),
     ({"thr": (2, 0, 0.0, 0.0), "skip_mask": FAKE}, 1), ({"thr": (2, 0, 0.0, 0.0), "stats_only": 1}, 1),
+    ({"max_pages_per_seq": 1 << 28}, 2),
 ]
 
 
