@@ -184,6 +184,50 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _device_of(*ts):
+    """The one GPU device that every given tensor lives on (the kernels read and write them all)."""
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("every tensor argument must be a GPU tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on {dev} and {t.device}: all must be on one GPU")
+    return dev
+
+
+def _buf(t, name, dtypes, numel, contiguous=True):
+    """Pointer to a buffer the kernels index as a flat array of at least `numel` elements."""
+    if t is None:
+        return None
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call writes {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _shape(t, name, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _torch_types():
+    import torch
+    f32, u8, i32 = (torch.float32,), (torch.uint8,), (torch.int32,)
+    cnt = (torch.int64,) + ((torch.uint64,) if hasattr(torch, "uint64") else ())
+    return f32, u8, i32, cnt
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
 def _dtype_code(t):
     import torch
     if t.dtype == torch.bfloat16:
@@ -205,11 +249,19 @@ def _threshold(lam, a, no_decision=False):
     return Threshold(THR_A_OVER_L, 0, 0.0, float(a))
 
 
-def _stream(stream):
+def _stream(stream, device=None):
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _call(fn, p, stream, device):
+    """Calls the library with the tensors' device current (the library launches on the current
+    device) on `stream` (default: that device's current stream)."""
+    import torch
+    with torch.cuda.device(device):
+        _check(fn(ctypes.byref(p), _stream(stream, device)))
 
 
 def _strides3(t):
@@ -222,12 +274,26 @@ def _strides3(t):
 def prefill_params(q, k, v, o, *, causal, block_q, block_k, num_splits=1, lam=None, a=None,
                    softmax_scale=0.0, lse=None, skip_mask=None, crit=None, counters=None,
                    stats_only=False, out_dtype=None, no_decision=False, head_counters=None, v_staging=V_KEPT):
-    """Fills the C params struct for blasst_prefill from tensors (no call)."""
+    """Fills the C params struct for blasst_prefill from tensors (no call).  Checks what the C side
+    cannot: one GPU for every tensor, matching shapes, and diagnostics buffers of the right dtype and
+    size."""
+    f32, u8, _, cnt = _torch_types()
+    _device_of(q, k, v, o, lse, skip_mask, crit, counters, head_counters)
+    B, Hq, Lq, _ = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    _shape(k, "k", (B, Hkv, Lk, q.shape[3]))
+    _shape(v, "v", (B, Hkv, Lk, v.shape[3]))
+    if o is not None:
+        _shape(o, "o", (B, Hq, Lq, v.shape[3]))
+    nmask = B * Hq * _cdiv(Lq, max(1, block_q)) * _cdiv(Lk, max(1, block_k))
     p = PrefillParams()
     p.struct_size = ctypes.sizeof(PrefillParams)
     p.q, p.k, p.v = _ptr(q), _ptr(k), _ptr(v)
     p.o = _ptr(o)
-    p.lse, p.skip_mask, p.crit, p.counters = _ptr(lse), _ptr(skip_mask), _ptr(crit), _ptr(counters)
+    p.lse = _buf(lse, "lse", f32, B * Hq * Lq)
+    p.skip_mask = _buf(skip_mask, "skip_mask", u8, nmask)
+    p.crit = _buf(crit, "crit", f32, nmask)
+    p.counters = _buf(counters, "counters", cnt, 2)
     p.q_stride, p.k_stride, p.v_stride = _strides3(q), _strides3(k), _strides3(v)
     p.o_stride = _strides3(o) if o is not None else (ctypes.c_int64 * 3)(0, 0, 0)
     p.thr = _threshold(lam, a, no_decision)
@@ -239,7 +305,7 @@ def prefill_params(q, k, v, o, *, causal, block_q, block_k, num_splits=1, lam=No
     p.causal, p.block_q, p.block_k = int(bool(causal)), block_q, block_k
     p.num_splits, p.stats_only = num_splits, int(bool(stats_only))
     p.softmax_scale = float(softmax_scale)
-    p.head_counters = _ptr(head_counters)
+    p.head_counters = _buf(head_counters, "head_counters", cnt, B * Hq * 2)
     p.v_staging = int(v_staging)
     return p
 
@@ -261,7 +327,7 @@ def blasst_prefill(q, k, v, o, *, stream=None, **kw):
     num_splits, lam or a, softmax_scale, lse, skip_mask, crit, counters, head_counters,
     stats_only, v_staging)."""
     p = prefill_params(q, k, v, o, **kw)
-    _check(lib().blasst_prefill(ctypes.byref(p), _stream(stream)))
+    _call(lib().blasst_prefill, p, stream, q.device)
 
 
 def paged_prefill_params(q, k_cache, v_cache, block_table, seq_lens, o, *, num_splits=1, lam=None, a=None,
@@ -269,12 +335,31 @@ def paged_prefill_params(q, k_cache, v_cache, block_table, seq_lens, o, *, num_s
                          out_dtype=None, block_q=128, block_k=128):
     """Fills the C params struct for blasst_prefill_paged from tensors (no call).  q [B, Hq, Lq, D]
     (any strides with a contiguous last dim, e.g. a [B, Lq, Hq, D] tensor viewed with permute)."""
+    f32, u8, i32, cnt = _torch_types()
+    _device_of(q, k_cache, v_cache, block_table, seq_lens, o, lse, skip_mask, crit, counters)
+    B, Hq, Lq, D = q.shape
+    P, Hkv, page, _ = k_cache.shape
+    _shape(k_cache, "k_cache", (P, Hkv, page, D))
+    _shape(v_cache, "v_cache", (P, Hkv, v_cache.shape[2], page))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table has shape {tuple(block_table.shape)}, expected ({B}, max_pages)")
+    _shape(seq_lens, "seq_lens", (B,))
+    if o is not None:
+        _shape(o, "o", (B, Hq, Lq, v_cache.shape[2]))
+    max_pages = block_table.shape[1]
+    nmask = B * Hq * _cdiv(Lq, max(1, block_q)) * _cdiv(max_pages * page, max(1, block_k))
     p = PagedPrefillParams()
     p.struct_size = ctypes.sizeof(PagedPrefillParams)
-    p.q, p.k_cache, p.v_cache = _ptr(q), _ptr(k_cache), _ptr(v_cache)
-    p.block_table, p.seq_lens = _ptr(block_table), _ptr(seq_lens)
-    p.o, p.lse = _ptr(o), _ptr(lse)
-    p.skip_mask, p.crit, p.counters = _ptr(skip_mask), _ptr(crit), _ptr(counters)
+    p.q = _ptr(q)
+    p.k_cache = _buf(k_cache, "k_cache", (k_cache.dtype,), 0)
+    p.v_cache = _buf(v_cache, "v_cache", (k_cache.dtype,), 0)
+    p.block_table = _buf(block_table, "block_table", i32, B * max_pages)
+    p.seq_lens = _buf(seq_lens, "seq_lens", i32, B)
+    p.o = _ptr(o)
+    p.lse = _buf(lse, "lse", f32, B * Hq * Lq)
+    p.skip_mask = _buf(skip_mask, "skip_mask", u8, nmask)
+    p.crit = _buf(crit, "crit", f32, nmask)
+    p.counters = _buf(counters, "counters", cnt, 2)
     p.q_stride = _strides3(q)
     p.o_stride = _strides3(o) if o is not None else (ctypes.c_int64 * 3)(0, 0, 0)
     p.thr = _threshold(lam, a)
@@ -294,17 +379,31 @@ def blasst_prefill_paged(q, k_cache, v_cache, block_table, seq_lens, o, *, strea
     sequence; k_cache [P, Hkv, 16, D], v_cache [P, Hkv, D, 16] (V transposed per page), block_table
     [B, max_pages] int32, seq_lens [B] int32; o [B, Hq, Lq, D].  Keyword args follow the C params."""
     p = paged_prefill_params(q, k_cache, v_cache, block_table, seq_lens, o, **kw)
-    _check(lib().blasst_prefill_paged(ctypes.byref(p), _stream(stream)))
+    _call(lib().blasst_prefill_paged, p, stream, q.device)
 
 
 def backward_params(q, k, v, o, dout, lse, dq, dk, dv, *, causal, block_q=128, block_k=128, skip_mask=None,
                     workspace=None, softmax_scale=0.0):
     """Fills the C params struct for blasst_prefill_backward from tensors (no call)."""
+    f32, u8, _, _ = _torch_types()
+    _device_of(q, k, v, o, dout, lse, dq, dk, dv, skip_mask, workspace)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    Dv = v.shape[3]
+    _shape(k, "k", (B, Hkv, Lk, D))
+    _shape(v, "v", (B, Hkv, Lk, Dv))
+    for t, name, shp in ((o, "o", (B, Hq, Lq, Dv)), (dout, "dout", (B, Hq, Lq, Dv)), (dq, "dq", (B, Hq, Lq, D)),
+                         (dk, "dk", (B, Hkv, Lk, D)), (dv, "dv", (B, Hkv, Lk, Dv))):
+        _shape(t, name, shp)
+    nmask = B * Hq * _cdiv(Lq, max(1, block_q)) * _cdiv(Lk, max(1, block_k))
     p = BackwardParams()
     p.struct_size = ctypes.sizeof(BackwardParams)
     p.q, p.k, p.v, p.o, p.dout = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout)
-    p.lse, p.skip_mask = _ptr(lse), _ptr(skip_mask)
+    p.lse = _buf(lse, "lse", f32, B * Hq * Lq)
+    p.skip_mask = _buf(skip_mask, "skip_mask", u8, nmask)
     p.dq, p.dk, p.dv = _ptr(dq), _ptr(dk), _ptr(dv)
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     p.workspace = _ptr(workspace)
     p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     p.q_stride, p.k_stride, p.v_stride = _strides3(q), _strides3(k), _strides3(v)
@@ -335,20 +434,54 @@ def blasst_prefill_backward(q, k, v, o, dout, lse, dq, dk, dv, *, stream=None, *
     shaped like q/k/v (bf16 or fp32).  Keyword args follow the C params (causal, skip_mask = the
     forward's mask or None for dense, workspace, softmax_scale)."""
     p = backward_params(q, k, v, o, dout, lse, dq, dk, dv, **kw)
-    _check(lib().blasst_prefill_backward(ctypes.byref(p), _stream(stream)))
+    _call(lib().blasst_prefill_backward, p, stream, q.device)
 
 
 def decode_params(q, k_cache, v_cache, block_table, seq_lens, o, *, page_size, block_k, num_splits,
                   lam=None, a=None, tile_rows=0, head_dim_v=None, softmax_scale=0.0, lse=None,
                   skip_mask=None, crit=None, counters=None, workspace=None, stats_only=False,
                   out_dtype=None, no_decision=False):
-    """Fills the C params struct for blasst_decode from tensors (no call)."""
+    """Fills the C params struct for blasst_decode from tensors (no call).  The decode takes dense
+    layouts (no strides), so q, the caches, o and the index arrays must be contiguous; checks one GPU
+    for every tensor, matching shapes, and diagnostics buffers of the right dtype and size."""
+    f32, u8, i32, cnt = _torch_types()
+    _device_of(q, k_cache, v_cache, block_table, seq_lens, o, lse, skip_mask, crit, counters, workspace)
+    if q.dim() == 4:
+        B, T, Hq, D = q.shape
+    else:
+        B, Hq, D = q.shape
+        T = 1
+    P, Hkv, page, _ = k_cache.shape
+    _shape(k_cache, "k_cache", (P, Hkv, page, D))
+    dv = head_dim_v if head_dim_v is not None else (v_cache.shape[2] if v_cache is not None else D)
+    if v_cache is not None:
+        _shape(v_cache, "v_cache", (P, Hkv, dv, page))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table has shape {tuple(block_table.shape)}, expected ({B}, max_pages)")
+    _shape(seq_lens, "seq_lens", (B,))
+    max_pages = block_table.shape[1]
+    G = Hq // max(1, Hkv)
+    tr = tile_rows if tile_rows else G
+    nmask = B * Hkv * (G // max(1, tr)) * _cdiv(max_pages * page, max(1, block_k))
     p = DecodeParams()
     p.struct_size = ctypes.sizeof(DecodeParams)
-    p.q, p.k_cache, p.v_cache = _ptr(q), _ptr(k_cache), _ptr(v_cache)
-    p.block_table, p.seq_lens = _ptr(block_table), _ptr(seq_lens)
-    p.o, p.lse = _ptr(o), _ptr(lse)
-    p.skip_mask, p.crit, p.counters = _ptr(skip_mask), _ptr(crit), _ptr(counters)
+    p.q = _buf(q, "q", (q.dtype,), 0)
+    p.k_cache = _buf(k_cache, "k_cache", (q.dtype,), 0)
+    p.v_cache = _buf(v_cache, "v_cache", (q.dtype,), 0)
+    p.block_table = _buf(block_table, "block_table", i32, B * max_pages)
+    p.seq_lens = _buf(seq_lens, "seq_lens", i32, B)
+    if o is not None:
+        if not o.is_contiguous():
+            raise ValueError("o must be contiguous")
+        if o.numel() != B * T * Hq * dv:
+            raise ValueError(f"o holds {o.numel()} elements, expected {B * T * Hq * dv}")
+    p.o = _ptr(o)
+    p.lse = _buf(lse, "lse", f32, B * T * Hq)
+    p.skip_mask = _buf(skip_mask, "skip_mask", u8, nmask)
+    p.crit = _buf(crit, "crit", f32, nmask)
+    p.counters = _buf(counters, "counters", cnt, 2)
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     p.workspace = _ptr(workspace)
     p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     p.thr = _threshold(lam, a, no_decision)
@@ -387,7 +520,7 @@ def blasst_decode(q, k_cache, v_cache, block_table, seq_lens, o, *, stream=None,
     [P, Hkv, Dv, page] (V transposed per page) or None for latent attention (V = K[..., :Dv]);
     block_table [B, max_pages] int32; seq_lens [B] int32; o [B, Hq, Dv] or [B, T, Hq, Dv]."""
     p = decode_params(q, k_cache, v_cache, block_table, seq_lens, o, **kw)
-    _check(lib().blasst_decode(ctypes.byref(p), _stream(stream)))
+    _call(lib().blasst_decode, p, stream, q.device)
 
 
 def blasst_decode_no_alloc(q, k_cache, v_cache, block_table, seq_lens, o, *, stream=None, **kw):
@@ -396,7 +529,7 @@ def blasst_decode_no_alloc(q, k_cache, v_cache, block_table, seq_lens, o, *, str
     if kw.get("workspace") is not None:
         raise ValueError("blasst_decode_no_alloc takes no workspace")
     p = decode_params(q, k_cache, v_cache, block_table, seq_lens, o, **kw)
-    _check(lib().blasst_decode_no_alloc(ctypes.byref(p), _stream(stream)))
+    _call(lib().blasst_decode_no_alloc, p, stream, q.device)
 
 
 def blasst_calib_quantile(crit, target_s: float) -> float:
