@@ -356,26 +356,37 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       const unsigned char *vtb = sV[buf ^ 1] + l32 * VTROW + hi * 16;
       const int vkey0 = (t - 1) * BC;
       const bool vtail = PAGED && vkey0 + BC > Lk;
+      // V^T operand of step q = (k-step q / MTV, dv m-tile q % MTV)
+      auto read_vf = [&](int q) -> bf16x8 {
+        const int kk = q / MTV, mv = q % MTV;
+        bf16x8 vf;
+        if constexpr (PAGED) {
+          // keys 16 kk + 8 hi ... + 7 of dv row 32 mv + l32 (the paged key order of the scores)
+          vf = *(const bf16x8 *)(vtb + mv * 32 * VTROW + kk * 32);
+          if (vtail) {
 #pragma unroll
-      for (int kk = 0; kk < KSV; ++kk) {
-#pragma unroll
-        for (int mv = 0; mv < MTV; ++mv) {
-          bf16x8 vf;
-          if constexpr (PAGED) {
-            // keys 16 kk + 8 hi ... + 7 of dv row 32 mv + l32 (the paged key order of the scores)
-            vf = *(const bf16x8 *)(vtb + mv * 32 * VTROW + kk * 32);
-            if (vtail) {
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                if (vkey0 + 16 * kk + 8 * hi + e >= Lk) vf[e] = (__bf16)0.f;
-            }
-          } else {
-            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + kk * 16 * VROW + mv * 64));
-            const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + (kk * 16 + 8) * VROW + mv * 64));
-            vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+            for (int e = 0; e < 8; ++e)
+              if (vkey0 + 16 * kk + 8 * hi + e >= Lk) vf[e] = (__bf16)0.f;
           }
-          o_acc[mv] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf_pend[kk], o_acc[mv], 0, 0, 0);
+        } else {
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + kk * 16 * VROW + mv * 64));
+          const v4i16 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(vb + (kk * 16 + 8) * VROW + mv * 64));
+          vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
         }
+        return vf;
+      };
+      // V^T fragments two MFMAs ahead of their use, in a ring of three (left to itself, the compiler
+      // placed each fragment's reads right before its MFMA here, so every MFMA waited for its own LDS
+      // reads)
+      constexpr int NQV = KSV * MTV;
+      bf16x8 vr[3];
+      vr[0] = read_vf(0);
+      vr[1] = read_vf(1);
+#pragma unroll
+      for (int q = 0; q < NQV; ++q) {
+        if (q + 2 < NQV) vr[(q + 2) % 3] = read_vf(q + 2);
+        o_acc[q % MTV] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[q % 3], pf_pend[q / MTV], o_acc[q % MTV], 0, 0, 0);
+        if (q & 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (t == J) break;

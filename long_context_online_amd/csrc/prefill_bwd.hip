@@ -263,12 +263,23 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
         for (int i = 0; i < NSPQ; ++i)
           if (jn < J && i * (MT - 1) / NSPQ == mt) stage_part(jn, buf ^ 1, i);
         f32x16 s = f32x16{}, dp = f32x16{};
+        // K and V fragments two k-steps ahead of their MFMAs, in rings of three (left to itself, the
+        // compiler read each fragment right before its MFMA and waited for it there)
+        bf16x8 kr[3], vr[3];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          kr[kk] = *(const bf16x8 *)(kb + mt * 32 * ROW_DQ_K + kk * 32);
+          vr[kk] = *(const bf16x8 *)(vb + mt * 32 * ROW_DQ_V + kk * 32);
+        }
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-          const bf16x8 kf = *(const bf16x8 *)(kb + mt * 32 * ROW_DQ_K + kk * 32);
-          const bf16x8 vf = *(const bf16x8 *)(vb + mt * 32 * ROW_DQ_V + kk * 32);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[kk], dp, 0, 0, 0);
+          if (kk + 2 < KS) {
+            kr[(kk + 2) % 3] = *(const bf16x8 *)(kb + mt * 32 * ROW_DQ_K + (kk + 2) * 32);
+            vr[(kk + 2) % 3] = *(const bf16x8 *)(vb + mt * 32 * ROW_DQ_V + (kk + 2) * 32);
+          }
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[kk % 3], qf[kk], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[kk % 3], df[kk], dp, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
         if (need_mask) {
 #pragma unroll
