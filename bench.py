@@ -806,6 +806,10 @@ def main():
             result["prefill_s050"] = pre.measure(lam50, max(3, args.steps // 2))
             result["prefill_s050"]["target_sparsity"] = 0.5
             result["prefill_decision_overhead"] = pre.decision_overhead(max(3, args.steps // 2))
+            # the headline step against both dense references: the same kernel at lambda = 0 (speedup_vs_dense)
+            # and the variant without any decision logic
+            r["speedup_vs_no_decision_dense"] = round(
+                result["prefill_decision_overhead"]["no_decision_ms"] / r["ms"], 3)
             result["prefill_v_staging"] = pre.v_staging_ablation(lam_p, max(3, args.steps // 2))
             result["prefill_heads"] = head_heterogeneity(m, torch, synth, pre, lam_p, max(3, args.steps // 2))
             bw = Backward(m, torch, pre, lam_p)
