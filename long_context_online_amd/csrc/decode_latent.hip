@@ -161,14 +161,19 @@ __global__ __launch_bounds__(TR / HPW * 64, 1) void decode_latent_kernel(DecodeA
 #pragma unroll
     for (int mt = 0; mt < MTK; ++mt) s[mt] = f32x4{};
     const unsigned char *kb = sK[buf] + n * ROW + grp * 16;
+    // step q = (k-step q / MTK, key m-tile q % MTK); its K fragment is read two MFMAs ahead into a
+    // ring of three (left to itself, the compiler read each fragment right before its MFMA and waited
+    // for it there, with one wave per SIMD and nothing else to hide the LDS latency)
+    constexpr int NQK = KSQ * MTK;
+    auto read_kf = [&](int q) { return *(const bf16x8 *)(kb + (q % MTK) * 16 * ROW + (q / MTK) * 64); };
+    bf16x8 kr[3];
+    kr[0] = read_kf(0);
+    kr[1] = read_kf(1);
 #pragma unroll
-    for (int kk = 0; kk < KSQ; ++kk) {
-#pragma unroll
-      for (int mt = 0; mt < MTK; ++mt) {
-        const bf16x8 kf = *(const bf16x8 *)(kb + mt * 16 * ROW + kk * 64);
-        s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], s[mt], 0, 0, 0);
-      }
-      if ((kk & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < NQK; ++q) {
+      if (q + 2 < NQK) kr[(q + 2) % 3] = read_kf(q + 2);
+      s[q % MTK] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[q % 3], qf[q / MTK], s[q % MTK], 0, 0, 0);
+      if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
     if (key0 + BK > L - a.T + 1) {   // keys past a row's last visible key (or the sequence end)
 #pragma unroll
