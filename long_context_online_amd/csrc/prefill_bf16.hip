@@ -317,6 +317,8 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
       };
       constexpr int NQ = MT * KS;
+      constexpr int KSTEP = NQ / NPK;  // score MFMAs between two direct loads of the next K tile
+      static_assert(KSTEP >= 1, "at most one K load per score MFMA");
       // K fragments two MFMAs ahead of their use, in a ring of three
       bf16x8 kf[3];
       kf[0] = *(const bf16x8 *)(kb);
@@ -325,9 +327,10 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       for (int q = 0; q < NQ; ++q) {
         const int mt = q / KS, kk = q % KS;
         if (q + 2 < NQ) kf[(q + 2) % 3] = *(const bf16x8 *)(kb + ((q + 2) / KS) * 32 * KROW + ((q + 2) % KS) * 32);
-#pragma unroll
-        for (int i = 0; i < NPK; ++i)
-          if (k_next && i * NQ / NPK == q) load_k_part(t + 1, buf ^ 1, i);
+        // one call site with the part index computed from q: with a call per part in the body, the
+        // paged kernel's loop body outgrew the unroller's budget, the loop stayed rolled and the K
+        // fragment ring was indexed at run time (select chains over every slot)
+        if (k_next && q % KSTEP == 0 && q / KSTEP < NPK) load_k_part(t + 1, buf ^ 1, q / KSTEP);
         s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[q % 3], qf[kk], kk == 0 ? f32x16{} : s[mt], 0, 0, 0);
         if (mt > 0 && kk == 1) fold(mt - 1);
         if (q & 1) __builtin_amdgcn_sched_barrier(0);
