@@ -61,7 +61,13 @@ __device__ __forceinline__ int paged_key_of_row(int m) {
 // 128-key blocks of eight 16-token pages): K rows are gathered page by page, and V, which the cache
 // stores transposed inside each page, is staged as a V^T tile ([dv][key]), so the A operand of
 // O^T += V^T P^T is two plain 8-byte LDS reads instead of transpose reads.
-template <int D, int BC, int TPW, bool OUT_F32, bool STATS, bool DEC = true, bool PAGED = false>
+//
+// QP = true (query pairs, for GQA groups of odd size, MHA among them): the two tiles of a workgroup are
+// two consecutive query tiles of ONE q head instead of one query tile of two heads of a group; they
+// read the same K/V stream, so every staged block still serves two tiles.  The workgroup runs the
+// block loop of its heavier tile; for the other tile the blocks past its causal range are not live
+// (its waves still issue their share of the K/V loads, vote skip and form no probabilities).
+template <int D, int BC, int TPW, bool OUT_F32, bool STATS, bool DEC = true, bool PAGED = false, bool QP = false>
 __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int WPT = BC / 32;       // waves per tile (32 rows each)
   constexpr int BR = BC;             // rows per tile
@@ -98,7 +104,8 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   const int hi = lane >> 5;
 
   // ---- tile coordinates: heavy causal tiles first, kv-head groups kept on one XCD per level -------
-  const int groups = a.Hq / TPW;               // head groups of TPW heads sharing a kv head
+  static_assert(!QP || TPW == 2, "query pairs are two tiles");
+  const int groups = QP ? a.Hq : a.Hq / TPW;   // head groups of TPW heads sharing a kv head (QP: heads)
   const int per_level = a.B * groups;
   const int bid = blockIdx.x;
   const int level = bid / per_level;
@@ -116,10 +123,14 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     const int rot = p < 8 ? p : 15 - p;
     rem = (((rem & 7) + rot) & 7) * (per_level >> 3) + (rem >> 3);
   }
-  const int qt = a.causal ? (a.nqt - 1 - level) : level;
+  // QP: level p holds query tiles 2p and 2p + 1 counted from the heavy end (tile 0 the heavier); an
+  // odd tile count leaves the last pair's tile 1 empty
+  const int qt = QP ? (a.causal ? a.nqt - 1 - (2 * level + tile) : 2 * level + tile)
+                    : (a.causal ? (a.nqt - 1 - level) : level);
+  const bool tile_on = !QP || (qt >= 0 && qt < a.nqt);
   const int b = rem / groups;
-  const int hq0 = (rem - b * groups) * TPW;    // first head of the group
-  const int hq = hq0 + tile;
+  const int hq0 = QP ? rem - b * groups : (rem - b * groups) * TPW;   // first head of the group
+  const int hq = QP ? hq0 : hq0 + tile;
   const int g = hq0 / a.G;                     // TPW divides G, so the group shares kv head g
   const int r0 = qt * BR;
   int Lk = a.Lk;                               // keys of this sequence
@@ -139,19 +150,19 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   const int32_t *tab = PAGED ? a.table + (int64_t)b * a.max_pages : nullptr;  // the sequence's page ids
   const int last_page = PAGED ? (Lk - 1) >> 4 : 0;
 
-  const int last_row = min(r0 + BR, a.Lq) - 1;
-  int J;  // live blocks (the same for every tile of the workgroup)
-  if (a.causal) {
-    const int lim = last_row + off;
-    J = lim < 0 ? 0 : min(a.nkb, lim / BC + 1);
-  } else {
-    J = a.nkb;
-  }
-  const int chunk = J > 0 ? (J + a.num_splits - 1) / a.num_splits : 1;
+  auto live_blocks = [&](int qtx) {  // live key blocks of query tile qtx
+    if (!a.causal) return a.nkb;
+    const int lim = min(qtx * BR + BR, a.Lq) - 1 + off;
+    return lim < 0 ? 0 : min(a.nkb, lim / BC + 1);
+  };
+  // J: blocks the workgroup's loop runs (its heavier tile's live blocks); J_me: this tile's live blocks
+  const int J_me = tile_on ? live_blocks(qt) : 0;
+  const int J = QP ? live_blocks(a.causal ? a.nqt - 1 - 2 * level : 2 * level) : J_me;
+  const int chunk = J_me > 0 ? (J_me + a.num_splits - 1) / a.num_splits : 1;
 
   // ---- Q fragments (B operand of S^T = K Q^T): row l32 of this wave, 8 dims per k-step ----------
   const int my_row = r0 + wit * 32 + l32;
-  const bool row_ok = my_row < a.Lq;
+  const bool row_ok = tile_on && my_row < a.Lq;
   bf16x8 qf[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk)
@@ -337,7 +348,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       }
       fold(MT - 1);
       mx = max_xor32(mx);
-      if (!row_ok) mx = kNegInf;
+      if (!row_ok || (QP && t >= J_me)) mx = kNegInf;   // every row of a block that is not live votes skip
       if (DEC) {
         const bool skip_row = row_votes_skip(mx, m_dec, thr_raw);
         const bool wave_keep = __ballot(!skip_row) != 0ull;
@@ -394,7 +405,8 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     }
     if (t == J) break;
 
-    int keep = 1, keep_any = 1;
+    const bool live = !QP || t < J_me;   // block t is live for this tile
+    int keep = live ? 1 : 0, keep_any = 1;
     if (DEC) {
       keep = 0;
       keep_any = 0;
@@ -405,9 +417,11 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       }
     }
     m_dec = fmaxf(m_dec, mx);
-    ++live_cnt;
-    if (!keep) ++skip_cnt;
-    if (DEC && tile_leader) {
+    if (live) {
+      ++live_cnt;
+      if (!keep) ++skip_cnt;
+    }
+    if (DEC && tile_leader && live) {
       if (a.mask) a.mask[mask_row + t] = keep ? kKept : kSkipped;
       if (a.crit) {
         float c = sCrit[buf][tile * WPT];
@@ -461,8 +475,8 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   }
 
   // ---- diagnostics for blocks that are not live ----
-  if (a.mask || a.crit) {
-    for (int j = J + wit * 64 + lane; j < a.nkb; j += WPT * 64) {
+  if ((a.mask || a.crit) && tile_on) {
+    for (int j = J_me + wit * 64 + lane; j < a.nkb; j += WPT * 64) {
       if (a.mask) a.mask[mask_row + j] = kNotLive;
       if (a.crit) a.crit[mask_row + j] = __builtin_nanf("");
     }
@@ -512,16 +526,18 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   }
 }
 
-template <int D, int BC, int TPW>
-static hipError_t launch_tpw(const PrefillArgs &a, bool out_f32, hipStream_t st) {
-  constexpr int NT = 64 * (BC / 32) * TPW;
-  const int grid = a.B * (a.Hq / TPW) * a.nqt;
+// QP: the two tiles of a workgroup are two query tiles of one head (odd GQA groups); otherwise two
+// heads of one group at one query tile
+template <int D, int BC, bool QP>
+static hipError_t launch_pair(const PrefillArgs &a, bool out_f32, hipStream_t st) {
+  constexpr int NT = 64 * (BC / 32) * 2;
+  const int grid = QP ? a.B * a.Hq * ((a.nqt + 1) / 2) : a.B * (a.Hq / 2) * a.nqt;
   if (a.stats_only)
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, TPW, false, true>), dim3(grid), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, 2, false, true, true, false, QP>), dim3(grid), dim3(NT), 0, st, a);
   else if (out_f32)
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, TPW, true, false>), dim3(grid), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, 2, true, false, true, false, QP>), dim3(grid), dim3(NT), 0, st, a);
   else
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, TPW, false, false>), dim3(grid), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, 2, false, false, true, false, QP>), dim3(grid), dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -539,32 +555,27 @@ static hipError_t launch_one(const PrefillArgs &a, bool out_f32, hipStream_t st)
       return hipGetLastError();
     }
   }
-  // two q heads of one GQA group share each staged K/V block when the group has an even size
-  if (a.G % 2 == 0) return launch_tpw<D, BC, 2>(a, out_f32, st);
-  return launch_tpw<D, BC, 1>(a, out_f32, st);
+  // two q heads of one GQA group share each staged K/V block when the group has an even size; for an
+  // odd group, two query tiles of one head do
+  if (a.G % 2 == 0) return launch_pair<D, BC, false>(a, out_f32, st);
+  return launch_pair<D, BC, true>(a, out_f32, st);
 }
 
 // Chunked prefill against a paged cache (head dim 128, 128 x 128 blocks, 16-token pages).
-hipError_t launch_prefill_paged(const PrefillArgs &a, bool out_f32, hipStream_t st) {
-  const int tpw = a.G % 2 == 0 ? 2 : 1;
-  const int grid = a.B * (a.Hq / tpw) * a.nqt;
-  const int nt = 256 * tpw;
-  if (tpw == 2) {
-    if (a.stats_only)
-      hipLaunchKernelGGL((prefill_bf16_kernel<128, 128, 2, false, true, true, true>), dim3(grid), dim3(nt), 0, st, a);
-    else if (out_f32)
-      hipLaunchKernelGGL((prefill_bf16_kernel<128, 128, 2, true, false, true, true>), dim3(grid), dim3(nt), 0, st, a);
-    else
-      hipLaunchKernelGGL((prefill_bf16_kernel<128, 128, 2, false, false, true, true>), dim3(grid), dim3(nt), 0, st, a);
-  } else {
-    if (a.stats_only)
-      hipLaunchKernelGGL((prefill_bf16_kernel<128, 128, 1, false, true, true, true>), dim3(grid), dim3(nt), 0, st, a);
-    else if (out_f32)
-      hipLaunchKernelGGL((prefill_bf16_kernel<128, 128, 1, true, false, true, true>), dim3(grid), dim3(nt), 0, st, a);
-    else
-      hipLaunchKernelGGL((prefill_bf16_kernel<128, 128, 1, false, false, true, true>), dim3(grid), dim3(nt), 0, st, a);
-  }
+template <bool QP>
+static hipError_t launch_paged_pair(const PrefillArgs &a, bool out_f32, hipStream_t st) {
+  const int grid = QP ? a.B * a.Hq * ((a.nqt + 1) / 2) : a.B * (a.Hq / 2) * a.nqt;
+  if (a.stats_only)
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, 128, 2, false, true, true, true, QP>), dim3(grid), dim3(512), 0, st, a);
+  else if (out_f32)
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, 128, 2, true, false, true, true, QP>), dim3(grid), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, 128, 2, false, false, true, true, QP>), dim3(grid), dim3(512), 0, st, a);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill_paged(const PrefillArgs &a, bool out_f32, hipStream_t st) {
+  return a.G % 2 == 0 ? launch_paged_pair<false>(a, out_f32, st) : launch_paged_pair<true>(a, out_f32, st);
 }
 
 // Returns hipErrorNotSupported when no instantiation matches.
