@@ -118,8 +118,12 @@ __device__ __forceinline__ void store4(void *base, int64_t idx, float x0, float 
 // ---------------------------------------------------------------------------------------------
 // dQ (and D)
 // ---------------------------------------------------------------------------------------------
-template <int TPW, bool OUT_F32>
+// QP = true (GQA groups of odd size, MHA among them): the two tiles are two consecutive query tiles
+// of one head instead of one query tile of two heads; tile 0 is the heavier, and the workgroup walks
+// the blocks either tile kept.
+template <int TPW, bool OUT_F32, bool QP = false>
 __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a) {
+  static_assert(!QP || TPW == 2, "query pairs are two tiles");
   constexpr int NW = 4 * TPW;    // waves per workgroup
   constexpr int KS = BD / 16;    // k-steps over the head dim
   constexpr int MT = BB / 32;    // key m-tiles of a block
@@ -135,24 +139,31 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // heavy causal tiles first; TPW heads of one kv head share the staged K/V blocks
-  const int groups = a.Hq / TPW;
+  // heavy causal tiles first; TPW heads of one kv head share the staged K/V blocks (QP: two query
+  // tiles of one head; an odd tile count leaves the last pair's tile 1 empty)
+  const int groups = QP ? a.Hq : a.Hq / TPW;
   const int per_level = a.B * groups;
   const int level = blockIdx.x / per_level;
   const int rem = blockIdx.x - level * per_level;
-  const int qt = a.causal ? (a.nqt - 1 - level) : level;
+  auto qt_of = [&](int tl) {
+    return QP ? (a.causal ? a.nqt - 1 - (2 * level + tl) : 2 * level + tl) : (a.causal ? a.nqt - 1 - level : level);
+  };
+  const int qt0 = qt_of(0), qt1 = qt_of(1);
+  const int qt = tile ? qt1 : qt0;
+  const bool tile_on = qt >= 0 && qt < a.nqt;
   const int b = rem / groups;
-  const int hq0 = (rem - b * groups) * TPW;
-  const int hq = hq0 + tile;
+  const int hq0 = QP ? rem - b * groups : (rem - b * groups) * TPW;
+  const int hq = QP ? hq0 : hq0 + tile;
   const int g = hq0 / a.G;
   const int r0 = qt * BB;
   const int off = a.Lk - a.Lq;
-  const int last_row = min(r0 + BB, a.Lq) - 1;
-  int J = a.nkb;
-  if (a.causal) {
-    const int lim = last_row + off;
-    J = lim < 0 ? 0 : min(a.nkb, lim / BB + 1);
-  }
+  auto live_blocks = [&](int qtx) {   // live key blocks of query tile qtx
+    if (!a.causal) return a.nkb;
+    const int lim = min(qtx * BB + BB, a.Lq) - 1 + off;
+    return lim < 0 ? 0 : min(a.nkb, lim / BB + 1);
+  };
+  const int J = live_blocks(qt0);                                          // tile 0 (the heavier)
+  const int J1 = TPW == 2 && qt1 >= 0 && qt1 < a.nqt ? live_blocks(qt1) : 0;   // tile 1
 
   const __bf16 *qp = (const __bf16 *)a.q + b * a.qs[0] + hq * a.qs[1];
   const __bf16 *dop = (const __bf16 *)a.dout + b * a.dos[0] + hq * a.dos[1];
@@ -162,7 +173,7 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
 
   // ---- this lane's query row: Q and dO fragments (B operands), D = dO . O, LSE ----
   const int my_row = r0 + wit * 32 + l32;
-  const bool row_ok = my_row < a.Lq;
+  const bool row_ok = tile_on && my_row < a.Lq;
   bf16x8 qf[KS], df[KS];
   float dsum = 0.f;
 #pragma unroll
@@ -198,14 +209,15 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
   if (row_ok && hi == 0) a.dvec[row_idx] = dsum;
 
   // ---- kept blocks, 64 per word: bit of block base + x = tile keeps block base + x ----
-  const uint8_t *mrow = a.mask ? a.mask + (((int64_t)b * a.Hq + hq0) * a.nqt + qt) * a.nkb : nullptr;
-  const int64_t mtile = (int64_t)a.nqt * a.nkb;   // distance between the mask rows of two heads
+  const uint8_t *mrow = a.mask ? a.mask + (((int64_t)b * a.Hq + hq0) * a.nqt + qt0) * a.nkb : nullptr;
+  // distance from tile 0's mask row to tile 1's: the next head's row, or (QP) the other query tile's
+  const int64_t mtile = QP ? (int64_t)(qt1 - qt0) * a.nkb : (int64_t)a.nqt * a.nkb;
   uint64_t w0 = 0, w1 = 0;
   int wbase = -64;
   auto fetch = [&](int base) {
     wbase = base;
     const int j = base + lane;
-    bool k0 = j < J, k1 = j < J;
+    bool k0 = j < J, k1 = j < J1;
     if (mrow) {
       k0 = k0 && mrow[j] == kKept;
       if (TPW == 2) k1 = k1 && mrow[mtile + j] == kKept;
@@ -563,21 +575,22 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
-template <int TPW>
+template <bool QP>
 static void launch_dq(const BwdArgs &a, hipStream_t st) {
-  const int grid = a.B * (a.Hq / TPW) * a.nqt;
+  const int grid = QP ? a.B * a.Hq * ((a.nqt + 1) / 2) : a.B * (a.Hq / 2) * a.nqt;
   if (a.out_f32)
-    hipLaunchKernelGGL((prefill_bwd_dq_kernel<TPW, true>), dim3(grid), dim3(256 * TPW), 0, st, a);
+    hipLaunchKernelGGL((prefill_bwd_dq_kernel<2, true, QP>), dim3(grid), dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL((prefill_bwd_dq_kernel<TPW, false>), dim3(grid), dim3(256 * TPW), 0, st, a);
+    hipLaunchKernelGGL((prefill_bwd_dq_kernel<2, false, QP>), dim3(grid), dim3(512), 0, st, a);
 }
 
 // The dQ kernel runs first: it writes D, which the dK/dV kernel reads (same stream).
 hipError_t launch_prefill_bwd(const BwdArgs &a, hipStream_t st) {
+  // two heads of a GQA group per workgroup, or (odd groups) two query tiles of one head
   if (a.G % 2 == 0)
-    launch_dq<2>(a, st);
+    launch_dq<false>(a, st);
   else
-    launch_dq<1>(a, st);
+    launch_dq<true>(a, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int grid = a.B * a.Hkv * a.nkb;

@@ -73,23 +73,24 @@ def _dout(shape, seed):
 
 
 @pytest.mark.parametrize("lam", [0.0, 0.02, 0.3])
-@pytest.mark.parametrize("hq,hkv", [(4, 2), (3, 1), (2, 2)])
-def test_backward_matches_oracle_ragged(lam, hq, hkv):
-    """Causal GQA / MQA with an odd group / MHA, L = 600 (a ragged last tile and block), two sequences,
-    the forward's mask at thresholds from dense to very sparse."""
+@pytest.mark.parametrize("hq,hkv,causal", [(4, 2, True), (3, 1, True), (2, 2, True), (3, 1, False), (2, 2, False)])
+def test_backward_matches_oracle_ragged(lam, hq, hkv, causal):
+    """GQA / MQA with an odd group / MHA, L = 600 (a ragged last tile and block, an odd number of query
+    tiles: odd groups pair two query tiles of one head and leave the last pair's second tile empty),
+    two sequences, the forward's mask at thresholds from dense to very sparse."""
     m = _lib()
     L = 600
     inp = synth.prefill_inputs(batch=2, hq=hq, hkv=hkv, L=L, d=128, block_k=128, window=True, seed=80 + hq,
                                device="cuda")
-    o, lse, mask = _forward(m, inp, causal=True, lam=lam)
+    o, lse, mask = _forward(m, inp, causal=causal, lam=lam)
     dout = _dout(o.shape, 5)
-    dq, dk, dv = _backward(m, inp, o, lse, dout, mask, causal=True)
+    dq, dk, dv = _backward(m, inp, o, lse, dout, mask, causal=causal)
     mh = mask.cpu().numpy()
-    ref = bw.prefill_backward(host64(inp.q), host64(inp.k), host64(inp.v), host64(dout), mh, causal=True,
+    ref = bw.prefill_backward(host64(inp.q), host64(inp.k), host64(inp.v), host64(dout), mh, causal=causal,
                               block_q=128, block_k=128)
     errs = [_check(dq, ref["dq"], "dq"), _check(dk, ref["dk"], "dk"), _check(dv, ref["dv"], "dv")]
     skipped = int((mh == SKIPPED).sum())
-    print(f"lam={lam} hq={hq} hkv={hkv}: skipped {skipped} rel errs dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}")
+    print(f"lam={lam} hq={hq} hkv={hkv} causal={causal}: skipped {skipped} rel errs dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}")
     if lam == 0.3:
         assert skipped > 0
 
