@@ -788,9 +788,9 @@ def main():
         result["prefill"] = r
         result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                              "traffic": profiled_traffic("prefill_bf16_kernel<128, 128, 2, false, false, true, false>"),
+                              "traffic": profiled_traffic("prefill_bf16_kernel<128, 128, 2, false, false, true, false, false>"),
                               "traffic_unit": "HBM bytes per launch",
-                              "counters": profiled_counters("prefill_bf16_kernel<128, 128, 2, false, false, true, false>"),
+                              "counters": profiled_counters("prefill_bf16_kernel<128, 128, 2, false, false, true, false, false>"),
                               "min_bytes": pre.min_bytes,
                               "kernel": "prefill_bf16_kernel<128, 128, 2, bf16 out>",
                               "algorithmic": "QK^T on every live 128x128 tile-block + PV on kept ones, "
