@@ -89,7 +89,11 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
 
   __shared__ __attribute__((aligned(16))) unsigned char sK[2][KBUF];
   __shared__ __attribute__((aligned(16))) unsigned char sV[2][VBUF];
-  __shared__ int sVote[2][NW];
+  // one byte per wave (wave w's vote in byte w), so that one 4- or 8-byte LDS read after the vote
+  // barrier gets every vote (with an int per wave the compiler issued two reads one after the other,
+  // each waited for, before the exponentials could start)
+  static_assert(NW == 4 || NW == 8, "one byte per wave in a 32- or 64-bit word");
+  __shared__ __attribute__((aligned(8))) unsigned char sVote[2][NW];
   // paged: ids of the 8 pages of blocks t .. t + 3 (a ring indexed by block & 3), staged two blocks
   // ahead by wave 0
   __shared__ int sIds[PAGED ? 4 : 1][BC / 16];
@@ -410,11 +414,10 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     if (DEC) {
       keep = 0;
       keep_any = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        keep_any |= sVote[buf][w];
-        if (w / WPT == tile) keep |= sVote[buf][w];
-      }
+      const unsigned long long votes = NW == 8 ? *(const unsigned long long *)sVote[buf]
+                                               : (unsigned long long)*(const unsigned *)sVote[buf];
+      keep_any = votes != 0ull;
+      keep = ((votes >> (tile * WPT * 8)) & ((1ull << (WPT * 8)) - 1ull)) != 0ull;
     }
     m_dec = fmaxf(m_dec, mx);
     if (live) {
