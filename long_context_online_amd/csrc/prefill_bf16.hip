@@ -366,6 +366,11 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K_{t+1} and V_{t-1} have landed in LDS
     __syncthreads();
+    // Each SIMD runs one wave of each tile (waves w and w + 4).  From here to the end of the
+    // iteration, tile 1's waves issue first: measured by phase timestamps, tile 0's wave otherwise ran
+    // ahead into the next block's score MFMAs while tile 1's wave, slowed by them, was still in its
+    // exponentials, and then waited for it at the next barrier.
+    if (tile == 1) __builtin_amdgcn_s_setprio(2);
 
     if (!STATS && keep_pend) {
       // ---- kept block t - 1: O^T += V^T P^T ----
@@ -475,6 +480,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       for (int i = 0; i < NPV; ++i) load_v_part(t, buf, i);
     }
     keep_pend = keep != 0;
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // ---- diagnostics for blocks that are not live ----
