@@ -422,7 +422,9 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       const unsigned long long votes = NW == 8 ? *(const unsigned long long *)sVote[buf]
                                                : (unsigned long long)*(const unsigned *)sVote[buf];
       keep_any = votes != 0ull;
-      keep = ((votes >> (tile * WPT * 8)) & ((1ull << (WPT * 8)) - 1ull)) != 0ull;
+      // (a block that is not live for this tile is never kept: at lambda = 0 the threshold is -inf and
+      // its rows, max -inf, would vote keep)
+      keep = live && ((votes >> (tile * WPT * 8)) & ((1ull << (WPT * 8)) - 1ull)) != 0ull;
     }
     m_dec = fmaxf(m_dec, mx);
     if (live) {

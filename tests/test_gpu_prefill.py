@@ -132,8 +132,8 @@ def test_bf16_shapes_splits_and_offsets(D, blk, causal):
 
 @pytest.mark.parametrize("D,blk", [(64, 64), (128, 128), (128, 64), (64, 128)])
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("hq,hkv", [(3, 3), (6, 2)])
-def test_odd_groups_query_tile_pairs(D, blk, causal, hq, hkv):
+@pytest.mark.parametrize("hq,hkv,lam", [(3, 3, 0.004), (6, 2, 0.004), (3, 3, 0.0)])
+def test_odd_groups_query_tile_pairs(D, blk, causal, hq, hkv, lam):
     """GQA groups of odd size (MHA among them) put two query tiles of one head in a workgroup: every
     head-dim / block-size kernel, Lq != Lk with an odd number of query tiles (the last pair's second
     tile is empty), 3 splits, outputs, masks, critical values and counters against the oracle; the
@@ -141,11 +141,10 @@ def test_odd_groups_query_tile_pairs(D, blk, causal, hq, hkv):
     m = _lib()
     inp = synth.prefill_inputs(batch=2, hq=hq, hkv=hkv, L=700, d=D, block_k=blk, window=True, seed=6,
                                device="cuda", Lq=300)
-    lam = 0.004
     res = _run(m, inp.q, inp.k, inp.v, causal=causal, bq=blk, bk=blk, splits=3, lam=lam)
     assert res[2].shape[2] % 2 == 1
     rep = _compare_all(inp.q, inp.k, inp.v, res, causal=causal, bq=blk, bk=blk, splits=3,
-                       ln_lam=math.log(lam))
+                       ln_lam=math.log(lam) if lam > 0 else -math.inf)
     st = _run(m, inp.q, inp.k, inp.v, causal=causal, bq=blk, bk=blk, splits=3, lam=lam, stats_only=True)
     assert torch.equal(st[2], res[2])
     assert np.array_equal(st[3].cpu().numpy(), res[3].cpu().numpy(), equal_nan=True)   # NaN: not live
