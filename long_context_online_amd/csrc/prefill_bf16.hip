@@ -8,9 +8,13 @@
 // V is not loaded either.
 //
 // MI355X design:
-//   * a workgroup owns TPW query tiles that read the same K/V stream (two q heads of one GQA group
-//     at the same query position), so every staged K/V block serves 2 * BR query rows; each tile
-//     has BR = 32 * WPT rows, one wave per 32 rows, and votes on its own;
+//   * a workgroup owns TPW = 2 query tiles that read the same K/V stream (two q heads of one GQA
+//     group at the same query position; for a group of odd size, MHA among them, two consecutive
+//     query tiles of one head), so every staged K/V block serves 2 * BR query rows; each tile has
+//     BR = 32 * WPT rows, one wave per 32 rows, and votes on its own; each SIMD runs one wave of
+//     each tile, and tile 1's waves issue at a raised priority after the vote barrier (without it
+//     tile 0's wave ran ahead into the next block while tile 1's wave, the laggard, was still in its
+//     exponentials);
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the A operand
 //     (K) comes from LDS, the B operand (Q) stays in registers for the whole tile, and each lane
 //     ends up holding all scores of ONE query row, so the block row max is an in-lane max plus one
@@ -26,9 +30,11 @@
 //     probabilities packed in registers, and only if block t was kept by a tile of the workgroup
 //     are its probabilities formed and V_t loaded, so a skipped block costs QK^T, the row max and
 //     the vote and nothing else;
-//   * the skip vote: per-row predicate -> wave ballot -> one LDS flag per wave -> OR over the
-//     tile's waves after the vote barrier; the skip is a uniform branch, so a skipped block issues
-//     no v_exp and no P.V MFMA;
+//   * the skip vote: per-row predicate -> wave ballot -> one LDS byte per wave -> one read of all
+//     the workgroup's bytes after the vote barrier, OR over the tile's; the skip is a uniform branch,
+//     so a skipped block issues no v_exp and no P.V MFMA;
+//   * LDS operands (K fragments of the scores, V^T fragments of P.V) are read two MFMAs ahead of use
+//     in rings of three, written out: left to itself the compiler read some right before their MFMA;
 //   * LDS rows are padded so that reads are free of bank conflicts on the 64-bank (256-byte) LDS:
 //     K rows are 16 mod 256 bytes apart (16 rows x 16 bytes of one read pass fall on distinct
 //     banks), V rows 64 mod 256 bytes apart (the two 16-lane groups of a transpose-read pass read
