@@ -190,7 +190,8 @@ typedef struct {
  *               NULL selects latent attention (MLA): V is the first head_dim_v channels of K.
  *   block_table [batch][max_pages_per_seq] int32 page ids; entries past a sequence's last page
  *               are never read
- *   seq_lens    [batch] int32, 1 <= seq_lens[b] <= max_pages_per_seq * page_size
+ *   seq_lens    [batch] int32, 0 <= seq_lens[b] <= max_pages_per_seq * page_size (an empty
+ *               sequence reads no key: its rows get o = 0 and lse = -inf, its blocks are not live)
  *   o           [batch][T][num_q_heads][head_dim_v], dtype out_dtype
  *   lse         [batch][T][num_q_heads] fp32, nullable
  * Query tile = tile_rows q heads of one sequence that share a kv head (0 selects all
