@@ -7,20 +7,22 @@
 //     dV = P^T dO,   dP = dO V^T,   dS = scale * P * (dP - D),   dQ = dS K,   dK = dS^T Q,
 // and a tile-block that the forward skipped (or that is not live) adds nothing to any of them.
 //
-// MI355X design (head dim 128, 128 x 128 tile-blocks, bf16 inputs, v_mfma_f32_32x32x16_bf16
-// throughout, with the operand arrangement of the forward kernel: products are taken in the
-// orientation that lets probabilities go from accumulator registers straight into the B operand of
-// the next product, and the one transposed operand of each product is read with the gfx950 transpose
-// read ds_read_b64_tr_b16 from a row-major LDS tile):
-//   * dQ kernel: one workgroup per (TPW q heads of a GQA group, query tile), 4 waves of 32 rows per
-//     tile; the rows' Q and dO stay in registers; K and V blocks go global -> LDS with direct loads
+// MI355X design (head dim 128, 128 x 128 tile-blocks, bf16 inputs; v_mfma_f32_32x32x16_bf16 in the dQ
+// kernel and v_mfma_f32_16x16x32_bf16 in the dK/dV kernel, with the operand arrangement of the
+// forward kernel: products are taken in the orientation that lets probabilities go from accumulator
+// registers straight into the B operand of the next product, and the one transposed operand of each
+// product is read with the gfx950 transpose read ds_read_b64_tr_b16 from a row-major LDS tile):
+//   * dQ kernel: one workgroup per (two q heads of a GQA group, query tile), or for a group of odd
+//     size per (one q head, two consecutive query tiles), 4 waves of 32 rows per tile; the rows' Q
+//     and dO stay in registers; K and V blocks go global -> LDS with direct loads
 //     into double-buffered tiles, one barrier per block, and only blocks that a tile of the workgroup
 //     kept are staged at all.  Per kept block: S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.  It
 //     also forms D from dO and O and stores it for the second kernel;
-//   * dK/dV kernel: one workgroup per (kv head, key block), 4 waves of 32 keys whose K and V rows stay
+//   * dK/dV kernel: one workgroup per (kv head, key block), 8 waves of 16 keys whose K and V rows stay
 //     in registers; it walks the (q head of the group, query tile) pairs whose forward decision for
-//     this block was "keep", staging their Q and dO tiles double-buffered; per pair and 32-row slice:
-//     S = Q K^T, dP = dO V^T, P, dS, then dV^T += dO^T P and dK^T += Q^T dS.  The q heads of the group
+//     this block was "keep", staging their Q and dO tiles double-buffered; per pair and 32-row k-step
+//     (two 16-row slices): S = Q K^T, dP = dO V^T, P, dS, then dV^T += dO^T P and dK^T += Q^T dS,
+//     software-pipelined by one k-step.  The q heads of the group
 //     accumulate in the same registers, so no atomics and no reduction pass are needed;
 //   * a skipped tile-block costs nothing at all (no staging, no product; the forward's QK^T is not
 //     repeated), so the backward's work follows the kept fraction;
