@@ -17,8 +17,9 @@
 //     (global_load_lds_dwordx4, issued as assembly so the compiler does not wait for it before the
 //     current block's LDS reads), double-buffered and prefetched one block ahead, with the page
 //     ids of the next block prefetched as one vector load;
-//   * S^T = K q^T with v_mfma_f32_16x16x32_bf16: K rows from LDS (A operand), the wave's 16 q heads
-//     in registers (B operand, 72 VGPRs); each lane holds 16 scores of one head;
+//   * S^T = K q^T with v_mfma_f32_16x16x32_bf16: K rows from LDS (A operand, read two MFMAs ahead
+//     in a ring of three), the wave's 16 q heads in registers (B operand, 72 VGPRs); each lane holds
+//     16 scores of one head;
 //   * O^T = V^T P^T with v_mfma_f32_16x16x32_bf16: P^T comes from the score registers; the V^T
 //     operand is read from the same LDS tile with ds_read_b64_tr_b16 (transpose read), so V never
 //     needs a second copy; the wave's 16 heads x 512 channels of O live in 128 registers.
