@@ -5,6 +5,8 @@
 // forward evaluated: for each query row, softmax attention over the visible keys of the blocks its
 // tile kept.  With P = exp(scale * Q K^T - LSE) on those (row, key) pairs and D_i = sum_d dO_id O_id:
 //     dV = P^T dO,   dP = dO V^T,   dS = scale * P * (dP - D),   dQ = dS K,   dK = dS^T Q,
+// with the products taken over P * (dP - D) and the scale applied once to each finished dQ and dK
+// value (one multiply per output instead of one per probability),
 // and a tile-block that the forward skipped (or that is not live) adds nothing to any of them.
 //
 // MI355X design (head dim 128, 128 x 128 tile-blocks, bf16 inputs; v_mfma_f32_32x32x16_bf16 in the dQ
@@ -302,12 +304,12 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
             if (key > lim) s[r] = kNegInf;
           }
         }
-        // dS^T = scale * P^T (dP^T - D), packed as the B operand of the two k-steps over these keys
+        // dS^T / scale = P^T (dP^T - D), packed as the B operand of the two k-steps over these keys
         bf16x8 dsf[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -lse_l2));
-          dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dsum) * a.scale);
+          dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dsum));
         }
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
@@ -329,8 +331,9 @@ __global__ __launch_bounds__(256 * TPW, 1) void prefill_bwd_dq_kernel(BwdArgs a)
     for (int mv = 0; mv < MV; ++mv)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        store4<OUT_F32>(a.dq, base + 32 * mv + 8 * q4 + 4 * hi, dq_acc[mv][4 * q4], dq_acc[mv][4 * q4 + 1],
-                        dq_acc[mv][4 * q4 + 2], dq_acc[mv][4 * q4 + 3]);
+        store4<OUT_F32>(a.dq, base + 32 * mv + 8 * q4 + 4 * hi, dq_acc[mv][4 * q4] * a.scale,
+                        dq_acc[mv][4 * q4 + 1] * a.scale, dq_acc[mv][4 * q4 + 2] * a.scale,
+                        dq_acc[mv][4 * q4 + 3] * a.scale);
   }
 }
 
@@ -358,7 +361,7 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char sQ[2][tile_bytes<ROWB>()];
   __shared__ __attribute__((aligned(16))) unsigned char sO[2][tile_bytes<ROWB>()];   // dO tiles
   __shared__ __attribute__((aligned(16))) float sL[2][BB];              // LSE * log2(e) of the tile's rows
-  __shared__ __attribute__((aligned(16))) float sD[2][BB];              // D of the tile's rows
+  __shared__ __attribute__((aligned(16))) float sD[2][BB];              // -D of the tile's rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -460,8 +463,8 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
   };
   // After a wave's staging loads have landed (its own vmcnt(0)), each lane of waves 0-3 rewrites the
   // value its own load wrote: LSE becomes the exponent offset LSE log2(e), +inf (P = 0 exactly) for
-  // rows without any kept key (LSE = -inf) and rows past the end, whose D becomes 0.  The next
-  // barrier publishes them.
+  // rows without any kept key (LSE = -inf) and rows past the end; D becomes -D, 0 for rows past the
+  // end.  The next barrier publishes them.
   auto fix_ld = [&](int p, int buf) {
     if (wave < 4) {
       const int t = p - (p / a.nqt) * a.nqt;
@@ -472,7 +475,7 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
         sL[buf][i] = (!ok || l == kNegInf) ? __builtin_huge_valf() : l * kLog2e;
       } else {
         const float d = sD[buf][i];
-        sD[buf][i] = ok ? d : 0.f;
+        sD[buf][i] = ok ? -d : 0.f;
       }
     }
   };
@@ -513,7 +516,10 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
       f32x4 s[2][2], dp[2][2];   // [k-step parity][slice]
       auto sdp = [&](int ks) {
         const int u = ks & 1;
-        s[u][0] = s[u][1] = dp[u][0] = dp[u][1] = f32x4{};
+        // the dP accumulators start from -D of their rows, so the products leave dP - D
+        s[u][0] = s[u][1] = f32x4{};
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) dp[u][h2] = *(const f32x4 *)&sD[buf][(2 * ks + h2) * 16 + 4 * q4];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
@@ -540,13 +546,12 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
         for (int h2 = 0; h2 < 2; ++h2) {
           const int rr = (2 * ks + h2) * 16 + 4 * q4;
           const f32x4 l4 = *(const f32x4 *)&sL[buf][rr];
-          const f32x4 d4 = *(const f32x4 *)&sD[buf][rr];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float p = fast_exp2(__builtin_fmaf(s[u][h2][e], a.scale_log2, -l4[e]));
             if (need_mask && my_key > row0 + rr + e + off) p = 0.f;
             pf[4 * h2 + e] = (__bf16)p;
-            dsf[4 * h2 + e] = (__bf16)(p * (dp[u][h2][e] - d4[e]) * a.scale);
+            dsf[4 * h2 + e] = (__bf16)(p * dp[u][h2][e]);
           }
         }
 #pragma unroll
@@ -571,7 +576,8 @@ __global__ __launch_bounds__(512) void prefill_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int mv = 0; mv < MV; ++mv) {
       const int d0 = 16 * mv + 4 * q4;
-      store4<OUT_F32>(a.dk, kb + d0, dk_acc[mv][0], dk_acc[mv][1], dk_acc[mv][2], dk_acc[mv][3]);
+      store4<OUT_F32>(a.dk, kb + d0, dk_acc[mv][0] * a.scale, dk_acc[mv][1] * a.scale, dk_acc[mv][2] * a.scale,
+                      dk_acc[mv][3] * a.scale);
       store4<OUT_F32>(a.dv, vb + d0, dv_acc[mv][0], dv_acc[mv][1], dv_acc[mv][2], dv_acc[mv][3]);
     }
   }
