@@ -179,6 +179,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     qf[kk] = row_ok ? *(const bf16x8 *)(qp + (int64_t)my_row * a.qs[2] + kk * 16 + hi * 8) : bf16x8{};
 
   // ---- staging: direct global -> LDS ---------------------------------------------------------
+  const uint32_t page_bytes = (uint32_t)a.Hkv * 16 * D * 2;   // one page of every kv head (paged tiles)
   // One wave instruction fills 1 KB = 64 consecutive 16-byte positions of a buffer; position p is
   // (row p / CP, chunk p % CP); pad chunks load chunk 0 of their row.  Contiguous K/V go through a
   // buffer resource per block whose extent ends at the last key, so keys past the end read as zero
@@ -213,11 +214,14 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     int row = p / CP, c = p - (p / CP) * CP;
     if (c >= CH) c = 0;
     if (row >= BC) row = 0;
-    const int key = min(key0 + paged_key_of_row(row), Lk - 1);
-    // K row of the key's page (16 tokens per page), the page id from the block's staged ids
-    const int pid = sIds[j & 3][(key >> 4) - (key0 >> 4)];
-    const __bf16 *src = base + ((int64_t)pid * a.Hkv + g) * (16 * D) + (key & 15) * D + c * 8;
-    direct_load16(src, lds_addr(dst + ins * 1024));
+    // K row of the key's page (16 tokens per page), the page id from the block's staged ids; keys
+    // past the sequence's end read rows of its last page (the ids are clamped to it) and are masked.
+    // The address is one 32 x 32 -> 64-bit multiply-add on top of the kv head's base.
+    const int kr = paged_key_of_row(row);
+    const uint32_t pid = (uint32_t)sIds[j & 3][kr >> 4];
+    const uint64_t src = (uint64_t)(uintptr_t)(base + g * (16 * D)) + (uint32_t)((kr & 15) * (D * 2) + c * 16) +
+                         (uint64_t)pid * page_bytes;
+    direct_load16((const void *)src, lds_addr(dst + ins * 1024));
   };
   constexpr int NPK = (KINS + NW - 1) / NW;  // direct loads per wave per K tile
   auto load_k_part = [&](int j, int buf, int i) {
@@ -240,9 +244,10 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
         const int dv = p / VTCP;
         int c = p - dv * VTCP;
         if (c >= 16) c = 0;
-        const int pid = sIds[j & 3][c >> 1];
-        const __bf16 *src = vp + (((int64_t)pid * a.Hkv + g) * D + dv) * 16 + (c & 1) * 8;
-        direct_load16(src, lds_addr(sV[buf] + ins * 1024));
+        const uint32_t pid = (uint32_t)sIds[j & 3][c >> 1];
+        const uint64_t src = (uint64_t)(uintptr_t)(vp + g * (D * 16)) + (uint32_t)(dv * 32 + (c & 1) * 16) +
+                             (uint64_t)pid * page_bytes;
+        direct_load16((const void *)src, lds_addr(sV[buf] + ins * 1024));
       }
     } else {
       load_tile_part(vp, a.vs[2], j, sV[buf], std::integral_constant<int, VCP>{}, std::integral_constant<int, VCH>{},
