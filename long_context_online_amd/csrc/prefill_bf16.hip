@@ -185,7 +185,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   // buffer resource per block whose extent ends at the last key, so keys past the end read as zero
   // (and are masked) without any clamping, and a load costs a few 24-bit integer ops for its offset.
   auto load_tile_part = [&](const __bf16 *base, int64_t stride, int j, unsigned char *dst, auto CPc, auto CHc,
-                            auto INSc, int i) {
+                            auto INSc, int i, uint32_t ids) {
     constexpr int CP = decltype(CPc)::value, CH = decltype(CHc)::value, INS = decltype(INSc)::value;
     const int key0 = j * BC;
     const int ins = i * NW + wave;
@@ -214,19 +214,26 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     int row = p / CP, c = p - (p / CP) * CP;
     if (c >= CH) c = 0;
     if (row >= BC) row = 0;
-    // K row of the key's page (16 tokens per page), the page id from the block's staged ids; keys
-    // past the sequence's end read rows of its last page (the ids are clamped to it) and are masked.
-    // The address is one 32 x 32 -> 64-bit multiply-add on top of the kv head's base.
+    // K row of the key's page (16 tokens per page); keys past the sequence's end read rows of its
+    // last page (the ids are clamped to it) and are masked.  The page id comes from `ids` (lane l
+    // holds the id of the block's page l % 8): the rows of one instruction span at most two pages,
+    // the first lane's and the next, so two lane reads and a select give it without an LDS read (and
+    // its wait, which would also drain the K fragment reads in flight).  The address is one
+    // 32 x 32 -> 64-bit multiply-add on top of the kv head's base.
     const int kr = paged_key_of_row(row);
-    const uint32_t pid = (uint32_t)sIds[j & 3][kr >> 4];
+    const int slot = row >> 4;   // = kr >> 4: the key order only permutes rows inside 16-row groups
+    const int slot0 = __builtin_amdgcn_readfirstlane(slot);
+    const uint32_t pid_a = (uint32_t)__builtin_amdgcn_readlane((int)ids, slot0);
+    const uint32_t pid_b = (uint32_t)__builtin_amdgcn_readlane((int)ids, min(slot0 + 1, BC / 16 - 1));
+    const uint32_t pid = slot == slot0 ? pid_a : pid_b;
     const uint64_t src = (uint64_t)(uintptr_t)(base + g * (16 * D)) + (uint32_t)((kr & 15) * (D * 2) + c * 16) +
                          (uint64_t)pid * page_bytes;
     direct_load16((const void *)src, lds_addr(dst + ins * 1024));
   };
   constexpr int NPK = (KINS + NW - 1) / NW;  // direct loads per wave per K tile
-  auto load_k_part = [&](int j, int buf, int i) {
+  auto load_k_part = [&](int j, int buf, int i, uint32_t ids) {
     load_tile_part(kp, a.ks[2], j, sK[buf], std::integral_constant<int, KCP>{}, std::integral_constant<int, KCH>{},
-                   std::integral_constant<int, KINS>{}, i);
+                   std::integral_constant<int, KINS>{}, i, ids);
   };
   // Paged V^T tile: row dv holds the block's 128 keys, 16 bytes (8 keys, half a page) per position;
   // row stride VTROW = 272 bytes (16 positions + 1 pad).  Keys past the sequence's last page read
@@ -251,7 +258,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
       }
     } else {
       load_tile_part(vp, a.vs[2], j, sV[buf], std::integral_constant<int, VCP>{}, std::integral_constant<int, VCH>{},
-                     std::integral_constant<int, VINS>{}, i);
+                     std::integral_constant<int, VINS>{}, i, 0u);
     }
   };
   // The K tile of block t + 1 is loaded during block t's score MFMAs, spread evenly over them: a
@@ -303,8 +310,9 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     __syncthreads();
   }
   if (J > 0) {
+    const uint32_t ids0 = PAGED ? (uint32_t)sIds[0][lane & 7] : 0u;   // block 0's page ids (paged)
 #pragma unroll
-    for (int i = 0; i < NPK; ++i) load_k_part(0, 0, i);
+    for (int i = 0; i < NPK; ++i) load_k_part(0, 0, i, ids0);
   }
   // a wait the compiler sees (not inline asm), on every path into the loop: without it the compiler
   // takes the Q fragments as possibly in flight at the loop head and waits for vmcnt(0), i.e. for the
@@ -316,6 +324,8 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     const int buf = t & 1;
     if (t + 2 < J) stage_ids(t + 2);
     const bool k_next = t + 1 < J;
+    // paged: lane l holds the id of block t + 1's page l % 8 (published by the previous barrier)
+    const uint32_t ids_next = PAGED && k_next ? (uint32_t)sIds[(t + 1) & 3][lane & 7] : 0u;
     float mx = kNegInf;
     if (t < J) {
       if (to_split == 0) {  // a split starts at this block
@@ -357,7 +367,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
         // one call site with the part index computed from q: with a call per part in the body, the
         // paged kernel's loop body outgrew the unroller's budget, the loop stayed rolled and the K
         // fragment ring was indexed at run time (select chains over every slot)
-        if (k_next && q % KSTEP == 0 && q / KSTEP < NPK) load_k_part(t + 1, buf ^ 1, q / KSTEP);
+        if (k_next && q % KSTEP == 0 && q / KSTEP < NPK) load_k_part(t + 1, buf ^ 1, q / KSTEP, ids_next);
         s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[q % 3], qf[kk], kk == 0 ? f32x16{} : s[mt], 0, 0, 0);
         if (mt > 0 && kk == 1) fold(mt - 1);
         if (q & 1) __builtin_amdgcn_sched_barrier(0);
