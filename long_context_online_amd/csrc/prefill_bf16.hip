@@ -65,8 +65,9 @@ __device__ __forceinline__ int paged_key_of_row(int m) {
 // DEC = false: no threshold at all (every live block kept, no vote); used to measure what the
 // decisions cost.  PAGED = true: K and V come from a paged cache (chunked prefill; head dim 128,
 // 128-key blocks of eight 16-token pages): K rows are gathered page by page, and V, which the cache
-// stores transposed inside each page, is staged as a V^T tile ([dv][key]), so the A operand of
-// O^T += V^T P^T is two plain 8-byte LDS reads instead of transpose reads.
+// stores transposed inside each page, is staged page-major as a V^T tile ([page][dv][16 keys], each
+// page a plain 4 KB copy), so the A operand of O^T += V^T P^T is one 16-byte LDS read per lane (1 KB
+// of consecutive bytes per wave) instead of transpose reads.
 //
 // QP = true (query pairs, for GQA groups of odd size, MHA among them): the two tiles of a workgroup are
 // two consecutive query tiles of ONE q head instead of one query tile of two heads of a group; they
@@ -235,24 +236,20 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     load_tile_part(kp, a.ks[2], j, sK[buf], std::integral_constant<int, KCP>{}, std::integral_constant<int, KCH>{},
                    std::integral_constant<int, KINS>{}, i, ids);
   };
-  // Paged V^T tile: row dv holds the block's 128 keys, 16 bytes (8 keys, half a page) per position;
-  // row stride VTROW = 272 bytes (16 positions + 1 pad).  Keys past the sequence's last page read
-  // that page (their values are zeroed before use).
-  constexpr int VTCP = 17, VTROW = VTCP * 16, VTINS = D * VTCP / 64;
+  // Paged V^T tile, page-major: page s of the block holds its 16 keys for every dv as the cache
+  // stores them ([dv][16 keys], 4 KB), so each 4 KB page is one plain copy: a direct load covers a
+  // quarter of one page, whose id comes from a lane read of `ids`, and a lane's offset is its own
+  // index.  Keys past the sequence's last page read that page (their values are zeroed before use).
+  constexpr int VTPAGE = D * 16 * 2, VTINS = BC / 16 * VTPAGE / 1024;
   static_assert(!PAGED || (D == 128 && BC == 128 && VTINS * 1024 <= VBUF), "paged tiles are 128 x 128");
   constexpr int NPV = ((PAGED ? VTINS : VINS) + NW - 1) / NW;  // direct loads per wave per V tile
-  auto load_v_part = [&](int j, int buf, int i) {
+  auto load_v_part = [&](int j, int buf, int i, uint32_t ids) {
     if constexpr (PAGED) {
       const int ins = i * NW + wave;
       if (ins < VTINS) {
-        int ln = lane;   // recomputed offsets, as for K
-        asm volatile("" : "+v"(ln));
-        const int p = ins * 64 + ln;
-        const int dv = p / VTCP;
-        int c = p - dv * VTCP;
-        if (c >= 16) c = 0;
-        const uint32_t pid = (uint32_t)sIds[j & 3][c >> 1];
-        const uint64_t src = (uint64_t)(uintptr_t)(vp + g * (D * 16)) + (uint32_t)(dv * 32 + (c & 1) * 16) +
+        constexpr int QPP = VTPAGE / 1024;   // direct loads per page
+        const uint32_t pid = (uint32_t)__builtin_amdgcn_readlane((int)ids, ins / QPP);
+        const uint64_t src = (uint64_t)(uintptr_t)(vp + g * (D * 16)) + (ins % QPP) * 1024 + lane * 16 +
                              (uint64_t)pid * page_bytes;
         direct_load16((const void *)src, lds_addr(sV[buf] + ins * 1024));
       }
@@ -309,10 +306,11 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
+  uint32_t ids_blk = 0u;   // paged: lane l holds the id of block t's page l % 8 (for the V_t loads)
   if (J > 0) {
-    const uint32_t ids0 = PAGED ? (uint32_t)sIds[0][lane & 7] : 0u;   // block 0's page ids (paged)
+    if (PAGED) ids_blk = (uint32_t)sIds[0][lane & 7];
 #pragma unroll
-    for (int i = 0; i < NPK; ++i) load_k_part(0, 0, i, ids0);
+    for (int i = 0; i < NPK; ++i) load_k_part(0, 0, i, ids_blk);
   }
   // a wait the compiler sees (not inline asm), on every path into the loop: without it the compiler
   // takes the Q fragments as possibly in flight at the loop head and waits for vmcnt(0), i.e. for the
@@ -397,8 +395,9 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     if (!STATS && keep_pend) {
       // ---- kept block t - 1: O^T += V^T P^T ----
       const unsigned char *vb = sV[buf ^ 1] + tr_off;
-      // paged: V^T row reads; keys past the sequence end hold arbitrary bytes and get V = 0
-      const unsigned char *vtb = sV[buf ^ 1] + l32 * VTROW + hi * 16;
+      // paged: V^T row reads from the page-major tile; keys past the sequence end hold arbitrary
+      // bytes and get V = 0
+      const unsigned char *vtb = sV[buf ^ 1] + l32 * 32 + hi * 16;
       const int vkey0 = (t - 1) * BC;
       const bool vtail = PAGED && vkey0 + BC > Lk;
       // V^T operand of step q = (k-step q / MTV, dv m-tile q % MTV)
@@ -406,8 +405,9 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
         const int kk = q / MTV, mv = q % MTV;
         bf16x8 vf;
         if constexpr (PAGED) {
-          // keys 16 kk + 8 hi ... + 7 of dv row 32 mv + l32 (the paged key order of the scores)
-          vf = *(const bf16x8 *)(vtb + mv * 32 * VTROW + kk * 32);
+          // keys 16 kk + 8 hi ... + 7 (page kk) of dv row 32 mv + l32 (the paged key order of the
+          // scores): the wave reads 1 KB of consecutive bytes
+          vf = *(const bf16x8 *)(vtb + kk * VTPAGE + mv * 32 * 32);
           if (vtail) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
@@ -501,8 +501,9 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     // (the buffer held V_{t-2}, whose P.V every wave finished before this iteration's barrier)
     if (!STATS && (keep_any || a.v_all)) {
 #pragma unroll
-      for (int i = 0; i < NPV; ++i) load_v_part(t, buf, i);
+      for (int i = 0; i < NPV; ++i) load_v_part(t, buf, i, ids_blk);
     }
+    if (PAGED) ids_blk = ids_next;
     keep_pend = keep != 0;
     __builtin_amdgcn_s_setprio(0);
   }
