@@ -154,7 +154,8 @@ typedef struct {
  * sees no key (seq_lens[b] < seqlen_q) gets o = 0 and lse = -inf.  The threshold's L is seq_lens[b]
  * (per sequence, resolved on the device).
  * Supported: bf16 in, bf16 or fp32 out, head_dim_qk == head_dim_v == 128, block_q == block_k == 128,
- * page_size 16, causal only, seq_lens[b] >= 1.
+ * page_size 16, causal only, seq_lens[b] >= 1, num_pages * num_kv_heads < 2^32 (a pool of at most
+ * 16 TB per cache; larger values return BLASST_ERR_UNSUPPORTED).
  */
 typedef struct {
   size_t struct_size;        /* sizeof(blasst_prefill_paged_params) */

@@ -134,9 +134,9 @@ blasst_status blasst_prefill_paged(const blasst_prefill_paged_params *p, void *s
       return fail(BLASST_ERR_UNSUPPORTED, "strides must be multiples of 16 bytes");
   if (!aligned16(p->q) || !aligned16(p->k_cache) || !aligned16(p->v_cache) || (p->o && !aligned16(p->o)))
     return fail(BLASST_ERR_UNSUPPORTED, "q, caches and o must be 16-byte aligned");
-  // 32-bit key positions, and the bytes of one page across every kv head in 32 bits
+  // 32-bit key positions, and the pool's (page, kv head) units counted in 32 bits
   if ((double)p->max_pages_per_seq * p->page_size > 2147483647.0 ||
-      (double)p->num_kv_heads * p->page_size * p->head_dim_qk * 2 > 4294967295.0)
+      (double)p->num_pages * p->num_kv_heads > 4294967295.0)
     return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
   const double scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0 / std::sqrt((double)p->head_dim_qk);
   blasst::PrefillArgs a{};

@@ -57,6 +57,13 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 // P.V product (registers 8 s ... 8 s + 7) are the consecutive keys 16 s + 8 h ... + 7, and their V^T
 // operand is one 16-byte read of a V^T row (the natural order needs two 8-byte reads, which conflict
 // on LDS banks at every row stride).
+// floor(p / d) == (p * ceil(2^16 / d)) >> 16 for every p < n (checked at compile time where used)
+constexpr bool div_by_magic_exact(int d, int n) {
+  for (int p = 0; p < n; ++p)
+    if ((p * ((65536 + d - 1) / d)) >> 16 != p / d) return false;
+  return true;
+}
+
 __device__ __forceinline__ int paged_key_of_row(int m) {
   const int a = m >> 3, h = (m >> 2) & 1, b = m & 3;
   return (m & ~31) + 16 * ((a & 3) >> 1) + 8 * h + 4 * (a & 1) + b;
@@ -180,7 +187,9 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     qf[kk] = row_ok ? *(const bf16x8 *)(qp + (int64_t)my_row * a.qs[2] + kk * 16 + hi * 8) : bf16x8{};
 
   // ---- staging: direct global -> LDS ---------------------------------------------------------
-  const uint32_t page_bytes = (uint32_t)a.Hkv * 16 * D * 2;   // one page of every kv head (paged tiles)
+  // paged tiles: a page id times the kv head count counts the pool's 4 KB (one head, 16 tokens)
+  // units before that page; it stays below 2^32 (validated), so it is one 32-bit multiply
+  const uint32_t hkv_u = (uint32_t)a.Hkv;
   // One wave instruction fills 1 KB = 64 consecutive 16-byte positions of a buffer; position p is
   // (row p / CP, chunk p % CP); pad chunks load chunk 0 of their row.  Contiguous K/V go through a
   // buffer resource per block whose extent ends at the last key, so keys past the end read as zero
@@ -211,16 +220,17 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     // load instead of being kept in registers across the block loop (where they spilled)
     int ln = lane;
     asm volatile("" : "+v"(ln));
+    static_assert(!PAGED || (INS * 64 == BC * CP && div_by_magic_exact(CP, INS * 64)),
+                  "every position is a chunk of a tile row, and the 24-bit division below is exact");
     const int p = ins * 64 + ln;
-    int row = p / CP, c = p - (p / CP) * CP;
+    const int row = (int)(__umul24((unsigned)p, (65536u + CP - 1) / CP) >> 16);   // p / CP
+    int c = p - row * CP;
     if (c >= CH) c = 0;
-    if (row >= BC) row = 0;
     // K row of the key's page (16 tokens per page); keys past the sequence's end read rows of its
     // last page (the ids are clamped to it) and are masked.  The page id comes from `ids` (lane l
     // holds the id of the block's page l % 8): the rows of one instruction span at most two pages,
     // the first lane's and the next, so two lane reads and a select give it without an LDS read (and
-    // its wait, which would also drain the K fragment reads in flight).  The address is one
-    // 32 x 32 -> 64-bit multiply-add on top of the kv head's base.
+    // its wait, which would also drain the K fragment reads in flight).
     const int kr = paged_key_of_row(row);
     const int slot = row >> 4;   // = kr >> 4: the key order only permutes rows inside 16-row groups
     const int slot0 = __builtin_amdgcn_readfirstlane(slot);
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
     const uint32_t pid_b = (uint32_t)__builtin_amdgcn_readlane((int)ids, min(slot0 + 1, BC / 16 - 1));
     const uint32_t pid = slot == slot0 ? pid_a : pid_b;
     const uint64_t src = (uint64_t)(uintptr_t)(base + g * (16 * D)) + (uint32_t)((kr & 15) * (D * 2) + c * 16) +
-                         (uint64_t)pid * page_bytes;
+                         (uint64_t)(pid * hkv_u) * (16 * D * 2);
     direct_load16((const void *)src, lds_addr(dst + ins * 1024));
   };
   constexpr int NPK = (KINS + NW - 1) / NW;  // direct loads per wave per K tile
@@ -250,7 +260,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
         constexpr int QPP = VTPAGE / 1024;   // direct loads per page
         const uint32_t pid = (uint32_t)__builtin_amdgcn_readlane((int)ids, ins / QPP);
         const uint64_t src = (uint64_t)(uintptr_t)(vp + g * (D * 16)) + (ins % QPP) * 1024 + lane * 16 +
-                             (uint64_t)pid * page_bytes;
+                             (uint64_t)(pid * hkv_u) * (16 * D * 2);
         direct_load16((const void *)src, lds_addr(sV[buf] + ins * 1024));
       }
     } else {

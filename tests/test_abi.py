@@ -323,7 +323,7 @@ PAGED_BAD = [
     ({"in_dtype": 1}, 2), ({"page_size": 32}, 2), ({"block_q": 64, "block_k": 64}, 2),
     ({"head_dim_qk": 64, "head_dim_v": 64}, 2), ({"q": FAKE + 4}, 2),
     ({"thr": (2, 0, 0.0, 0.0), "skip_mask": FAKE}, 1), ({"thr": (2, 0, 0.0, 0.0), "stats_only": 1}, 1),
-    ({"max_pages_per_seq": 1 << 28}, 2), ({"num_q_heads": 1 << 20, "num_kv_heads": 1 << 20}, 2),
+    ({"max_pages_per_seq": 1 << 28}, 2), ({"num_pages": 1 << 30}, 2),
 ]
 
 
