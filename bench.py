@@ -48,6 +48,7 @@ M_B, M_HQ, M_D, M_DV, M_CTX, M_TARGETS = 64, 128, 576, 512, 32768, (0.5, 0.73)
 # 8 splits: 512 workgroups of 64 blocks; with 16 the per-split first blocks (always kept) cap the
 # sparsity at 65 % even at lambda = 1, and the partials to merge double (see mla_decode.splits_sweep)
 M_SPLITS = 8
+CHUNKED_KERNEL = "prefill_bf16_kernel<128, 128, 2, false, false, true, true, false>"
 DEC_KERNEL = {False: "decode_gqa_kernel<false, true>", True: "decode_mla_kernel<false, false>"}
 MLA_WORKLOAD = ("latent decode, DeepSeek-shaped: batch 64, 128 q heads on one latent head, 576-dim scores, "
                 "V = first 512 channels, context 32768, 16-token pages, 64-token blocks, 8 splits, 128-head "
@@ -94,9 +95,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "mla", "backward"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "mla", "backward", "chunked"], default="all",
                     help="restrict the timed step (for profiling runs; backward: the prefill's backward with "
-                         "the forward's skip mask at the calibrated lambda)")
+                         "the forward's skip mask at the calibrated lambda; chunked: the chunked prefill against "
+                         "the paged cache)")
     ap.add_argument("--quick", action="store_true",
                     help="only the timed step (no 128K decode, latent decode or calibration sweep)")
     ap.add_argument("--profile-only", action="store_true",
@@ -714,14 +716,18 @@ def main():
     if args.only == "backward":  # the prefill's backward as the timed step
         base = Prefill(m, torch, synth)
         bwd = Backward(m, torch, base, base.calibrate(P_TARGET))
+    chk = PagedPrefill(m, torch, synth) if args.only == "chunked" else None  # chunked prefill as the timed step
     torch.cuda.synchronize()
 
     lam_p = pre.calibrate(P_TARGET) if pre else None
     lam_d = (dec.calibrate(M_TARGETS[-1] if dec.latent else D_TARGET)) if dec else None
+    lam_c = chk.calibrate(P_TARGET) if chk else None
 
     def step():
         if pre:
             pre.run(lam_p)
+        if chk:
+            chk.run(lam_c)
         if dec:
             dec.run(lam_d)
         if bwd:
@@ -741,6 +747,8 @@ def main():
         e[0].record()
         if pre:
             pre.run(lam_p)
+        if chk:
+            chk.run(lam_c)
         e[1].record()
         if dec:
             dec.run(lam_d)
@@ -760,6 +768,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"profile_only": True, "steps": args.steps, "warmup": args.warmup,
                           "prefill_ms": round(pre_ms, 4) if pre else None,
+                          "chunked_prefill_ms": round(pre_ms, 4) if chk else None, "chunked_lambda": lam_c,
                           "decode_ms": round(dec_ms, 4) if dec else None,
                           "backward_ms": round(dec_ms, 4) if bwd else None,
                           "prefill_lambda": lam_p, "decode_lambda": lam_d,
@@ -862,6 +871,8 @@ def main():
         lam = cp.calibrate(P_TARGET)
         r = cp.measure(lam, args.steps)
         r["target_sparsity"] = P_TARGET
+        r["profiled_traffic_bytes_per_launch"] = profiled_traffic(CHUNKED_KERNEL)
+        r["profiled_counters"] = profiled_counters(CHUNKED_KERNEL)
         result["chunked_prefill"] = r
         del cp
         torch.cuda.empty_cache()
