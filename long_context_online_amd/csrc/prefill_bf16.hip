@@ -126,7 +126,7 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   const int groups = QP ? a.Hq : a.Hq / TPW;   // head groups of TPW heads sharing a kv head (QP: heads)
   const int per_level = a.B * groups;
   const int bid = blockIdx.x;
-  const int level = bid / per_level;
+  int level = bid / per_level;
   int rem = bid - level * per_level;
   // Workgroups go to the 8 XCDs round robin.  A level's head groups are cut into 8 contiguous
   // chunks; the q heads of one kv head stay together and share its K/V in that XCD's L2, and an
@@ -135,7 +135,22 @@ __global__ __launch_bounds__(64 * (BC / 32) * TPW, 2) void prefill_bf16_kernel(P
   // stripe to stripe, forward over 8 stripes and back over the next 8, so every XCD takes every
   // chunk on stripes of equal total causal work: heads whose sparsity differs then load all XCDs
   // alike instead of one XCD getting every tile of the densest heads and finishing last.
-  if ((per_level & 7) == 0) {
+  if (PAGED && (gridDim.x & 7) == 0) {
+    // Chunked prefill: every query tile of a chunk reads nearly all of its sequence's context, and
+    // one kv head's K/V stream (16 MB at 32K keys) is several times an XCD's L2, so tiles share it
+    // only while they run together.  XCD x takes the contiguous run x * n / 8 ... of workgroups
+    // ordered stream-major ((sequence, kv head), then level, then head group), so the workgroups
+    // resident on an XCD read the same stream side by side and each stream is fetched by one XCD.
+    const int gpk = groups / (a.Hq / a.G);           // head groups per kv head
+    const int per_stream = gpk * (int)(gridDim.x / per_level);
+    const int lid = (bid & 7) * (int)(gridDim.x >> 3) + (bid >> 3);
+    const int stream = lid / per_stream;
+    const int w = lid - stream * per_stream;
+    const int lvl = w / gpk;
+    const int sb = stream / (a.Hq / a.G), skv = stream - sb * (a.Hq / a.G);
+    level = lvl;
+    rem = sb * groups + skv * gpk + (w - lvl * gpk);
+  } else if ((per_level & 7) == 0) {
     const int stripe = level / max(1, 256 / per_level);
     const int p = stripe & 15;
     const int rot = p < 8 ? p : 15 - p;
